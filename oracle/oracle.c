@@ -1,0 +1,308 @@
+/*
+ * oracle.c -- plain, slow fp64 reference for attention over a block-paged
+ * KV cache whose keys are Q8_0 and whose values are Q4_0.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this file's library.  It shares
+ * no code, header, table or constant with the HIP library: the page layout,
+ * the page-table entry encoding and the fp16 format are decoded here from
+ * their written definitions.
+ *
+ * What is computed (per layer):
+ *   Exact softmax attention of each query row over the complete, logically
+ *   ordered KV history.  Streaming and residency change only where a page
+ *   physically lives, never the result ("Adaptive KV Streaming for
+ *   llama.cpp", section "Adaptive KV streaming"; "troed's fork of Raymond's
+ *   adaptive KV streaming", section "Keep the stock attention order").
+ *   Pages hold 256 token positions ("troed's fork ...", section "KV data
+ *   movement and attention").
+ *
+ * Readings taken where the pages are silent (each is listed in the design
+ * notes of the repository):
+ *   - Q8_0 block: 32 values, one IEEE binary16 scale d, 32 int8 codes c;
+ *     value = d * c.  Q4_0 block: 32 values, one binary16 scale d, 32 4-bit
+ *     codes n; value = d * (n - 8).
+ *   - Query rows are the last W positions of the N-token history; row r sits
+ *     at position N - W + r and sees keys 0 .. N - W + r (causal among the
+ *     rows).
+ *   - Grouped-query attention: query head h reads KV head floor(h / G),
+ *     G = n_q_heads / n_kv_heads.
+ *   - Page layout (head_dim 128, T tokens per page, H KV heads), four
+ *     sections in this order:
+ *       K codes   int8    H * T * 128 bytes
+ *       K scales  binary16 H * T * 4
+ *       V nibbles uint8   H * T * 64 bytes
+ *       V scales  binary16 H * T * 4
+ *     Scales are stored [head][token][block].  K codes of head h start at
+ *     h*T*128; a 16-token tile occupies 2048 bytes; inside it, the byte of
+ *     (token j, dim t) is at
+ *         (t/64)*1024 + (((t%32)/8)*16 + j%16)*16 + ((t/32)%2)*8 + t%8.
+ *     V nibbles of head h start at h*T*64; a 32-token tile occupies 2048
+ *     bytes; inside it, for token j (jj = j%32) and dim t the byte is at
+ *         (t/64)*1024 + (((jj%16)/4)*16 + t%16)*16 + ((t/16)%4)*4 + jj%4
+ *     and the code is the low nibble when jj < 16, else the high nibble.
+ *   - Page-table entry: an id below 0x80000000 names a pool page;
+ *     0x80000000|s names ring slot s; 0xFFFFFFFF means "in the host
+ *     history", i.e. logical page P is page P of the layer's host copy.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define HEAD_DIM 128
+#define BLOCK 32
+#define N_BLOCKS (HEAD_DIM / BLOCK)
+
+/* ---------------------------------------------------------------------- */
+/* IEEE 754 binary16 -> double, from the format's definition.              */
+/* ---------------------------------------------------------------------- */
+double oracle_f16_to_f64(uint16_t bits) {
+    int sign = (bits >> 15) & 1;
+    int exponent = (bits >> 10) & 0x1F;
+    int mantissa = bits & 0x3FF;
+    double v;
+    if (exponent == 0) {
+        v = ldexp((double)mantissa, -24); /* subnormal: m * 2^-14 * 2^-10 */
+    } else if (exponent == 31) {
+        v = mantissa ? NAN : INFINITY;
+    } else {
+        v = ldexp((double)(1024 + mantissa), exponent - 25); /* 1.m * 2^(e-15) */
+    }
+    return sign ? -v : v;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Page layout reading                                                     */
+/* ---------------------------------------------------------------------- */
+static size_t sec_k_codes(int H, int T) { (void)H; (void)T; return 0; }
+static size_t sec_k_scales(int H, int T) { return (size_t)H * T * HEAD_DIM; }
+static size_t sec_v_codes(int H, int T) { return sec_k_scales(H, T) + (size_t)H * T * N_BLOCKS * 2; }
+static size_t sec_v_scales(int H, int T) { return sec_v_codes(H, T) + (size_t)H * T * (HEAD_DIM / 2); }
+
+size_t oracle_page_bytes(int n_kv_heads, int page_tokens) {
+    return sec_v_scales(n_kv_heads, page_tokens) + (size_t)n_kv_heads * page_tokens * N_BLOCKS * 2;
+}
+
+static uint16_t read_u16(const uint8_t *p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+
+int oracle_k_code(const uint8_t *page, int H, int T, int head, int j, int t) {
+    size_t base = sec_k_codes(H, T) + (size_t)head * T * HEAD_DIM + (size_t)(j / 16) * 2048;
+    size_t off = (size_t)(t / 64) * 1024 + (size_t)(((t % 32) / 8) * 16 + j % 16) * 16 +
+                 (size_t)((t / 32) % 2) * 8 + (size_t)(t % 8);
+    return (int)(int8_t)page[base + off];
+}
+
+int oracle_v_code(const uint8_t *page, int H, int T, int head, int j, int t) {
+    int jj = j % 32;
+    size_t base = sec_v_codes(H, T) + (size_t)head * T * (HEAD_DIM / 2) + (size_t)(j / 32) * 2048;
+    size_t off = (size_t)(t / 64) * 1024 + (size_t)(((jj % 16) / 4) * 16 + t % 16) * 16 +
+                 (size_t)((t / 16) % 4) * 4 + (size_t)(jj % 4);
+    uint8_t byte = page[base + off];
+    return jj < 16 ? (byte & 0x0F) : (byte >> 4);
+}
+
+double oracle_k_scale(const uint8_t *page, int H, int T, int head, int j, int block) {
+    size_t off = sec_k_scales(H, T) + (((size_t)head * T + j) * N_BLOCKS + block) * 2;
+    return oracle_f16_to_f64(read_u16(page + off));
+}
+
+double oracle_v_scale(const uint8_t *page, int H, int T, int head, int j, int block) {
+    size_t off = sec_v_scales(H, T) + (((size_t)head * T + j) * N_BLOCKS + block) * 2;
+    return oracle_f16_to_f64(read_u16(page + off));
+}
+
+/* Dequantised key / value element (exact in fp64). */
+double oracle_k_value(const uint8_t *page, int H, int T, int head, int j, int t) {
+    return oracle_k_scale(page, H, T, head, j, t / BLOCK) * (double)oracle_k_code(page, H, T, head, j, t);
+}
+
+double oracle_v_value(const uint8_t *page, int H, int T, int head, int j, int t) {
+    return oracle_v_scale(page, H, T, head, j, t / BLOCK) * (double)(oracle_v_code(page, H, T, head, j, t) - 8);
+}
+
+/* ---------------------------------------------------------------------- */
+/* Page-table resolution                                                   */
+/* ---------------------------------------------------------------------- */
+typedef struct {
+    const uint8_t *pool;    size_t n_pool;   /* pool pages */
+    const uint8_t *ring;    size_t n_ring;   /* ring slots */
+    const uint8_t *history;                  /* layer's host copy, logical order (may be NULL) */
+    size_t page_bytes;
+} oracle_store;
+
+/* Returns the page's bytes, or NULL when the entry names nothing valid. */
+static const uint8_t *resolve(const oracle_store *st, uint32_t entry, size_t logical_page) {
+    if (entry == 0xFFFFFFFFu) {
+        return st->history ? st->history + logical_page * st->page_bytes : NULL;
+    }
+    if (entry & 0x80000000u) {
+        size_t slot = entry & 0x7FFFFFFFu;
+        return slot < st->n_ring ? st->ring + slot * st->page_bytes : NULL;
+    }
+    return entry < st->n_pool ? st->pool + (size_t)entry * st->page_bytes : NULL;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Attention over one row / head: scores, softmax, weighted sum.           */
+/* A "key source" gives K-hat and V-hat rows of one KV head.               */
+/* ---------------------------------------------------------------------- */
+typedef struct {
+    /* paged */
+    const uint8_t *const *pages; int H; int T;
+    /* logical (unpaged): [N][H][128] codes, [N][H][4] scales */
+    const int8_t *kc; const uint16_t *kd; const uint8_t *vc; const uint16_t *vd;
+} key_source;
+
+static void k_row(const key_source *src, int g, int j, double *out) {
+    if (src->pages) {
+        const uint8_t *pg = src->pages[j / src->T];
+        for (int t = 0; t < HEAD_DIM; t++) out[t] = oracle_k_value(pg, src->H, src->T, g, j % src->T, t);
+    } else {
+        size_t row = ((size_t)j * src->H + g);
+        for (int t = 0; t < HEAD_DIM; t++)
+            out[t] = oracle_f16_to_f64(src->kd[row * N_BLOCKS + t / BLOCK]) * (double)src->kc[row * HEAD_DIM + t];
+    }
+}
+
+static void v_row(const key_source *src, int g, int j, double *out) {
+    if (src->pages) {
+        const uint8_t *pg = src->pages[j / src->T];
+        for (int t = 0; t < HEAD_DIM; t++) out[t] = oracle_v_value(pg, src->H, src->T, g, j % src->T, t);
+    } else {
+        size_t row = ((size_t)j * src->H + g);
+        for (int t = 0; t < HEAD_DIM; t++)
+            out[t] = oracle_f16_to_f64(src->vd[row * N_BLOCKS + t / BLOCK]) * ((double)src->vc[row * HEAD_DIM + t] - 8.0);
+    }
+}
+
+/* Softmax attention of query q (fp32, 128) over keys [k0, k1) of KV head g.
+ * Writes the un-normalised partial (m, l, acc) of the split: m = max score,
+ * l = sum exp(s - m), acc = sum exp(s - m) * v.  An empty range gives
+ * m = -inf, l = 0, acc = 0. */
+static void attend_range(const key_source *src, int g, const float *q, double scale, int k0, int k1,
+                         double *m_out, double *l_out, double *acc) {
+    double krow[HEAD_DIM], vrow[HEAD_DIM];
+    int n = k1 - k0;
+    memset(acc, 0, sizeof(double) * HEAD_DIM);
+    if (n <= 0) { *m_out = -INFINITY; *l_out = 0.0; return; }
+    double *s = (double *)malloc(sizeof(double) * (size_t)n);
+    double m = -INFINITY;
+    for (int j = k0; j < k1; j++) {
+        k_row(src, g, j, krow);
+        double dot = 0.0;
+        for (int t = 0; t < HEAD_DIM; t++) dot += (double)q[t] * krow[t];
+        s[j - k0] = scale * dot;
+        if (s[j - k0] > m) m = s[j - k0];
+    }
+    double l = 0.0;
+    for (int j = k0; j < k1; j++) {
+        double w = exp(s[j - k0] - m);
+        l += w;
+        v_row(src, g, j, vrow);
+        for (int t = 0; t < HEAD_DIM; t++) acc[t] += w * vrow[t];
+    }
+    free(s);
+    *m_out = m; *l_out = l;
+}
+
+/* Full attention for a list of rows. q: [W][Hq][128] fp32.  rows: which of
+ * the W rows to compute (NULL = all); out: [n_rows][Hq][128]; lse:
+ * [n_rows][Hq] natural-log sum-exp of the scaled scores. */
+static int attend_rows(const key_source *src, int n_tokens, int Hq, int Hkv, const float *q, int W,
+                       double scale, const int *rows, int n_rows, double *out, double *lse, int n_threads) {
+    if (Hkv <= 0 || Hq % Hkv != 0 || W <= 0 || W > n_tokens) return -1;
+    int G = Hq / Hkv;
+    if (!rows) n_rows = W;
+    int units = n_rows * Hq;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(n_threads > 0 ? n_threads : 1)
+    for (int u = 0; u < units; u++) {
+        int ri = u / Hq, h = u % Hq;
+        int r = rows ? rows[ri] : ri;
+        if (r < 0 || r >= W) { bad = 1; continue; }
+        int pos = n_tokens - W + r;               /* row's own position */
+        double m, l, acc[HEAD_DIM];
+        attend_range(src, h / G, q + ((size_t)r * Hq + h) * HEAD_DIM, scale, 0, pos + 1, &m, &l, acc);
+        double *o = out + ((size_t)ri * Hq + h) * HEAD_DIM;
+        for (int t = 0; t < HEAD_DIM; t++) o[t] = acc[t] / l;
+        if (lse) lse[(size_t)ri * Hq + h] = m + log(l);
+    }
+    return bad ? -1 : 0;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Public entry points                                                     */
+/* ---------------------------------------------------------------------- */
+
+/* Attention through a page table.  page_table[P] for P < ceil(N / T). */
+int oracle_attend_paged(const uint8_t *pool, size_t n_pool, const uint8_t *ring, size_t n_ring,
+                        const uint8_t *history, const uint32_t *page_table, int n_tokens, int page_tokens,
+                        int Hq, int Hkv, const float *q, int W, double scale, const int *rows, int n_rows,
+                        double *out, double *lse, int n_threads) {
+    if (n_tokens <= 0 || page_tokens <= 0 || page_tokens % 32 != 0) return -1;
+    oracle_store st = {pool, n_pool, ring, n_ring, history, oracle_page_bytes(Hkv, page_tokens)};
+    int n_pages = (n_tokens + page_tokens - 1) / page_tokens;
+    const uint8_t **pages = (const uint8_t **)malloc(sizeof(uint8_t *) * (size_t)n_pages);
+    for (int p = 0; p < n_pages; p++) {
+        pages[p] = resolve(&st, page_table[p], (size_t)p);
+        if (!pages[p]) { free(pages); return -2; }
+    }
+    key_source src = {pages, Hkv, page_tokens, NULL, NULL, NULL, NULL};
+    int rc = attend_rows(&src, n_tokens, Hq, Hkv, q, W, scale, rows, n_rows, out, lse, n_threads);
+    free(pages);
+    return rc;
+}
+
+/* Attention over unpaged logical arrays (the quantiser's own output). */
+int oracle_attend_logical(const int8_t *kc, const uint16_t *kd, const uint8_t *vc, const uint16_t *vd,
+                          int n_tokens, int Hq, int Hkv, const float *q, int W, double scale, const int *rows,
+                          int n_rows, double *out, double *lse, int n_threads) {
+    key_source src = {NULL, Hkv, 0, kc, kd, vc, vd};
+    return attend_rows(&src, n_tokens, Hq, Hkv, q, W, scale, rows, n_rows, out, lse, n_threads);
+}
+
+/* Split partials: keys of row r (0 .. pos_r) cut at the given boundaries
+ * (bounds[0] = 0 < ... < bounds[n_splits] >= n_tokens), each split reduced
+ * on its own to (m, l, acc).  Layout: m, l [n_splits][W][Hq]; acc
+ * [n_splits][W][Hq][128].  Keys beyond a row's position are excluded. */
+int oracle_split_partials(const uint8_t *const *pages, int page_tokens, int n_tokens, int Hq, int Hkv,
+                          const float *q, int W, double scale, const int *bounds, int n_splits,
+                          double *m, double *l, double *acc) {
+    if (Hkv <= 0 || Hq % Hkv != 0 || W <= 0 || W > n_tokens) return -1;
+    int G = Hq / Hkv;
+    key_source src = {pages, Hkv, page_tokens, NULL, NULL, NULL, NULL};
+    for (int s = 0; s < n_splits; s++)
+        for (int r = 0; r < W; r++)
+            for (int h = 0; h < Hq; h++) {
+                int pos = n_tokens - W + r;
+                int k0 = bounds[s], k1 = bounds[s + 1] < pos + 1 ? bounds[s + 1] : pos + 1;
+                size_t u = ((size_t)s * W + r) * Hq + h;
+                attend_range(&src, h / G, q + ((size_t)r * Hq + h) * HEAD_DIM, scale, k0, k1, &m[u], &l[u],
+                             acc + u * HEAD_DIM);
+            }
+    return 0;
+}
+
+/* Log-sum-exp merge of split partials, splits taken in index order:
+ *   M = max_s m_s;  L = sum_s e^(m_s - M) l_s;  O = sum_s e^(m_s - M) acc_s / L.
+ * Empty splits (l = 0) are skipped.  units = W * Hq. */
+int oracle_merge(const double *m, const double *l, const double *acc, int n_splits, int units, double *out) {
+    for (int u = 0; u < units; u++) {
+        double M = -INFINITY;
+        for (int s = 0; s < n_splits; s++)
+            if (l[(size_t)s * units + u] > 0.0 && m[(size_t)s * units + u] > M) M = m[(size_t)s * units + u];
+        double L = 0.0, o[HEAD_DIM];
+        memset(o, 0, sizeof(o));
+        for (int s = 0; s < n_splits; s++) {
+            size_t i = (size_t)s * units + u;
+            if (l[i] <= 0.0) continue;
+            double w = exp(m[i] - M);
+            L += w * l[i];
+            for (int t = 0; t < HEAD_DIM; t++) o[t] += w * acc[i * HEAD_DIM + t];
+        }
+        if (L <= 0.0) return -1;
+        for (int t = 0; t < HEAD_DIM; t++) out[(size_t)u * HEAD_DIM + t] = o[t] / L;
+    }
+    return 0;
+}
