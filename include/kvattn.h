@@ -1,0 +1,233 @@
+/*
+ * kvattn.h -- exact attention over a block-paged KV cache with Q8_0 keys and
+ * Q4_0 values, on AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes: for each query row, softmax attention over the
+ * complete, logically ordered KV history of a layer.  Where a page lives
+ * (resident pool page, caller-placed ring slot, or streamed from the pinned
+ * host history through the transfer ring) changes only the physical address
+ * the kernels read, never the attended history ("Adaptive KV Streaming for
+ * llama.cpp", section "Adaptive KV streaming"; "troed's fork of Raymond's
+ * adaptive KV streaming", sections "KV data movement and attention" and
+ * "Keep the stock attention order").  Per-split partial softmax results are
+ * merged by log-sum-exp in fixed logical order.
+ *
+ * Conventions (all entry points):
+ *   - Every call returns a kvattn_status; nothing aborts.  Unsupported
+ *     formats or shapes fail closed with KVATTN_E_UNSUPPORTED; there is no
+ *     silent fallback to another format ("troed's fork ...", section
+ *     "Required FlashAttention kernels", describes the trap of one).
+ *   - A rejected call enqueues no GPU work.
+ *   - All device buffers (pool, ring, workspace, q, out) and the pinned host
+ *     history are owned by the caller; the library keeps raw pointers and
+ *     never frees them.  They must outlive the handle.
+ *   - Compute is stream-ordered on the compute stream passed to
+ *     kvattn_create; outputs are valid once that stream has passed the call.
+ *   - One handle is used by one host thread at a time.
+ *   - Streams are passed as hipStream_t values cast to void *.
+ */
+#ifndef KVATTN_H
+#define KVATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct kvattn *kvattn_t;
+
+typedef enum kvattn_status {
+    KVATTN_OK = 0,
+    KVATTN_E_ARG = -1,         /* null pointer, zero size, W or R out of range, W > n_tokens */
+    KVATTN_E_UNSUPPORTED = -2, /* K/V type pair, head_dim, page size or geometry not implemented */
+    KVATTN_E_RANGE = -3,       /* layer, pool page or ring slot index out of range */
+    KVATTN_E_PLAN = -4,        /* page table with a duplicate physical page, or streamed pages
+                                  without a host history, or ring slots mixed with streaming */
+    KVATTN_E_NOSPACE = -5,     /* a caller buffer is smaller than the sizes below require */
+    KVATTN_E_STATE = -6,       /* call out of order (layer not set, handle destroyed, ...) */
+    KVATTN_E_HIP = -7          /* a HIP runtime call failed; kvattn_last_error names it */
+} kvattn_status;
+
+/* Block formats: 32 values per block, one IEEE binary16 scale d.
+ * Q8_0: 32 int8 codes c, value = d * c.  Q4_0: 32 4-bit codes n, value =
+ * d * (n - 8).  (The cache types the pages qualify: "troed's fork ...",
+ * section "Adaptive KV Streaming for llama.cpp V2": Q8_0 K / Q4_0 V.) */
+enum { KVATTN_TYPE_Q4_0 = 2, KVATTN_TYPE_Q8_0 = 8 };
+
+/* Page-table entries (one uint32 per logical page):
+ *   id < 0x80000000       resident pool page `id`
+ *   KVATTN_PT_RING(slot)  a ring slot the caller filled (kvattn_upload_pages)
+ *   KVATTN_PT_HOST        not resident: the scheduler streams logical page P
+ *                         from page P of the layer's pinned host history into
+ *                         a ring slot before the kernels read it. */
+#define KVATTN_PT_RING_FLAG 0x80000000u
+#define KVATTN_PT_RING(slot) (KVATTN_PT_RING_FLAG | (uint32_t)(slot))
+#define KVATTN_PT_HOST 0xFFFFFFFFu
+
+/*
+ * Page byte layout (head_dim 128, T = page_tokens, H = n_kv_heads), in
+ * order.  A page is T token positions of every KV head of one layer ("troed's
+ * fork ...", section "KV data movement and attention": 256 positions per
+ * page, K and V page sizes follow the quant types).  The code sections are
+ * tiled so that each lane of a 64-wide wavefront reads its matrix-core
+ * operand with one aligned 16-byte load.
+ *   1. K codes, int8, H*T*128 bytes.  Head h starts at h*T*128; 16-token
+ *      tiles of 2048 bytes.  In a tile, token j (0..15) and dim t have byte
+ *         (t/64)*1024 + (((t%32)/8)*16 + j)*16 + ((t/32)%2)*8 + t%8.
+ *   2. K scales, binary16 [H][T][4] (one per 32-dim block).
+ *   3. V codes, 4 bits, H*T*64 bytes.  Head h starts at h*T*64; 32-token
+ *      tiles of 2048 bytes.  In a tile, token j (0..31) and dim t have byte
+ *         (t/64)*1024 + (((j%16)/4)*16 + t%16)*16 + ((t/16)%4)*4 + j%4,
+ *      low nibble for j < 16, high nibble for j >= 16.
+ *   4. V scales, binary16 [H][T][4].
+ * Page size = H*T*208 bytes (425,984 at H = 8, T = 256).  Pool pages, ring
+ * slots and host-history pages all use this layout, so a host-to-device copy
+ * of a page is a plain memcpy.
+ */
+
+/* Parameters.  Append-only: new fields go at the end, and struct_size (the
+ * caller's sizeof) tells the library which fields the caller knows. */
+typedef struct kvattn_params {
+    uint32_t struct_size;         /* sizeof(kvattn_params) as compiled by the caller */
+    uint32_t n_layers;            /* layers with their own page table (>= 1) */
+    uint32_t n_q_heads;           /* query heads; a multiple of n_kv_heads */
+    uint32_t n_kv_heads;          /* KV heads; query head h reads KV head h / (n_q_heads / n_kv_heads) */
+    uint32_t head_dim;            /* must be 128 */
+    uint32_t page_tokens;         /* token positions per page; a multiple of 32 (256 in the workloads) */
+    uint32_t k_type;              /* KVATTN_TYPE_Q8_0 */
+    uint32_t v_type;              /* KVATTN_TYPE_Q4_0 */
+    uint32_t n_pool_pages;        /* pages in the resident pool buffer */
+    uint32_t n_ring_slots;        /* pages in the ring buffer (0 = no ring) */
+    uint32_t max_pages_per_layer; /* upper bound of ceil(n_tokens / page_tokens) */
+    uint32_t max_rows;            /* upper bound of W (verify) and R (prefill chunk) */
+    float softmax_scale;          /* 0 => 1/sqrt(head_dim) */
+    uint32_t split_pages;         /* pages per split for narrow calls (rows per KV head <= 32);
+                                     0 => chosen from the page count and the CU count */
+    uint32_t chunk_slots;         /* ring slots per streamed chunk; 0 => 16 (clamped to the ring) */
+} kvattn_params;
+
+/* 1 if the K/V type pair and head_dim are implemented, else 0. */
+int kvattn_supported(uint32_t k_type, uint32_t v_type, uint32_t head_dim);
+
+/* Bytes of one page (0 if the parameters are invalid). */
+size_t kvattn_page_bytes(const kvattn_params *params);
+
+/* Bytes the caller must provide as d_workspace (0 if the parameters are
+ * invalid): device page tables, page lists, one staging page and the split
+ * partials (m, l, acc[128] per split, row and query head, fp32). */
+size_t kvattn_workspace_bytes(const kvattn_params *params);
+
+/*
+ * Create a handle.  d_pool: n_pool_pages pages (pool_bytes >= that);
+ * d_ring: n_ring_slots pages or NULL when n_ring_slots is 0; d_workspace:
+ * kvattn_workspace_bytes bytes.  compute_stream runs the kernels;
+ * copy_stream runs host-to-device page copies (it may equal compute_stream).
+ * The current HIP device must be the one that owns the buffers.
+ */
+int kvattn_create(const kvattn_params *params, void *d_pool, size_t pool_bytes, void *d_ring,
+                  size_t ring_bytes, void *d_workspace, size_t workspace_bytes, void *compute_stream,
+                  void *copy_stream, kvattn_t *out);
+
+/*
+ * Copy n pages from host memory h_pages (n * page_bytes, pinned for an
+ * asynchronous copy) to the pool pages or ring slots named by dst[i]
+ * (pool id, or KVATTN_PT_RING(slot)).  The copy runs on the copy stream;
+ * later compute on the compute stream waits for it.  h_pages must stay
+ * valid until the compute stream has passed the next call.
+ */
+int kvattn_upload_pages(kvattn_t h, const void *h_pages, const uint32_t *dst, uint32_t n);
+
+/*
+ * Set layer `layer`'s history: n_tokens positions in ceil(n_tokens /
+ * page_tokens) logical pages, page_table[P] naming where logical page P
+ * lives.  Rejects (KVATTN_E_PLAN) a table that names one physical page
+ * twice, names KVATTN_PT_HOST without a host history, or mixes
+ * caller-placed ring slots with streamed pages on one handle (the scheduler
+ * owns the ring once any page streams).  h_history: the layer's pages in
+ * logical order (ceil(n_tokens / page_tokens) pages, pinned host memory),
+ * read for KVATTN_PT_HOST entries; may be NULL when there are none.  The
+ * table is copied to the device (stream-ordered on the compute stream).
+ */
+int kvattn_set_layer(kvattn_t h, uint32_t layer, const uint32_t *page_table, uint32_t n_tokens,
+                     const void *h_history);
+
+/*
+ * Attention for W query rows at the tail of the layer's history (positions
+ * n_tokens - W .. n_tokens - 1, causal among themselves: row r sees keys
+ * 0 .. n_tokens - W + r).  d_q: fp32 [W][n_q_heads][128]; d_out: fp32
+ * [W][n_q_heads][128].  Both device memory.  Decode is W = 1
+ * (TG1); verify is 1 + the draft length ("troed's fork ...", footnote 1).
+ * 1 <= W <= min(max_rows, n_tokens).
+ */
+int kvattn_decode(kvattn_t h, uint32_t layer, const float *d_q, float *d_out);
+int kvattn_verify(kvattn_t h, uint32_t layer, const float *d_q, uint32_t W, float *d_out);
+
+/*
+ * Prefill chunk: R query rows whose own keys are already the last R
+ * positions of the history (row r sees keys 0 .. n_tokens - R + r).  Uses
+ * the matrix-core path with splits sized for many rows ("Adaptive KV
+ * Streaming for llama.cpp", section "Batch and micro-batch sizes").  The
+ * layer must have no streamed (KVATTN_PT_HOST) pages.
+ * 1 <= R <= min(max_rows, n_tokens).
+ */
+int kvattn_prefill_chunk(kvattn_t h, uint32_t layer, const float *d_q, uint32_t R, float *d_out);
+
+/* Block the host until both streams have finished the handle's work. */
+int kvattn_synchronize(kvattn_t h);
+
+/*
+ * Test aid: copy the bytes of `layer`'s logical page through the kernels'
+ * own device-side page resolver into h_out (page_bytes of host memory).
+ * Synchronous.  Streamed pages resolve to their most recently assigned
+ * ring slot.
+ */
+int kvattn_debug_read_page(kvattn_t h, uint32_t layer, uint32_t logical_page, void *h_out);
+
+/*
+ * Host only (no GPU work): the page-table checks kvattn_set_layer applies
+ * that need no handle state -- range of pool ids and ring slots, no physical
+ * page named twice, streamed pages need a host history (has_history != 0)
+ * and a ring, page count within max_pages_per_layer.  Returns the status
+ * kvattn_set_layer would return; the message is in kvattn_global_error().
+ */
+int kvattn_validate_page_table(const kvattn_params *params, const uint32_t *page_table, uint32_t n_tokens,
+                               int has_history);
+
+/*
+ * Test aid, host only (no GPU work): run the streaming planner over a
+ * sequence of layer calls (call_layers[0 .. n_calls), layers with no streamed
+ * pages skipped) for layers whose streamed-page counts are
+ * streamed_counts[0 .. n_layers), and log the enqueue sequence the HIP path
+ * issues.  Each op is 7 int64 values: kind (1 = copy a chunk on the copy
+ * stream after waiting on consumed[wait] when wait >= 0, then record
+ * ready[event]; 2 = wait ready[event], compute the chunk, record
+ * consumed[event]; 3 = drain both streams; 4 = merge the layer; 5 =
+ * compute the layer's resident pages; 6 = the layer's call has begun:
+ * copies logged after it may run one streamed layer ahead of it), layer,
+ * first and count (the chunk's
+ * range of the layer's streamed pages, in logical order), ordinal base
+ * (streamed page o sits in ring slot (base + o) mod n_slots), event, wait.
+ * ops holds max_ops * 7 values; *n_ops receives the count.
+ */
+int kvattn_sched_simulate(uint32_t n_layers, uint32_t n_slots, uint32_t chunk_slots, const uint32_t *streamed_counts,
+                          const uint32_t *call_layers, uint32_t n_calls, int64_t *ops, uint32_t max_ops,
+                          uint32_t *n_ops);
+
+/* Drain both streams, release events, free the handle (NULL is a no-op). */
+int kvattn_destroy(kvattn_t h);
+
+/* Message of the handle's last failed call ("" if none); static text for
+ * NULL.  Valid until the next call on the handle. */
+const char *kvattn_last_error(kvattn_t h);
+
+/* Message of the last failure of a call that had no handle to report on
+ * (kvattn_create).  Thread-local. */
+const char *kvattn_global_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVATTN_H */

@@ -1,0 +1,54 @@
+"""Build the HIP library in-tree: long_context_attention_amd/libkvattn.so (gfx950)."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libkvattn.so")
+SOURCES = ["kvattn.hip", "attn_kernels.hip"]
+HEADERS = ["attn_kernels.h", "sched.h"]
+
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    # packed fp32 instructions stay off (the compiler would otherwise form them)
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def hipcc() -> str:
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    return os.path.join(rocm, "bin", "hipcc")
+
+
+def build(verbose: bool = False) -> str:
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), *FLAGS, "-I", os.path.join(os.path.dirname(HERE), "include"), "-o", tmp, *srcs]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "'-packed-fp32-ops' is not a recognized feature"
+    errs = "\n".join(l for l in (proc.stderr or "").splitlines() if noise not in l)
+    if proc.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{errs}")
+    if verbose and errs.strip():
+        print(errs, file=sys.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def is_stale() -> bool:
+    if not os.path.exists(LIB):
+        return True
+    t = os.path.getmtime(LIB)
+    deps = [os.path.join(CSRC, f) for f in SOURCES + HEADERS]
+    deps.append(os.path.join(os.path.dirname(HERE), "include", "kvattn.h"))
+    return any(os.path.getmtime(d) > t for d in deps)
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,40 @@
+// attn_kernels.h -- kernel arguments and launchers shared by the host code.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+struct SplitArgs {
+    const uint8_t *pool;          // resident pool pages
+    const uint8_t *ring;          // ring slots
+    const uint32_t *page_table;   // this layer's device entries (see resolve_page)
+    const uint32_t *page_list;    // optional: logical pages, one split each (nullptr = ranges)
+    uint32_t list_offset;         // first page_list entry of this launch
+    uint32_t n_tokens;            // history length N
+    uint32_t n_pages;             // ceil(N / T)
+    uint32_t T;                   // tokens per page
+    uint32_t W;                   // query rows (positions)
+    uint32_t Hq, Hkv, G;          // query heads, KV heads, Hq / Hkv
+    uint32_t split_pages;         // pages per split when page_list is null
+    uint32_t ring_base;           // ring slot of streamed ordinal 0 (mod n_ring_slots)
+    uint32_t n_ring_slots;
+    size_t page_bytes;
+    size_t sec_kd, sec_vc, sec_vd; // section offsets inside a page
+    float qscale;                 // softmax_scale * log2(e)
+    const float *q;               // [W][Hq][128]
+    float *part_o;                // [splits][W*Hq][128]
+    float *part_ml;               // [splits][W*Hq][2]
+};
+
+struct MergeArgs {
+    const float *part_o;
+    const float *part_ml;
+    uint32_t n_splits;
+    uint32_t units;               // W * Hq
+    float *out;                   // [W][Hq][128]
+};
+
+size_t kvattn_split_smem_bytes(int nrt);
+hipError_t kvattn_launch_split(const SplitArgs &a, uint32_t n_items, uint32_t n_row_blocks, int nrt, hipStream_t s);
+hipError_t kvattn_launch_merge(const MergeArgs &a, hipStream_t s);
+hipError_t kvattn_launch_read_page(const SplitArgs &a, uint32_t logical_page, uint8_t *dst, hipStream_t s);

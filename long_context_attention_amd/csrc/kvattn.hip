@@ -1,0 +1,711 @@
+// kvattn.hip -- C-ABI of the paged Q8_0-K / Q4_0-V attention library.
+//
+// Host side: argument and page-table validation, the split plan, kernel
+// launches, and the single-GPU streaming scheduler that copies non-resident
+// pages from the pinned host history into ring slots on a side stream, one
+// layer ahead, and recycles each slot once its consumer has run ("troed's
+// fork of Raymond's adaptive KV streaming", section "KV data movement and
+// attention": ready fence before a read, consumed fence before reuse;
+// "Adaptive KV Streaming for llama.cpp", section "Adaptive KV streaming").
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/kvattn.h"
+#include "attn_kernels.h"
+#include "sched.h"
+
+namespace {
+
+constexpr uint32_t kHeadDim = 128;
+constexpr uint32_t kNarrowRows = 32;      // rows per KV head handled with the verify split plan
+constexpr uint32_t kPrefillMaxSplits = 16;
+constexpr uint32_t kEntryStream = 0xC0000000u;  // device entry tag: streamed ordinal
+constexpr size_t kAlign = 256;
+
+thread_local std::string g_error;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+    size_t page_bytes, sec_kd, sec_vc, sec_vd;
+};
+
+Layout page_layout(uint32_t H, uint32_t T) {
+    Layout l;
+    l.sec_kd = (size_t)H * T * kHeadDim;
+    l.sec_vc = l.sec_kd + (size_t)H * T * 8;
+    l.sec_vd = l.sec_vc + (size_t)H * T * (kHeadDim / 2);
+    l.page_bytes = l.sec_vd + (size_t)H * T * 8;
+    return l;
+}
+
+// Reads the caller's params honouring struct_size (append-only struct).
+bool read_params(const kvattn_params *in, kvattn_params *out) {
+    if (!in || in->struct_size < offsetof(kvattn_params, split_pages)) return false;
+    std::memset(out, 0, sizeof(*out));
+    std::memcpy(out, in, std::min<size_t>(in->struct_size, sizeof(*out)));
+    out->struct_size = sizeof(*out);
+    return true;
+}
+
+int check_params(const kvattn_params &p, std::string &why) {
+    if (p.n_layers == 0 || p.n_q_heads == 0 || p.n_kv_heads == 0 || p.max_pages_per_layer == 0 || p.max_rows == 0) {
+        why = "n_layers, n_q_heads, n_kv_heads, max_pages_per_layer and max_rows must be >= 1";
+        return KVATTN_E_ARG;
+    }
+    if (p.k_type != KVATTN_TYPE_Q8_0 || p.v_type != KVATTN_TYPE_Q4_0) {
+        why = "only the Q8_0 K / Q4_0 V pair is implemented";
+        return KVATTN_E_UNSUPPORTED;
+    }
+    if (p.head_dim != kHeadDim) {
+        why = "only head_dim 128 is implemented";
+        return KVATTN_E_UNSUPPORTED;
+    }
+    if (p.page_tokens == 0 || p.page_tokens % 32 != 0) {
+        why = "page_tokens must be a positive multiple of 32";
+        return KVATTN_E_UNSUPPORTED;
+    }
+    if (p.n_q_heads % p.n_kv_heads != 0) {
+        why = "n_q_heads must be a multiple of n_kv_heads";
+        return KVATTN_E_UNSUPPORTED;
+    }
+    if (p.n_kv_heads > 65535) {
+        why = "n_kv_heads too large";
+        return KVATTN_E_UNSUPPORTED;
+    }
+    if (p.n_pool_pages >= 0x80000000u || p.n_ring_slots >= 0x40000000u || p.max_pages_per_layer >= 0x40000000u) {
+        why = "pool / ring / page counts exceed the page-table encoding";
+        return KVATTN_E_RANGE;
+    }
+    if (!(p.softmax_scale >= 0.f) || std::isinf(p.softmax_scale)) {
+        why = "softmax_scale must be finite and >= 0";
+        return KVATTN_E_ARG;
+    }
+    return KVATTN_OK;
+}
+
+// Partial-buffer capacity in (split, row, query head) units.
+size_t partial_units(const kvattn_params &p) {
+    const uint32_t G = p.n_q_heads / p.n_kv_heads;
+    const uint64_t narrow_w = std::min<uint64_t>(p.max_rows, std::max<uint32_t>(1, kNarrowRows / G));
+    const uint64_t narrow = (uint64_t)p.max_pages_per_layer * narrow_w * p.n_q_heads;
+    const uint64_t wide = (uint64_t)std::min(kPrefillMaxSplits, p.max_pages_per_layer) * p.max_rows * p.n_q_heads;
+    return (size_t)std::max(narrow, wide);
+}
+
+struct WsLayout {
+    size_t tables, lists, staging, part_ml, part_o, total;
+};
+
+WsLayout workspace_layout(const kvattn_params &p) {
+    WsLayout w;
+    const size_t ents = (size_t)p.n_layers * p.max_pages_per_layer * sizeof(uint32_t);
+    const size_t units = partial_units(p);
+    w.tables = 0;
+    w.lists = align_up(ents);
+    w.staging = w.lists + align_up(ents);
+    w.part_ml = w.staging + align_up(page_layout(p.n_kv_heads, p.page_tokens).page_bytes);
+    w.part_o = w.part_ml + align_up(units * 2 * sizeof(float));
+    w.total = w.part_o + align_up(units * kHeadDim * sizeof(float));
+    return w;
+}
+
+// Planner plus the events the copy and compute streams exchange.
+class StreamScheduler : public StreamPlanner {
+   public:
+    bool init(uint32_t n_layers, uint32_t n_slots, uint32_t chunk) {
+        StreamPlanner::init(n_layers, n_slots, chunk);
+        ready_.assign(n_events(), nullptr);
+        consumed_.assign(n_events(), nullptr);
+        for (int i = 0; i < n_events(); i++) {
+            if (hipEventCreateWithFlags(&ready_[i], hipEventDisableTiming) != hipSuccess) return false;
+            if (hipEventCreateWithFlags(&consumed_[i], hipEventDisableTiming) != hipSuccess) return false;
+        }
+        return true;
+    }
+    void destroy() {
+        for (hipEvent_t e : ready_)
+            if (e) (void)hipEventDestroy(e);
+        for (hipEvent_t e : consumed_)
+            if (e) (void)hipEventDestroy(e);
+        ready_.clear();
+        consumed_.clear();
+    }
+    hipEvent_t ready_event(int i) const { return ready_[i]; }
+    hipEvent_t consumed_event(int i) const { return consumed_[i]; }
+
+   private:
+    std::vector<hipEvent_t> ready_, consumed_;
+};
+
+struct LayerState {
+    bool set = false;
+    uint32_t n_tokens = 0, n_pages = 0;
+    uint32_t n_resident = 0, n_streamed = 0;
+    bool uses_ring_slots = false;
+    const uint8_t *history = nullptr;
+    std::vector<uint32_t> resident;   // logical pages, ascending
+    std::vector<uint32_t> streamed;   // logical pages, ascending (ordinal order)
+};
+
+}  // namespace
+
+struct kvattn {
+    kvattn_params p{};
+    Layout lay{};
+    WsLayout ws{};
+    uint8_t *pool = nullptr, *ring = nullptr, *wsp = nullptr;
+    size_t pool_bytes = 0, ring_bytes = 0, ws_bytes = 0;
+    hipStream_t compute = nullptr, copy = nullptr;
+    int device = 0;
+    hipEvent_t upload_done = nullptr;
+    std::vector<LayerState> layers;
+    StreamScheduler sched;
+    bool any_streamed = false, any_ring_slots = false;
+    std::string err;
+    float qscale = 0.f;
+
+    uint32_t *d_table(uint32_t layer) { return reinterpret_cast<uint32_t *>(wsp + ws.tables) + (size_t)layer * p.max_pages_per_layer; }
+    uint32_t *d_list(uint32_t layer) { return reinterpret_cast<uint32_t *>(wsp + ws.lists) + (size_t)layer * p.max_pages_per_layer; }
+    float *part_ml() { return reinterpret_cast<float *>(wsp + ws.part_ml); }
+    float *part_o() { return reinterpret_cast<float *>(wsp + ws.part_o); }
+};
+
+namespace {
+
+int fail(kvattn_t h, int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    if (h)
+        h->err = buf;
+    else
+        g_error = buf;
+    return code;
+}
+
+#define HIP_TRY(h, call)                                                                            \
+    do {                                                                                            \
+        hipError_t e_ = (call);                                                                     \
+        if (e_ != hipSuccess) return fail((h), KVATTN_E_HIP, "%s failed: %s", #call, hipGetErrorString(e_)); \
+    } while (0)
+
+SplitArgs base_args(kvattn_t h, uint32_t layer, uint32_t W, const float *q) {
+    const LayerState &L = h->layers[layer];
+    SplitArgs a{};
+    a.pool = h->pool;
+    a.ring = h->ring;
+    a.page_table = h->d_table(layer);
+    a.page_list = nullptr;
+    a.list_offset = 0;
+    a.n_tokens = L.n_tokens;
+    a.n_pages = L.n_pages;
+    a.T = h->p.page_tokens;
+    a.W = W;
+    a.Hq = h->p.n_q_heads;
+    a.Hkv = h->p.n_kv_heads;
+    a.G = h->p.n_q_heads / h->p.n_kv_heads;
+    a.split_pages = 1;
+    a.ring_base = 0;
+    a.n_ring_slots = std::max<uint32_t>(1, h->p.n_ring_slots);
+    a.page_bytes = h->lay.page_bytes;
+    a.sec_kd = h->lay.sec_kd;
+    a.sec_vc = h->lay.sec_vc;
+    a.sec_vd = h->lay.sec_vd;
+    a.qscale = h->qscale;
+    a.q = q;
+    a.part_o = h->part_o();
+    a.part_ml = h->part_ml();
+    return a;
+}
+
+// Split plan of a call on an all-resident layer.
+struct Plan {
+    uint32_t split_pages, n_splits, n_row_blocks;
+    int nrt;
+};
+
+Plan plan_resident(const kvattn_params &p, uint32_t n_pages, uint32_t W, bool prefill, int n_cus) {
+    const uint32_t G = p.n_q_heads / p.n_kv_heads;
+    const uint32_t rows = W * G;
+    Plan pl;
+    pl.nrt = rows <= 16 ? 1 : 2;
+    pl.n_row_blocks = (rows + 31) / 32;
+    if (pl.nrt == 1) pl.n_row_blocks = 1;
+    if (!prefill && rows <= kNarrowRows) {
+        uint32_t sp = p.split_pages;
+        if (sp == 0) {
+            // enough workgroups to cover every CU about four times
+            const uint64_t target = 4ull * (uint64_t)std::max(n_cus, 1);
+            sp = (uint32_t)std::max<uint64_t>(1, ((uint64_t)n_pages * p.n_kv_heads) / target);
+        }
+        pl.split_pages = std::min(sp, n_pages);
+    } else {
+        const uint64_t target = 8ull * (uint64_t)std::max(n_cus, 1);
+        uint64_t per = (uint64_t)p.n_kv_heads * pl.n_row_blocks;
+        uint32_t splits = (uint32_t)std::min<uint64_t>(kPrefillMaxSplits, std::max<uint64_t>(1, target / per));
+        splits = std::min(splits, n_pages);
+        pl.split_pages = (n_pages + splits - 1) / splits;
+    }
+    pl.n_splits = (n_pages + pl.split_pages - 1) / pl.split_pages;
+    return pl;
+}
+
+int validate_call(kvattn_t h, uint32_t layer, const float *q, uint32_t W, const float *out) {
+    if (!h) return fail(nullptr, KVATTN_E_ARG, "null handle");
+    if (layer >= h->p.n_layers) return fail(h, KVATTN_E_RANGE, "layer %u out of range (n_layers %u)", layer, h->p.n_layers);
+    const LayerState &L = h->layers[layer];
+    if (!L.set) return fail(h, KVATTN_E_STATE, "layer %u has no history (kvattn_set_layer first)", layer);
+    if (!q || !out) return fail(h, KVATTN_E_ARG, "null q or out");
+    if (W == 0 || W > h->p.max_rows) return fail(h, KVATTN_E_ARG, "row count %u outside 1..max_rows (%u)", W, h->p.max_rows);
+    if (W > L.n_tokens) return fail(h, KVATTN_E_ARG, "row count %u exceeds the history length %u", W, L.n_tokens);
+    return KVATTN_OK;
+}
+
+int run_merge(kvattn_t h, uint32_t W, uint32_t n_splits, float *out) {
+    MergeArgs m;
+    m.part_o = h->part_o();
+    m.part_ml = h->part_ml();
+    m.n_splits = n_splits;
+    m.units = W * h->p.n_q_heads;
+    m.out = out;
+    HIP_TRY(h, kvattn_launch_merge(m, h->compute));
+    return KVATTN_OK;
+}
+
+int n_cus_of(int device) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || v <= 0) v = 256;
+    return v;
+}
+
+// Attention on a layer without streamed pages.
+int attend_resident(kvattn_t h, uint32_t layer, const float *q, uint32_t W, float *out, bool prefill) {
+    const LayerState &L = h->layers[layer];
+    Plan pl = plan_resident(h->p, L.n_pages, W, prefill, n_cus_of(h->device));
+    SplitArgs a = base_args(h, layer, W, q);
+    a.split_pages = pl.split_pages;
+    HIP_TRY(h, kvattn_launch_split(a, pl.n_splits, pl.n_row_blocks, pl.nrt, h->compute));
+    return run_merge(h, W, pl.n_splits, out);
+}
+
+// One streamed layer's enqueue sequence, shared by the HIP path and the CPU
+// simulator (kvattn_sched_simulate): resident pages first (no wait), then
+// each ring chunk after its ready fence, recording its consumed fence; the
+// copies of later chunks and of the next streamed layer are enqueued as soon
+// as the fence each depends on has been recorded.
+template <class Exec>
+int drive_streamed_layer(StreamPlanner &pl, uint32_t layer, Exec &x) {
+    int rc;
+    if (!pl.begin_layer(layer)) {
+        if ((rc = x.drain())) return rc;  // out-of-order call: restart the schedule here
+        pl.restart(layer);
+        if (!pl.begin_layer(layer)) return x.internal("schedule restart failed");
+    }
+    x.begin(layer);
+    ChunkRef c;
+    while (pl.next_copy(&c))
+        if ((rc = x.copy(c))) return rc;
+    if ((rc = x.resident(layer))) return rc;
+    while (pl.next_compute(layer, &c)) {
+        if ((rc = x.compute(c))) return rc;
+        pl.mark_consumed(c);
+        while (pl.next_copy(&c))
+            if ((rc = x.copy(c))) return rc;
+    }
+    pl.end_layer(layer);
+    while (pl.next_copy(&c))
+        if ((rc = x.copy(c))) return rc;
+    return x.merge(layer);
+}
+
+struct HipExec {
+    kvattn_t h;
+    uint32_t W;
+    const float *q;
+    float *out;
+    SplitArgs a;
+    int nrt;
+
+    int drain() {
+        HIP_TRY(h, hipStreamSynchronize(h->copy));
+        HIP_TRY(h, hipStreamSynchronize(h->compute));
+        return KVATTN_OK;
+    }
+    int internal(const char *what) { return fail(h, KVATTN_E_STATE, "%s", what); }
+    void begin(uint32_t) {}
+    // Runs of consecutive logical pages landing in consecutive ring slots
+    // become one hipMemcpyAsync each.
+    int copy(const ChunkRef &c) {
+        const LayerState &L = h->layers[c.layer];
+        if (c.wait_event >= 0) HIP_TRY(h, hipStreamWaitEvent(h->copy, h->sched.consumed_event(c.wait_event), 0));
+        const size_t pb = h->lay.page_bytes;
+        uint32_t o = c.first;
+        while (o < c.first + c.count) {
+            const uint32_t slot = (uint32_t)((c.ordinal_base + o) % h->p.n_ring_slots);
+            uint32_t run = 1;
+            while (o + run < c.first + c.count && L.streamed[o + run] == L.streamed[o] + run && slot + run < h->p.n_ring_slots) run++;
+            HIP_TRY(h, hipMemcpyAsync(h->ring + (size_t)slot * pb, L.history + (size_t)L.streamed[o] * pb, (size_t)run * pb,
+                                      hipMemcpyHostToDevice, h->copy));
+            o += run;
+        }
+        HIP_TRY(h, hipEventRecord(h->sched.ready_event(c.event), h->copy));
+        return KVATTN_OK;
+    }
+    int resident(uint32_t layer) {
+        const LayerState &L = h->layers[layer];
+        if (!L.n_resident) return KVATTN_OK;
+        a.list_offset = 0;
+        HIP_TRY(h, kvattn_launch_split(a, L.n_resident, 1, nrt, h->compute));
+        return KVATTN_OK;
+    }
+    int compute(const ChunkRef &c) {
+        const LayerState &L = h->layers[c.layer];
+        HIP_TRY(h, hipStreamWaitEvent(h->compute, h->sched.ready_event(c.event), 0));
+        a.list_offset = L.n_resident + c.first;
+        a.ring_base = (uint32_t)(c.ordinal_base % h->p.n_ring_slots);
+        HIP_TRY(h, kvattn_launch_split(a, c.count, 1, nrt, h->compute));
+        HIP_TRY(h, hipEventRecord(h->sched.consumed_event(c.event), h->compute));
+        return KVATTN_OK;
+    }
+    int merge(uint32_t layer) { return run_merge(h, W, h->layers[layer].n_pages, out); }
+};
+
+int attend_streamed(kvattn_t h, uint32_t layer, const float *q, uint32_t W, float *out) {
+    const uint32_t G = h->p.n_q_heads / h->p.n_kv_heads;
+    if (W * G > kNarrowRows)
+        return fail(h, KVATTN_E_UNSUPPORTED, "streamed layers support at most %u rows per KV head (W*G = %u)", kNarrowRows, W * G);
+    HipExec x{h, W, q, out, base_args(h, layer, W, q), W * G <= 16 ? 1 : 2};
+    x.a.page_list = h->d_list(layer);
+    x.a.split_pages = 1;
+    return drive_streamed_layer(h->sched, layer, x);
+}
+
+// CPU simulator executor: logs the enqueue sequence.
+struct SimExec {
+    int64_t *ops;
+    uint32_t max_ops, n = 0;
+    bool overflow = false;
+    void put(int64_t kind, int64_t layer, int64_t first, int64_t count, int64_t base, int64_t ev, int64_t wait) {
+        if (n >= max_ops) {
+            overflow = true;
+            return;
+        }
+        int64_t *o = ops + (size_t)n * 7;
+        o[0] = kind, o[1] = layer, o[2] = first, o[3] = count, o[4] = base, o[5] = ev, o[6] = wait;
+        n++;
+    }
+    int drain() {
+        put(3, -1, 0, 0, 0, -1, -1);
+        return 0;
+    }
+    int internal(const char *) { return KVATTN_E_STATE; }
+    void begin(uint32_t layer) { put(6, layer, 0, 0, 0, -1, -1); }
+    int copy(const ChunkRef &c) {
+        put(1, c.layer, c.first, c.count, (int64_t)c.ordinal_base, c.event, c.wait_event);
+        return 0;
+    }
+    int resident(uint32_t layer) {
+        put(5, layer, 0, 0, 0, -1, -1);
+        return 0;
+    }
+    int compute(const ChunkRef &c) {
+        put(2, c.layer, c.first, c.count, (int64_t)c.ordinal_base, c.event, -1);
+        return 0;
+    }
+    int merge(uint32_t layer) {
+        put(4, layer, 0, 0, 0, -1, -1);
+        return 0;
+    }
+};
+
+// Page-table checks of kvattn_set_layer that need no handle state.
+int validate_table(kvattn_t h, const kvattn_params &p, const uint32_t *page_table, uint32_t n_tokens, bool has_history,
+                   PlanCheck *chk, uint32_t *n_pages_out) {
+    if (!page_table || n_tokens == 0) return fail(h, KVATTN_E_ARG, "null page table or zero tokens");
+    const uint32_t T = p.page_tokens;
+    const uint32_t n_pages = (uint32_t)(((uint64_t)n_tokens + T - 1) / T);
+    if (n_pages > p.max_pages_per_layer)
+        return fail(h, KVATTN_E_NOSPACE, "%u pages exceed max_pages_per_layer %u", n_pages, p.max_pages_per_layer);
+    int rc = check_page_table(page_table, n_pages, p.n_pool_pages, p.n_ring_slots, chk);
+    if (rc == PT_BAD_POOL) return fail(h, KVATTN_E_RANGE, "page %u: pool page out of range", chk->bad_index);
+    if (rc == PT_BAD_RING) return fail(h, KVATTN_E_RANGE, "page %u: ring slot out of range", chk->bad_index);
+    if (rc == PT_DUPLICATE)
+        return fail(h, KVATTN_E_PLAN, "page %u names a physical page already used by page %u", chk->bad_index, chk->other_index);
+    if (chk->n_host && !has_history) return fail(h, KVATTN_E_PLAN, "%u streamed pages but no host history", chk->n_host);
+    if (chk->n_host && p.n_ring_slots == 0) return fail(h, KVATTN_E_PLAN, "streamed pages need a ring (n_ring_slots is 0)");
+    *n_pages_out = n_pages;
+    return KVATTN_OK;
+}
+
+int attend(kvattn_t h, uint32_t layer, const float *q, uint32_t W, float *out, bool prefill) {
+    int rc = validate_call(h, layer, q, W, out);
+    if (rc) return rc;
+    const LayerState &L = h->layers[layer];
+    if (L.n_streamed) {
+        if (prefill) return fail(h, KVATTN_E_UNSUPPORTED, "prefill chunks need an all-resident layer (layer %u streams %u pages)", layer, L.n_streamed);
+        return attend_streamed(h, layer, q, W, out);
+    }
+    return attend_resident(h, layer, q, W, out, prefill);
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+extern "C" {
+
+int kvattn_supported(uint32_t k_type, uint32_t v_type, uint32_t head_dim) {
+    return k_type == KVATTN_TYPE_Q8_0 && v_type == KVATTN_TYPE_Q4_0 && head_dim == kHeadDim;
+}
+
+size_t kvattn_page_bytes(const kvattn_params *params) {
+    kvattn_params p;
+    std::string why;
+    if (!read_params(params, &p) || check_params(p, why) != KVATTN_OK) return 0;
+    return page_layout(p.n_kv_heads, p.page_tokens).page_bytes;
+}
+
+size_t kvattn_workspace_bytes(const kvattn_params *params) {
+    kvattn_params p;
+    std::string why;
+    if (!read_params(params, &p) || check_params(p, why) != KVATTN_OK) return 0;
+    return workspace_layout(p).total;
+}
+
+int kvattn_create(const kvattn_params *params, void *d_pool, size_t pool_bytes, void *d_ring, size_t ring_bytes,
+                  void *d_workspace, size_t workspace_bytes, void *compute_stream, void *copy_stream, kvattn_t *out) {
+    if (!out) return fail(nullptr, KVATTN_E_ARG, "null output handle pointer");
+    *out = nullptr;
+    kvattn_params p;
+    if (!read_params(params, &p)) return fail(nullptr, KVATTN_E_ARG, "null params or struct_size too small");
+    std::string why;
+    int rc = check_params(p, why);
+    if (rc) return fail(nullptr, rc, "%s", why.c_str());
+    const Layout lay = page_layout(p.n_kv_heads, p.page_tokens);
+    const WsLayout ws = workspace_layout(p);
+    if (p.n_pool_pages && !d_pool) return fail(nullptr, KVATTN_E_ARG, "null pool with n_pool_pages > 0");
+    if (p.n_ring_slots && !d_ring) return fail(nullptr, KVATTN_E_ARG, "null ring with n_ring_slots > 0");
+    if (!d_workspace) return fail(nullptr, KVATTN_E_ARG, "null workspace");
+    if (pool_bytes < (size_t)p.n_pool_pages * lay.page_bytes)
+        return fail(nullptr, KVATTN_E_NOSPACE, "pool_bytes %zu < %u pages x %zu", pool_bytes, p.n_pool_pages, lay.page_bytes);
+    if (ring_bytes < (size_t)p.n_ring_slots * lay.page_bytes)
+        return fail(nullptr, KVATTN_E_NOSPACE, "ring_bytes %zu < %u slots x %zu", ring_bytes, p.n_ring_slots, lay.page_bytes);
+    if (workspace_bytes < ws.total)
+        return fail(nullptr, KVATTN_E_NOSPACE, "workspace_bytes %zu < required %zu", workspace_bytes, ws.total);
+    if ((reinterpret_cast<uintptr_t>(d_pool) | reinterpret_cast<uintptr_t>(d_ring) | reinterpret_cast<uintptr_t>(d_workspace)) & 15)
+        return fail(nullptr, KVATTN_E_ARG, "pool, ring and workspace must be 16-byte aligned");
+
+    kvattn *h = new (std::nothrow) kvattn();
+    if (!h) return fail(nullptr, KVATTN_E_NOSPACE, "out of host memory");
+    h->p = p;
+    h->lay = lay;
+    h->ws = ws;
+    h->pool = static_cast<uint8_t *>(d_pool);
+    h->ring = static_cast<uint8_t *>(d_ring);
+    h->wsp = static_cast<uint8_t *>(d_workspace);
+    h->pool_bytes = pool_bytes;
+    h->ring_bytes = ring_bytes;
+    h->ws_bytes = workspace_bytes;
+    h->compute = static_cast<hipStream_t>(compute_stream);
+    h->copy = copy_stream ? static_cast<hipStream_t>(copy_stream) : h->compute;
+    const float scale = p.softmax_scale > 0.f ? p.softmax_scale : 1.0f / std::sqrt((float)kHeadDim);
+    h->qscale = scale * 1.4426950408889634f;
+    h->layers.resize(p.n_layers);
+    hipError_t e = hipGetDevice(&h->device);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&h->upload_done, hipEventDisableTiming);
+    if (e != hipSuccess) {
+        int code = fail(nullptr, KVATTN_E_HIP, "device / event setup failed: %s", hipGetErrorString(e));
+        delete h;
+        return code;
+    }
+    const uint32_t chunk = p.chunk_slots ? p.chunk_slots : 16;
+    if (p.n_ring_slots) {
+        if (!h->sched.init(p.n_layers, p.n_ring_slots, std::min(chunk, p.n_ring_slots))) {
+            (void)hipEventDestroy(h->upload_done);
+            delete h;
+            return fail(nullptr, KVATTN_E_HIP, "ring event setup failed");
+        }
+    }
+    *out = h;
+    return KVATTN_OK;
+}
+
+int kvattn_upload_pages(kvattn_t h, const void *h_pages, const uint32_t *dst, uint32_t n) {
+    if (!h) return fail(nullptr, KVATTN_E_ARG, "null handle");
+    if (n == 0) return KVATTN_OK;
+    if (!h_pages || !dst) return fail(h, KVATTN_E_ARG, "null host pages or destination list");
+    for (uint32_t i = 0; i < n; i++) {
+        uint32_t e = dst[i];
+        if (e & KVATTN_PT_RING_FLAG) {
+            uint32_t s = e & ~KVATTN_PT_RING_FLAG;
+            if (e == KVATTN_PT_HOST || s >= h->p.n_ring_slots) return fail(h, KVATTN_E_RANGE, "destination %u: ring slot out of range", i);
+            if (h->any_streamed) return fail(h, KVATTN_E_PLAN, "the ring belongs to the streaming scheduler on this handle");
+        } else if (e >= h->p.n_pool_pages) {
+            return fail(h, KVATTN_E_RANGE, "destination %u: pool page %u out of range (%u pages)", i, e, h->p.n_pool_pages);
+        }
+    }
+    const size_t pb = h->lay.page_bytes;
+    const uint8_t *src = static_cast<const uint8_t *>(h_pages);
+    for (uint32_t i = 0; i < n; i++) {
+        uint32_t e = dst[i];
+        uint8_t *d = (e & KVATTN_PT_RING_FLAG) ? h->ring + (size_t)(e & ~KVATTN_PT_RING_FLAG) * pb : h->pool + (size_t)e * pb;
+        HIP_TRY(h, hipMemcpyAsync(d, src + (size_t)i * pb, pb, hipMemcpyHostToDevice, h->copy));
+    }
+    if (h->copy != h->compute) {
+        HIP_TRY(h, hipEventRecord(h->upload_done, h->copy));
+        HIP_TRY(h, hipStreamWaitEvent(h->compute, h->upload_done, 0));
+    }
+    return KVATTN_OK;
+}
+
+int kvattn_set_layer(kvattn_t h, uint32_t layer, const uint32_t *page_table, uint32_t n_tokens, const void *h_history) {
+    if (!h) return fail(nullptr, KVATTN_E_ARG, "null handle");
+    if (layer >= h->p.n_layers) return fail(h, KVATTN_E_RANGE, "layer %u out of range (n_layers %u)", layer, h->p.n_layers);
+    PlanCheck chk;
+    uint32_t n_pages = 0;
+    int rc = validate_table(h, h->p, page_table, n_tokens, h_history != nullptr, &chk, &n_pages);
+    if (rc) return rc;
+    // the ring is either caller-placed or scheduler-owned on one handle
+    bool other_ring = false, other_stream = false;
+    for (uint32_t l = 0; l < h->p.n_layers; l++) {
+        if (l == layer || !h->layers[l].set) continue;
+        other_ring |= h->layers[l].uses_ring_slots;
+        other_stream |= h->layers[l].n_streamed > 0;
+    }
+    if ((chk.n_ring && (chk.n_host || other_stream)) || (chk.n_host && other_ring))
+        return fail(h, KVATTN_E_PLAN, "caller-placed ring slots and streamed pages cannot share the ring");
+
+    // drain: copies in flight may read the old history or table
+    HIP_TRY(h, hipStreamSynchronize(h->copy));
+    HIP_TRY(h, hipStreamSynchronize(h->compute));
+
+    LayerState &L = h->layers[layer];
+    L = LayerState();
+    L.n_tokens = n_tokens;
+    L.n_pages = n_pages;
+    L.history = static_cast<const uint8_t *>(h_history);
+    L.uses_ring_slots = chk.n_ring > 0;
+    std::vector<uint32_t> dev(n_pages);
+    for (uint32_t P = 0; P < n_pages; P++) {
+        if (page_table[P] == KVATTN_PT_HOST) {
+            dev[P] = kEntryStream | (uint32_t)L.streamed.size();
+            L.streamed.push_back(P);
+        } else {
+            dev[P] = page_table[P];
+            L.resident.push_back(P);
+        }
+    }
+    L.n_resident = (uint32_t)L.resident.size();
+    L.n_streamed = (uint32_t)L.streamed.size();
+    std::vector<uint32_t> list(L.resident);
+    list.insert(list.end(), L.streamed.begin(), L.streamed.end());
+    HIP_TRY(h, hipMemcpy(h->d_table(layer), dev.data(), n_pages * sizeof(uint32_t), hipMemcpyHostToDevice));
+    HIP_TRY(h, hipMemcpy(h->d_list(layer), list.data(), n_pages * sizeof(uint32_t), hipMemcpyHostToDevice));
+    L.set = true;
+    h->any_streamed = false;
+    h->any_ring_slots = false;
+    std::vector<uint32_t> counts(h->p.n_layers, 0);
+    for (uint32_t l = 0; l < h->p.n_layers; l++) {
+        h->any_streamed |= h->layers[l].set && h->layers[l].n_streamed > 0;
+        h->any_ring_slots |= h->layers[l].set && h->layers[l].uses_ring_slots;
+        counts[l] = h->layers[l].set ? h->layers[l].n_streamed : 0;
+    }
+    if (h->p.n_ring_slots) h->sched.set_layer_counts(counts);
+    return KVATTN_OK;
+}
+
+int kvattn_decode(kvattn_t h, uint32_t layer, const float *d_q, float *d_out) { return attend(h, layer, d_q, 1, d_out, false); }
+
+int kvattn_verify(kvattn_t h, uint32_t layer, const float *d_q, uint32_t W, float *d_out) {
+    return attend(h, layer, d_q, W, d_out, false);
+}
+
+int kvattn_prefill_chunk(kvattn_t h, uint32_t layer, const float *d_q, uint32_t R, float *d_out) {
+    return attend(h, layer, d_q, R, d_out, true);
+}
+
+int kvattn_synchronize(kvattn_t h) {
+    if (!h) return fail(nullptr, KVATTN_E_ARG, "null handle");
+    HIP_TRY(h, hipStreamSynchronize(h->copy));
+    HIP_TRY(h, hipStreamSynchronize(h->compute));
+    return KVATTN_OK;
+}
+
+int kvattn_debug_read_page(kvattn_t h, uint32_t layer, uint32_t logical_page, void *h_out) {
+    if (!h) return fail(nullptr, KVATTN_E_ARG, "null handle");
+    if (layer >= h->p.n_layers) return fail(h, KVATTN_E_RANGE, "layer %u out of range", layer);
+    if (!h->layers[layer].set) return fail(h, KVATTN_E_STATE, "layer %u has no history", layer);
+    if (logical_page >= h->layers[layer].n_pages) return fail(h, KVATTN_E_RANGE, "logical page %u out of range", logical_page);
+    if (!h_out) return fail(h, KVATTN_E_ARG, "null output");
+    SplitArgs a = base_args(h, layer, 1, nullptr);
+    a.ring_base = (uint32_t)(h->sched.last_ordinal_base(layer) % std::max<uint32_t>(1, h->p.n_ring_slots));
+    uint8_t *staging = h->wsp + h->ws.staging;
+    HIP_TRY(h, kvattn_launch_read_page(a, logical_page, staging, h->compute));
+    HIP_TRY(h, hipMemcpyAsync(h_out, staging, h->lay.page_bytes, hipMemcpyDeviceToHost, h->compute));
+    HIP_TRY(h, hipStreamSynchronize(h->compute));
+    return KVATTN_OK;
+}
+
+int kvattn_destroy(kvattn_t h) {
+    if (!h) return KVATTN_OK;
+    int rc = KVATTN_OK;
+    if (hipStreamSynchronize(h->copy) != hipSuccess) rc = KVATTN_E_HIP;
+    if (hipStreamSynchronize(h->compute) != hipSuccess) rc = KVATTN_E_HIP;
+    h->sched.destroy();
+    if (h->upload_done) (void)hipEventDestroy(h->upload_done);
+    delete h;
+    return rc;
+}
+
+const char *kvattn_last_error(kvattn_t h) { return h ? h->err.c_str() : "null handle"; }
+
+const char *kvattn_global_error(void) { return g_error.c_str(); }
+
+/* Host only: the checks kvattn_set_layer applies to a page table that need
+ * no handle state (see the header). */
+int kvattn_validate_page_table(const kvattn_params *params, const uint32_t *page_table, uint32_t n_tokens, int has_history) {
+    kvattn_params p;
+    if (!read_params(params, &p)) return fail(nullptr, KVATTN_E_ARG, "null params or struct_size too small");
+    std::string why;
+    int rc = check_params(p, why);
+    if (rc) return fail(nullptr, rc, "%s", why.c_str());
+    PlanCheck chk;
+    uint32_t n_pages = 0;
+    return validate_table(nullptr, p, page_table, n_tokens, has_history != 0, &chk, &n_pages);
+}
+
+/* Test aid (host only, no GPU): run the streaming planner over a sequence of
+ * layer calls and log the enqueue sequence the HIP path would issue.  Each op
+ * is 7 int64: kind (1 copy, 2 compute, 3 drain, 4 merge, 5 resident pages,
+ * 6 layer begun),
+ * layer, first, count, ordinal base, event, wait event. */
+int kvattn_sched_simulate(uint32_t n_layers, uint32_t n_slots, uint32_t chunk_slots, const uint32_t *streamed_counts,
+                          const uint32_t *call_layers, uint32_t n_calls, int64_t *ops, uint32_t max_ops, uint32_t *n_ops) {
+    if (!streamed_counts || !call_layers || !ops || !n_ops || n_layers == 0 || n_slots == 0) return KVATTN_E_ARG;
+    StreamPlanner pl;
+    pl.init(n_layers, n_slots, chunk_slots ? chunk_slots : 16);
+    pl.set_layer_counts(std::vector<uint32_t>(streamed_counts, streamed_counts + n_layers));
+    SimExec x{ops, max_ops};
+    for (uint32_t i = 0; i < n_calls; i++) {
+        if (call_layers[i] >= n_layers) return KVATTN_E_RANGE;
+        if (streamed_counts[call_layers[i]] == 0) continue;
+        int rc = drive_streamed_layer(pl, call_layers[i], x);
+        if (rc) return rc;
+    }
+    *n_ops = x.n;
+    return x.overflow ? KVATTN_E_NOSPACE : KVATTN_OK;
+}
+
+}  // extern "C"

@@ -82,7 +82,7 @@ def _ptr(a):
 
 
 def _threads(n):
-    return n if n else (os.cpu_count() or 1)
+    return n if n else max(1, min(16, os.cpu_count() or 1))
 
 
 def f16_to_f64(bits: int) -> float:
