@@ -1,0 +1,280 @@
+#!/usr/bin/env python3
+"""Benchmark of paged Q8_0-K / Q4_0-V attention on one MI355X.
+
+A step is one pass of the hot path over one batch: every layer of the
+workload attends once (64 layers).  Default workload: all-resident TG1 decode,
+40,960-token history (160 pages of 256 tokens) per layer, 40 query heads over
+8 KV heads, head_dim 128, 64 layers with their own seeded N(0,1) data, pages
+scattered over the pool by a seeded permutation.  Inputs are resident in HBM
+before timing starts.
+
+Prints one JSON line: throughput (tokens/s = query rows per pass x passes/s),
+the roofline of the dominant kernel (the split-KV attention kernel: quantised
+K+V bytes it must read per launch / its mean device time, from HIP events
+recorded around each launch on the compute stream during the timed region),
+and the fp64 CPU oracle timed on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+                       [--workload decode-40k|verify-160k|stream-256k|prefill-120k]
+                       [--width W] [--mode graph|eager] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attn tokens/s and quantized-KV GB/s (% of HBM peak) at 40k-256k ctx, 1 GPU"
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, vendor figure
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix, vendor figure
+BYTES_PER_TOKEN_HEAD = 208    # Q8_0 K (4 x 34 B) + Q4_0 V (4 x 18 B) per token per KV head
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="decode-40k")
+    ap.add_argument("--width", type=int, default=0, help="query rows for verify / streamed workloads")
+    ap.add_argument("--mode", choices=["graph", "eager"], default=None,
+                    help="graph: replay a captured HIP graph of the 64-layer pass (resident workloads); "
+                         "eager: one C-ABI call per layer")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layers", type=int, default=0, help="override the layer count (testing only)")
+    return ap.parse_args()
+
+
+# --------------------------------------------------------------------------- setup
+def build(w, width, n_layers, torch, kv, inputs):
+    """Create the handle and place every layer's pages.  Returns (handle,
+    queries, outputs, call kind, rows, host histories)."""
+    dev = "cuda"
+    n = w.n_pages
+    streamed = w.resident_fraction < 1.0
+    rows = width if width else w.widths[-1] if w.prefill_rows else (w.widths[0] if not streamed else 1)
+    n_res = w.n_resident if streamed else n
+    n_pool = n_layers * n_res
+    compute = torch.cuda.Stream()
+    copy = torch.cuda.Stream()
+    params = kv.make_params(n_layers, w.n_q_heads, w.n_kv_heads, n_pool, n, max(rows, 1),
+                            n_ring_slots=w.ring_slots)
+    h = kv.allocate(params, compute_stream=compute, copy_stream=copy)
+    pb = kv.page_bytes(params)
+    pool = h.pool.view(n_pool, pb)
+    perm = np.random.default_rng(inputs.derive_seed(inputs.BASE_SEED, w.wid, 0, inputs.T_PERM)).permutation(n_pool)
+    hist = []
+    for l in range(n_layers):
+        kvl = inputs.draw_layer(w.n_tokens, w.n_kv_heads, l, w.wid, device=dev)
+        table = np.empty(n, dtype=np.uint32)
+        if streamed:
+            res = inputs.resident_subset(n, n_res, l, w.wid)
+            ids = perm[l * n_res:(l + 1) * n_res]
+            table[:] = kv.PT_HOST
+            table[res] = ids
+            pool[torch.from_numpy(ids).to(dev)] = kvl.pages[torch.from_numpy(res).to(dev)]
+            host = torch.empty((n, pb), dtype=torch.uint8, pin_memory=True)
+            host.copy_(kvl.pages)
+            hist.append(host)
+            torch.cuda.synchronize()
+            h.set_layer(l, table, w.n_tokens, host)
+        else:
+            ids = perm[l * n:(l + 1) * n]
+            table[:] = ids
+            pool[torch.from_numpy(ids.astype(np.int64)).to(dev)] = kvl.pages
+            torch.cuda.synchronize()
+            h.set_layer(l, table, w.n_tokens)
+        del kvl
+    qs = [inputs.draw_queries(rows, w.n_q_heads, l, w.wid, device=dev) for l in range(n_layers)]
+    outs = [torch.empty_like(q) for q in qs]
+    kind = "prefill" if w.prefill_rows else ("decode" if rows == 1 else "verify")
+    torch.cuda.synchronize()
+    return h, qs, outs, kind, rows, hist
+
+
+def one_pass(h, qs, outs, kind, rows):
+    for l in range(len(qs)):
+        if kind == "decode":
+            h.decode(l, qs[l], outs[l])
+        elif kind == "verify":
+            h.verify(l, qs[l], rows, outs[l])
+        else:
+            h.prefill_chunk(l, qs[l], rows, outs[l])
+
+
+# --------------------------------------------------------------------------- cpu baseline
+def cpu_baseline(w, rows, kind, inputs):
+    """The oracle (fp64 C, OpenMP over (row, head)) on a bounded sample of the
+    same workload, scaled to tokens/s of the full 64-layer pass."""
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    layer = 0
+    kvl = inputs.draw_layer(w.n_tokens, w.n_kv_heads, layer, w.wid, device="cuda")
+    pages = kvl.pages.cpu().numpy()
+    q = inputs.draw_queries(rows, w.n_q_heads, layer, w.wid, device="cuda").cpu().numpy()
+    if kind == "prefill":
+        # a sample of rows: first, last and 6 seeded others
+        rng = np.random.default_rng(7)
+        sample_rows = sorted({0, rows - 1, *rng.choice(rows, 6, replace=False).tolist()})
+    else:
+        sample_rows = list(range(rows))
+    t0 = time.perf_counter()
+    oracle.attend_paged(np.arange(pages.shape[0], dtype=np.uint32), w.n_tokens, 256, w.n_q_heads, w.n_kv_heads, q,
+                        inputs.scale_for(), pool=pages, rows=sample_rows, n_threads=threads)
+    dt = time.perf_counter() - t0
+    # full pass = n_layers layers x rows rows; sample = 1 layer x len(sample_rows) rows
+    pass_s = dt * w.n_layers * rows / len(sample_rows)
+    return {"value": rows / pass_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"1 layer of {w.name} ({w.n_tokens} keys, {w.n_q_heads} query heads, "
+                      f"{len(sample_rows)} of {rows} rows), {dt:.2f} s measured, scaled x{w.n_layers} layers"
+                      + ("" if len(sample_rows) == rows else f" x{rows / len(sample_rows):.0f} rows")}
+
+
+# --------------------------------------------------------------------------- main
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this path has no multi-GPU mode (asked for --gpus {args.gpus}). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import inputs
+    import long_context_attention_amd as kv
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = inputs.WORKLOADS[args.workload]
+    n_layers = args.layers or w.n_layers
+    streamed = w.resident_fraction < 1.0
+    mode = args.mode or ("eager" if streamed else "graph")
+    if streamed and mode == "graph":
+        print("streamed workloads run eagerly (the copy stream is driven by the host)", file=sys.stderr)
+        sys.exit(2)
+    log(f"bench: workload {w.name}, {n_layers} layers, mode {mode}: building inputs")
+    t0 = time.perf_counter()
+    h, qs, outs, kind, rows, hist = build(w, args.width, n_layers, torch, kv, inputs)
+    log(f"bench: inputs ready in {time.perf_counter() - t0:.1f} s; {kind} rows={rows}")
+    stream = h.compute_stream
+
+    graph = None
+    if mode == "graph":
+        with torch.cuda.stream(stream):
+            one_pass(h, qs, outs, kind, rows)  # warm the code paths before capture
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            one_pass(h, qs, outs, kind, rows)
+        torch.cuda.synchronize()
+
+    def step():
+        if graph is not None:
+            graph.replay()
+        else:
+            one_pass(h, qs, outs, kind, rows)
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+    torch.cuda.synchronize()
+    log(f"bench: warmup {args.warmup} done; timing {args.steps} steps")
+
+    chunks = -(-(w.n_pages - w.n_resident) // 16) if streamed else 0
+    launches_per_pass = n_layers * (chunks + 3)
+    if graph is None:
+        h.profile(max(1, args.steps) * launches_per_pass)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        t_start = time.perf_counter()
+        for i in range(args.steps):
+            step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    elapsed_ms = e0.elapsed_time(e1)
+    ms_per_step = elapsed_ms / args.steps
+    kernel_timing = "per-launch HIP events on the compute stream during the timed steps"
+    passes_profiled = args.steps
+    if graph is not None:
+        # HIP cannot time events recorded inside a captured graph: time the
+        # same kernels launched eagerly, with per-launch events, over the same
+        # number of passes
+        kernel_timing = "per-launch HIP events on the compute stream, eager passes after the graph-timed steps"
+        h.profile(max(1, args.steps) * launches_per_pass)
+        with torch.cuda.stream(stream):
+            for i in range(args.steps):
+                one_pass(h, qs, outs, kind, rows)
+    split_ms, n_split, merge_ms, n_merge = h.profile_read(reset=True)
+    h.profile(0)
+
+    # ---- figures
+    tokens_per_step = rows
+    value = tokens_per_step / (ms_per_step / 1e3)
+    keys_per_layer = w.n_tokens  # every key of the history is read once per layer (all rows share it)
+    kv_bytes_layer = keys_per_layer * w.n_kv_heads * BYTES_PER_TOKEN_HEAD
+    kv_gbps = kv_bytes_layer * n_layers / (ms_per_step / 1e3) / 1e9
+    flops_layer = 4.0 * w.n_q_heads * 128 * sum(w.n_tokens - rows + r + 1 for r in range(rows))
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": n_layers, "context": w.n_tokens, "page_tokens": 256,
+                   "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": 128, "rows": rows,
+                   "kv_types": "Q8_0 K / Q4_0 V", "mode": mode,
+                   "resident_fraction": w.resident_fraction, "ring_slots": w.ring_slots},
+        "layers_per_s": round(n_layers / (ms_per_step / 1e3), 1),
+        "kv_gbps": round(kv_gbps, 1),
+        "kv_frac_hbm_peak": round(kv_gbps / HBM_PEAK_GBPS, 4),
+        "wall_s": round(wall, 3),
+    }
+    if streamed:
+        n_str = w.n_pages - w.n_resident
+        h2d = n_str * w.page_bytes * n_layers / (ms_per_step / 1e3) / 1e9
+        result["h2d_gbps"] = round(h2d, 2)
+    if n_split:
+        split_mean_ms = split_ms / n_split
+        achieved = kv_bytes_layer * n_layers * passes_profiled / (split_ms / 1e3) / 1e9
+        if kind == "prefill":
+            tflops = flops_layer * n_layers * passes_profiled / (split_ms / 1e3) / 1e12
+            result["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                                  "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                                  "traffic": None}
+            result["split_kv_gbps"] = round(achieved, 1)
+        else:
+            result["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                                  "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None}
+        result["kernel_ms"] = {"split_mean": round(split_mean_ms, 5), "split_launches": n_split,
+                               "merge_mean": round(merge_ms / max(n_merge, 1), 5), "merge_launches": n_merge,
+                               "passes_profiled": passes_profiled, "timing": kernel_timing}
+    if not args.no_cpu_baseline:
+        log("bench: timing the oracle on a CPU sample")
+        result["cpu_baseline"] = cpu_baseline(w, rows, kind, inputs)
+    h.destroy()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

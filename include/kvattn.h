@@ -81,7 +81,9 @@ enum { KVATTN_TYPE_Q4_0 = 2, KVATTN_TYPE_Q8_0 = 8 };
  *      tiles of 2048 bytes.  In a tile, token j (0..31) and dim t have byte
  *         (t/64)*1024 + (((j%16)/4)*16 + t%16)*16 + ((t/16)%4)*4 + j%4,
  *      low nibble for j < 16, high nibble for j >= 16.
- *   4. V scales, binary16 [H][T][4].
+ *   4. V scales, binary16, H*T*8 bytes.  Head h starts at h*T*8; 32-token
+ *      tiles of 256 bytes.  In a tile, token j (0..31) and block b have byte
+ *         (b*4 + (j%16)/4)*16 + ((j/16)*4 + j%4)*2.
  * Page size = H*T*208 bytes (425,984 at H = 8, T = 256).  Pool pages, ring
  * slots and host-history pages all use this layout, so a host-to-device copy
  * of a page is a plain memcpy.
@@ -214,6 +216,19 @@ int kvattn_validate_page_table(const kvattn_params *params, const uint32_t *page
 int kvattn_sched_simulate(uint32_t n_layers, uint32_t n_slots, uint32_t chunk_slots, const uint32_t *streamed_counts,
                           const uint32_t *call_layers, uint32_t n_calls, int64_t *ops, uint32_t max_ops,
                           uint32_t *n_ops);
+
+/*
+ * Profiling aid.  kvattn_profile(h, n) with n > 0 brackets each of the next
+ * n kernel launches (split or merge) with timing events on the compute
+ * stream; n = 0 stops.  kvattn_profile_read waits for the compute stream and
+ * returns the summed device time (ms) and launch counts of the split and the
+ * merge kernels recorded since kvattn_profile; reset != 0 starts a new count
+ * (reset = 0 re-reads the same events, e.g. after each replay of a captured
+ * graph that contains them).
+ */
+int kvattn_profile(kvattn_t h, uint32_t max_launches);
+int kvattn_profile_read(kvattn_t h, int reset, double *split_ms, uint32_t *n_split, double *merge_ms,
+                        uint32_t *n_merge);
 
 /* Drain both streams, release events, free the handle (NULL is a no-op). */
 int kvattn_destroy(kvattn_t h);

@@ -25,7 +25,9 @@ bytes; binary16 little-endian), four sections in order:
      16*((off%16)//4) + (off%1024//16) % 16`` of two keys: key
      ``4*(off%1024//256) + off%4`` in the low nibble and that key + 16 in the
      high nibble.
-  4. V scales, binary16 [H][T][4].
+  4. V scales, binary16: head h at h*T*8, then 32-token tiles of 256 bytes;
+     inside a tile, the 2-byte scale at ``off`` is block ``off//64`` of key
+     ``16*(off%16//8) + 4*(off%64//16) + (off%8)//2``.
 """
 from __future__ import annotations
 
@@ -185,6 +187,19 @@ def _gather_maps(page_tokens: int, device):
     return maps
 
 
+def _vscale_map(page_tokens: int, device):
+    """For each 2-byte V-scale slot of one head's section, the flat index
+    (token * 4 + block) of the scale stored there."""
+    key = ("vd", page_tokens, str(device))
+    if key not in _gather_cache:
+        slot = np.arange(page_tokens * 4, dtype=np.int64)
+        tile, o = slot // 128, (slot % 128) * 2      # o: byte offset inside the 256-byte tile
+        block = o // 64
+        tok = 32 * tile + 16 * ((o % 16) // 8) + 4 * ((o % 64) // 16) + (o % 8) // 2
+        _gather_cache[key] = torch.from_numpy(tok * 4 + block).to(device)
+    return _gather_cache[key]
+
+
 def pack_pages(kc, kd, vc, vd, page_tokens: int = PAGE_TOKENS, pad: str = "zero", pad_seed: int = 0):
     """Pack logical arrays into pages.
 
@@ -229,7 +244,9 @@ def pack_pages(kc, kd, vc, vd, page_tokens: int = PAGE_TOKENS, pad: str = "zero"
     k_bytes = kflat[:, :, k_src]
     v_bytes = (vflat[:, :, v_lo] & 0x0F) | ((vflat[:, :, v_hi] & 0x0F) << 4)
     kd_bytes = kd_p.contiguous().view(torch.uint8).reshape(n_pages, H * T * 8)
-    vd_bytes = vd_p.contiguous().view(torch.uint8).reshape(n_pages, H * T * 8)
+    vd_src = _vscale_map(T, dev)
+    vd_flat = vd_p.contiguous().reshape(n_pages, H, T * 4)   # (token, block) flat
+    vd_bytes = vd_flat[:, :, vd_src].contiguous().view(torch.uint8).reshape(n_pages, H * T * 8)
     pages = torch.cat([k_bytes.reshape(n_pages, -1), kd_bytes, v_bytes.reshape(n_pages, -1), vd_bytes], 1)
     assert pages.shape[1] == page_bytes(H, T)
     return pages.contiguous()

@@ -15,7 +15,7 @@ struct SplitArgs {
     uint32_t T;                   // tokens per page
     uint32_t W;                   // query rows (positions)
     uint32_t Hq, Hkv, G;          // query heads, KV heads, Hq / Hkv
-    uint32_t split_pages;         // pages per split when page_list is null
+    uint32_t split_chunks;        // 32-key chunks per split when page_list is null
     uint32_t ring_base;           // ring slot of streamed ordinal 0 (mod n_ring_slots)
     uint32_t n_ring_slots;
     size_t page_bytes;
@@ -34,7 +34,10 @@ struct MergeArgs {
     float *out;                   // [W][Hq][128]
 };
 
-size_t kvattn_split_smem_bytes(int nrt);
-hipError_t kvattn_launch_split(const SplitArgs &a, uint32_t n_items, uint32_t n_row_blocks, int nrt, hipStream_t s);
+size_t kvattn_split_smem_bytes(int rt);
+hipError_t kvattn_split_setup();
+uint32_t kvattn_merge_max_splits();
+// rt: row tiles of 16 rows per workgroup (1 or 2); n_row_blocks blocks of 16 * rt rows
+hipError_t kvattn_launch_split(const SplitArgs &a, uint32_t n_items, uint32_t n_row_blocks, int rt, hipStream_t s);
 hipError_t kvattn_launch_merge(const MergeArgs &a, hipStream_t s);
 hipError_t kvattn_launch_read_page(const SplitArgs &a, uint32_t logical_page, uint8_t *dst, hipStream_t s);

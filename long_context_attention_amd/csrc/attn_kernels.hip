@@ -38,7 +38,6 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 namespace kvattn_dev {
 
-constexpr int kWaves = 4;
 constexpr float kNegInf = -__builtin_inff();
 
 // ---------------------------------------------------------------------------
@@ -89,238 +88,347 @@ __device__ __forceinline__ const uint8_t *resolve_page(const SplitArgs &a, uint3
     uint32_t e = a.page_table[logical_page];
     if (e < 0x80000000u) return a.pool + (size_t)e * a.page_bytes;
     uint32_t v = e & 0x3FFFFFFFu;
-    if (e & 0x40000000u) v = (uint32_t)(((uint64_t)a.ring_base + v) % a.n_ring_slots);
+    if (e & 0x40000000u) v = (a.ring_base + v) % a.n_ring_slots;  // both < 2^30: no overflow
     return a.ring + (size_t)v * a.page_bytes;
 }
 
 // ---------------------------------------------------------------------------
-// Split kernel.  NRT = row tiles of 16 query rows per wave (1 or 2).
-// Rows of a KV head are ordered (w, hh): r = w * G + hh, hh < G.
+// One 32-key chunk of one KV head.
+// In flight (registers): the lane's code bytes and 8 bytes of scales.
+//   kq[16]  K codes of 16-key tile tt (dwords 8tt .. 8tt+7): blocks 2k, 2k+1
+//           of load k, 8 codes each
+//   vq[8]   V codes, one dword per 16-dim tile
+//   sc      lanes 0-31: K scales of the chunk's 32 keys ([key][block], 256
+//           bytes); lanes 32-63: the chunk's V-scale tile (256 bytes)
+// The scales are shared by the 16 lanes of a group, so they go through a
+// 512-byte LDS slot per wave instead of being loaded 16 times.
 // ---------------------------------------------------------------------------
-template <int NRT>
-__global__ __launch_bounds__(256) void split_kernel(const SplitArgs a) {
-    constexpr int ROWS = NRT * 16;
-    extern __shared__ float smem[];  // [waves][ROWS] m, [waves][ROWS] l, [waves][ROWS][132] acc
+struct ChunkG {
+    uint32_t kq[16];
+    uint32_t vq[8];
+    uint2 sc;
+};
+
+// Scales of one chunk as the lane uses them.
+//   kd[16]  [tt][8]: binary16 pairs, key 4g + v of tile tt, block b at half 4v + b
+//   vd[16]  [b][4]: binary16 pairs of block b, operand slots 2i, 2i + 1
+struct ChunkS {
+    uint32_t kd[16];
+    uint32_t vd[16];
+};
+
+__device__ __forceinline__ void put4(uint32_t *d, const uint4 &x) {
+    d[0] = x.x;
+    d[1] = x.y;
+    d[2] = x.z;
+    d[3] = x.w;
+}
+
+__device__ __forceinline__ void load_chunk(const SplitArgs &a, uint32_t kvh, uint32_t chunk, int lane, ChunkG &r) {
+    const uint32_t cpp = a.T >> 5;  // chunks per page
+    const uint32_t page = chunk / cpp;
+    const uint32_t jj0 = (chunk - page * cpp) << 5;
+    const uint8_t *base = resolve_page(a, page);
+    const size_t T = a.T;
+    const uint4 *kcp = reinterpret_cast<const uint4 *>(base + (size_t)kvh * T * 128 + (size_t)(jj0 >> 4) * 2048) + lane;
+    const uint4 *vcp = reinterpret_cast<const uint4 *>(base + a.sec_vc + (size_t)kvh * T * 64 + (size_t)(jj0 >> 5) * 2048) + lane;
+    const uint8_t *scp = lane < 32 ? base + a.sec_kd + ((size_t)kvh * T + jj0) * 8 + lane * 8
+                                   : base + a.sec_vd + (size_t)kvh * T * 8 + (size_t)(jj0 >> 5) * 256 + (lane - 32) * 8;
+    put4(r.kq + 0, kcp[0]);
+    put4(r.kq + 4, kcp[64]);
+    put4(r.kq + 8, kcp[128]);
+    put4(r.kq + 12, kcp[192]);
+    put4(r.vq + 0, vcp[0]);
+    put4(r.vq + 4, vcp[64]);
+    r.sc = *reinterpret_cast<const uint2 *>(scp);
+}
+
+// Stage the chunk's scales through the wave's LDS slot (64 x uint2) and read
+// back the lane's K scales; the V scales are read when the P' operands are
+// formed (read_vscales), so they do not occupy registers during Q.K^T.
+__device__ __forceinline__ void stage_scales(uint2 *slot, const ChunkG &g, int lane, int grp, ChunkS &s) {
+    slot[lane] = g.sc;
+    const uint4 *k4 = reinterpret_cast<const uint4 *>(slot);  // K scales: key j at bytes 8j
+    put4(s.kd + 0, k4[2 * grp]);                              // keys 4g .. 4g+3
+    put4(s.kd + 4, k4[2 * grp + 1]);
+    put4(s.kd + 8, k4[8 + 2 * grp]);                          // keys 16 + 4g ..
+    put4(s.kd + 12, k4[8 + 2 * grp + 1]);
+}
+
+__device__ __forceinline__ void read_vscales(const uint2 *slot, int grp, ChunkS &s) {
+    const uint4 *v4 = reinterpret_cast<const uint4 *>(slot + 32);  // V tile
+#pragma unroll
+    for (int b = 0; b < 4; b++) put4(s.vd + 4 * b, v4[b * 4 + grp]);
+}
+
+// binary16 half `i` of a packed array (lo half = even index)
+__device__ __forceinline__ float half_of(const uint32_t *w, int i) { return (i & 1) ? h2f_hi(w[i >> 1]) : h2f_lo(w[i >> 1]); }
+
+// Softmax reference of a row moves only when a score exceeds it by more than
+// kRescale (log2 units), so P = exp2(s - ref) <= 2^kRescale stays exact
+// enough in binary16 and the accumulators are rarely rescaled.  Any
+// reference gives the same result in exact arithmetic; the partial carries
+// the reference it used.
+constexpr float kRescale = 8.0f;
+
+// Per-wave state: one tile of 16 query rows (the lane's row is c16).
+struct RowState {
+    half8 qf[4];     // B operand of S^T = K Q^T, block b
+    int row_pos;     // position of the lane's row; -1 = padding row
+    float m_ref;     // softmax reference (log2 units), uniform per row
+    float l_run;     // lane's share of the softmax denominator
+    floatx4 acc[8];  // O^T tile n: dims 16n + 4g + v of the lane's row
+};
+
+// Scores of one chunk: s[4tt + v] is key 16tt + 4g + v of the chunk,
+// log2-scaled.  One MFMA per 32-dim block, scaled by that block's d_K.
+template <bool MASK>
+__device__ __forceinline__ void chunk_scores(const RowState &st, const ChunkG &r, const ChunkS &sc, uint32_t kpos0,
+                                             int grp, float s[8]) {
+#pragma unroll
+    for (int tt = 0; tt < 2; tt++) {
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+            const uint32_t *w = r.kq + 8 * tt + 4 * (b >> 1) + 2 * (b & 1);
+            const half8 kf = q8_to_half8(w[0], w[1]);
+            const floatx4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, st.qf[b], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+            for (int v = 0; v < 4; v++) {
+                // fma with the binary16 operand read in place (v_fma_mix_f32)
+                const float dk = half_of(sc.kd + 8 * tt, 4 * v + b);
+                s[4 * tt + v] = __builtin_fmaf(dk, d[v], b == 0 ? 0.0f : s[4 * tt + v]);
+            }
+        }
+    }
+    if (MASK) {
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const int key = (int)(kpos0 + 16 * (i >> 2) + 4 * grp + (i & 3));
+            if (key > st.row_pos) s[i] = kNegInf;
+        }
+    }
+}
+
+// Softmax step of one chunk: lazy reference update (rescaling the
+// accumulators, which already hold every earlier chunk), probabilities, the
+// denominator, and the P' operands P * d_V of the four value blocks.
+template <bool MASK>
+__device__ __forceinline__ void chunk_probs(RowState &st, const float s[8], const uint2 *slot, int grp, half8 pf[4]) {
+    float m = s[0];
+#pragma unroll
+    for (int i = 1; i < 8; i++) m = fmaxf(m, s[i]);
+    if (__any(m > st.m_ref + kRescale)) {
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        const float m_new = fmaxf(st.m_ref, m);
+        const float alpha = (st.m_ref == kNegInf) ? 0.f : fast_exp2(st.m_ref - m_new);
+        st.l_run *= alpha;
+#pragma unroll
+        for (int n = 0; n < 8; n++) st.acc[n] *= alpha;
+        st.m_ref = m_new;
+    }
+    const float mu = (st.m_ref == kNegInf) ? 0.f : st.m_ref;
+    float p[8];
+    float lsum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        p[i] = fast_exp2(s[i] - mu);
+        lsum += p[i];
+    }
+    st.l_run += lsum;
+    ChunkS sc;
+    read_vscales(slot, grp, sc);
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+        float e[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const float pd = __builtin_fmaf(p[i], half_of(sc.vd + 4 * b, i), 0.0f);
+            // masked keys have p = 0 but may sit on garbage (NaN) scales
+            e[i] = MASK ? ((p[i] == 0.f) ? 0.f : pd) : pd;
+        }
+        pf[b] = half8{(_Float16)e[0], (_Float16)e[1], (_Float16)e[2], (_Float16)e[3],
+                      (_Float16)e[4], (_Float16)e[5], (_Float16)e[6], (_Float16)e[7]};
+    }
+}
+
+// O^T += V^T P'^T for one chunk: dim tile n = 2b + nn of value block b.
+__device__ __forceinline__ void chunk_pv(RowState &st, const uint32_t vq[8], const half8 pf[4]) {
+#pragma unroll
+    for (int n = 0; n < 8; n++) {
+        const half8 vf = q4_to_half8(vq[n]);
+        st.acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[n >> 1], st.acc[n], 0, 0, 0);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Split kernel.  A workgroup of 8 waves handles one split (a range of 32-key
+// chunks) of one KV head for RT tiles of 16 query rows; 8 / RT waves share a
+// row tile and take its chunks round robin.  Rows of a KV head are ordered
+// (w, hh): r = w * G + hh, hh < G.
+// Each wave keeps the next chunk's loads in flight and overlaps chunk i's
+// Q.K^T with chunk i-1's P.V, whose operands it carries over.
+// ---------------------------------------------------------------------------
+constexpr int kSplitWaves = 8;
+
+template <int RT>
+__global__ __launch_bounds__(64 * kSplitWaves, 1) void split_kernel(const SplitArgs a) {
+    constexpr int RTW = kSplitWaves / RT;  // waves per row tile
+    extern __shared__ float smem[];        // [waves][16] m, [waves][16] l, [waves][16][132] acc
+    __shared__ uint2 sc_slot[kSplitWaves][64];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // wave index, made visibly uniform so chunk bookkeeping stays scalar
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int rt = wave / RTW, cw = wave - rt * RTW;
     const int grp = lane >> 4;  // 16-lane group
     const int c16 = lane & 15;
     const uint32_t kvh = blockIdx.y;
-    const uint32_t row0 = blockIdx.z * ROWS;  // first row of this block within the KV head
+    const uint32_t row0 = blockIdx.z * (16 * RT) + 16 * rt;  // first row of this wave's tile
     const uint32_t rows_kv = a.W * a.G;
+    const uint32_t n_chunks_all = (a.n_tokens + 31) >> 5;
 
-    // ---- split -> logical page range
-    uint32_t split, first_page, n_pg;
+    // ---- split -> chunk range
+    uint32_t split, c_begin, c_end;
     if (a.page_list) {
         split = a.page_list[a.list_offset + blockIdx.x];
-        first_page = split;
-        n_pg = 1;
+        c_begin = split * (a.T >> 5);
+        c_end = min(c_begin + (a.T >> 5), n_chunks_all);
     } else {
         split = blockIdx.x;
-        first_page = blockIdx.x * a.split_pages;
-        n_pg = min(a.split_pages, a.n_pages - first_page);
+        c_begin = blockIdx.x * a.split_chunks;
+        c_end = min(c_begin + a.split_chunks, n_chunks_all);
     }
-    const uint32_t k_begin = first_page * a.T;
-    const uint32_t k_end = min(k_begin + n_pg * a.T, a.n_tokens);
-    const uint32_t n_chunks = (k_end - k_begin + 31) >> 5;
+    // chunks whose keys every row sees (keys <= n_tokens - W) need no mask
+    const uint32_t clean_end = (a.n_tokens - a.W + 1) >> 5;
 
-    // ---- query fragments (B operand of S^T = K Q^T): lane (row c16, group g)
-    // holds dims 32b + 8g .. +8 of block b, pre-scaled by softmax_scale*log2(e).
-    half8 qf[NRT][4];
-    int row_pos[NRT];  // position of the lane's row (as a column of S^T); -1 = padding
+    // ---- row state and raw query loads (issued first: their latency then
+    // overlaps the chunk loads issued next)
+    RowState st;
+    float4 qraw[8];
+    st.row_pos = -1;
+    st.m_ref = kNegInf;
+    st.l_run = 0.f;
 #pragma unroll
-    for (int rt = 0; rt < NRT; rt++) {
-        uint32_t r = row0 + rt * 16 + c16;
-        row_pos[rt] = -1;
+    for (int n = 0; n < 8; n++) st.acc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 8; i++) qraw[i] = float4{0.f, 0.f, 0.f, 0.f};
+    {
+        const uint32_t r = row0 + c16;
         if (r < rows_kv) {
-            uint32_t w = r / a.G, hh = r - w * a.G;
-            uint32_t h = kvh * a.G + hh;
-            row_pos[rt] = (int)(a.n_tokens - a.W + w);
-            const float *qp = a.q + ((size_t)w * a.Hq + h) * 128;
+            const uint32_t w = r / a.G, hh = r - w * a.G;
+            const uint32_t h = kvh * a.G + hh;
+            st.row_pos = (int)(a.n_tokens - a.W + w);
+            const float4 *qp = reinterpret_cast<const float4 *>(a.q + ((size_t)w * a.Hq + h) * 128 + 8 * grp);
 #pragma unroll
             for (int b = 0; b < 4; b++) {
-                const float4 *p4 = reinterpret_cast<const float4 *>(qp + 32 * b + 8 * grp);
-                float4 x = p4[0], y = p4[1];
-                qf[rt][b] = half8{(_Float16)(x.x * a.qscale), (_Float16)(x.y * a.qscale),
-                                  (_Float16)(x.z * a.qscale), (_Float16)(x.w * a.qscale),
-                                  (_Float16)(y.x * a.qscale), (_Float16)(y.y * a.qscale),
-                                  (_Float16)(y.z * a.qscale), (_Float16)(y.w * a.qscale)};
+                qraw[2 * b] = qp[8 * b];
+                qraw[2 * b + 1] = qp[8 * b + 1];
             }
+        }
+    }
+
+    uint2 *slot = sc_slot[wave];
+    uint32_t c = c_begin + cw;
+    // this wave's last chunk; the prefetch past it reloads that chunk (an L2
+    // hit) so every iteration issues the same loads and the wait for the
+    // current chunk never covers the next one
+    const uint32_t c_last = c < c_end ? c + ((c_end - 1 - c) / RTW) * RTW : c;
+    ChunkG ga, gb;
+    if (c < c_end) load_chunk(a, kvh, c, lane, ga);
+
+    // ---- query fragments: lane (row c16, group g) holds dims 32b + 8g .. +8
+    // of block b, pre-scaled by softmax_scale * log2(e)
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+        const float4 x = qraw[2 * b], y = qraw[2 * b + 1];
+        st.qf[b] = half8{(_Float16)(x.x * a.qscale), (_Float16)(x.y * a.qscale), (_Float16)(x.z * a.qscale),
+                         (_Float16)(x.w * a.qscale), (_Float16)(y.x * a.qscale), (_Float16)(y.y * a.qscale),
+                         (_Float16)(y.z * a.qscale), (_Float16)(y.w * a.qscale)};
+    }
+
+    if (c < c_end) {
+        ChunkS cs;
+        float s[8];
+        uint32_t pv_vq[8];
+        half8 pv_pf[4];
+        // first chunk: scores and probabilities only
+        load_chunk(a, kvh, min(c + RTW, c_last), lane, gb);
+        stage_scales(slot, ga, lane, grp, cs);
+        if (c < clean_end) {
+            chunk_scores<false>(st, ga, cs, 32 * c, grp, s);
+            chunk_probs<false>(st, s, slot, grp, pv_pf);
         } else {
-#pragma unroll
-            for (int b = 0; b < 4; b++) qf[rt][b] = half8{0, 0, 0, 0, 0, 0, 0, 0};
+            chunk_scores<true>(st, ga, cs, 32 * c, grp, s);
+            chunk_probs<true>(st, s, slot, grp, pv_pf);
         }
+#pragma unroll
+        for (int i = 0; i < 8; i++) pv_vq[i] = ga.vq[i];
+        c += RTW;
+        // steady state: scores of chunk c, values of the chunk before it
+#define KVATTN_STEP(CUR, NXT)                                                   \
+    if (c >= c_end) break;                                                      \
+    load_chunk(a, kvh, min(c + RTW, c_last), lane, NXT);                        \
+    stage_scales(slot, CUR, lane, grp, cs);                                     \
+    if (c < clean_end) {                                                        \
+        chunk_scores<false>(st, CUR, cs, 32 * c, grp, s);                       \
+        chunk_pv(st, pv_vq, pv_pf);                                             \
+        chunk_probs<false>(st, s, slot, grp, pv_pf);                                   \
+    } else {                                                                    \
+        chunk_scores<true>(st, CUR, cs, 32 * c, grp, s);                        \
+        chunk_pv(st, pv_vq, pv_pf);                                             \
+        chunk_probs<true>(st, s, slot, grp, pv_pf);                                    \
+    }                                                                           \
+    for (int i = 0; i < 8; i++) pv_vq[i] = CUR.vq[i];                           \
+    c += RTW;
+        while (true) {
+            KVATTN_STEP(gb, ga)
+            KVATTN_STEP(ga, gb)
+        }
+#undef KVATTN_STEP
+        chunk_pv(st, pv_vq, pv_pf);
     }
 
-    float m_run[NRT], l_run[NRT];
-    floatx4 acc[NRT][8];
-#pragma unroll
-    for (int rt = 0; rt < NRT; rt++) {
-        m_run[rt] = kNegInf;
-        l_run[rt] = 0.f;
-#pragma unroll
-        for (int n = 0; n < 8; n++) acc[rt][n] = floatx4{0.f, 0.f, 0.f, 0.f};
-    }
-
-    const size_t T = a.T;
-    for (uint32_t c = wave; c < n_chunks; c += kWaves) {
-        const uint32_t kpos0 = k_begin + 32 * c;
-        const uint32_t page = kpos0 / a.T;
-        const uint32_t jj0 = kpos0 - page * a.T;
-        const uint8_t *base = resolve_page(a, page);
-
-        // ---- loads: K codes (2 tiles x 2), K scales (2 x 32 B), V codes (2), V scales (2 x 32 B)
-        const uint4 *kcp = reinterpret_cast<const uint4 *>(base + (size_t)kvh * T * 128 + (size_t)(jj0 >> 4) * 2048) + lane;
-        uint4 kq[2][2];
-        kq[0][0] = kcp[0];
-        kq[0][1] = kcp[64];
-        kq[1][0] = kcp[128];
-        kq[1][1] = kcp[192];
-        const uint4 *kdp = reinterpret_cast<const uint4 *>(base + a.sec_kd + (((size_t)kvh * T + jj0 + 4 * grp) * 4) * 2);
-        uint4 kd[2][2];
-        kd[0][0] = kdp[0];
-        kd[0][1] = kdp[1];
-        kd[1][0] = kdp[8];  // +16 keys = 128 bytes
-        kd[1][1] = kdp[9];
-        const uint4 *vcp = reinterpret_cast<const uint4 *>(base + a.sec_vc + (size_t)kvh * T * 64 + (size_t)(jj0 >> 5) * 2048) + lane;
-        uint4 vq[2];
-        vq[0] = vcp[0];
-        vq[1] = vcp[64];
-        const uint4 *vdp = reinterpret_cast<const uint4 *>(base + a.sec_vd + (((size_t)kvh * T + jj0 + 4 * grp) * 4) * 2);
-        uint4 vd[2][2];
-        vd[0][0] = vdp[0];
-        vd[0][1] = vdp[1];
-        vd[1][0] = vdp[8];
-        vd[1][1] = vdp[9];
-
-        // ---- scores S^T: lane holds keys 16tt + 4g + v (v = 0..3) of its row c16
-        float s[NRT][2][4];
-#pragma unroll
-        for (int tt = 0; tt < 2; tt++) {
-            // d_K for the lane's 4 keys: key v, block b at half (4v + b)
-            const uint32_t dk[8] = {kd[tt][0].x, kd[tt][0].y, kd[tt][0].z, kd[tt][0].w,
-                                    kd[tt][1].x, kd[tt][1].y, kd[tt][1].z, kd[tt][1].w};
-#pragma unroll
-            for (int b = 0; b < 4; b++) {
-                const uint4 &w = kq[tt][b >> 1];
-                half8 kf = (b & 1) ? q8_to_half8(w.z, w.w) : q8_to_half8(w.x, w.y);
-#pragma unroll
-                for (int rt = 0; rt < NRT; rt++) {
-                    floatx4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[rt][b], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-#pragma unroll
-                    for (int v = 0; v < 4; v++) {
-                        // half index 4v + b -> dword (4v + b) / 2, lo if even
-                        const int hi = 4 * v + b;
-                        float scale = (hi & 1) ? h2f_hi(dk[hi >> 1]) : h2f_lo(dk[hi >> 1]);
-                        s[rt][tt][v] = (b == 0) ? scale * d[v] : __builtin_fmaf(scale, d[v], s[rt][tt][v]);
-                    }
-                }
-            }
-        }
-
-        // ---- mask, online softmax
-        float p[NRT][2][4];
-#pragma unroll
-        for (int rt = 0; rt < NRT; rt++) {
-            float mloc = kNegInf;
-#pragma unroll
-            for (int tt = 0; tt < 2; tt++)
-#pragma unroll
-                for (int v = 0; v < 4; v++) {
-                    int key = (int)(kpos0 + 16 * tt + 4 * grp + v);
-                    if (key > row_pos[rt]) s[rt][tt][v] = kNegInf;
-                    mloc = fmaxf(mloc, s[rt][tt][v]);
-                }
-            mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-            mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-            const float m_new = fmaxf(m_run[rt], mloc);
-            const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-            const float alpha = fast_exp2(m_run[rt] - m_use);
-            float lsum = 0.f;
-#pragma unroll
-            for (int tt = 0; tt < 2; tt++)
-#pragma unroll
-                for (int v = 0; v < 4; v++) {
-                    p[rt][tt][v] = fast_exp2(s[rt][tt][v] - m_use);
-                    lsum += p[rt][tt][v];
-                }
-            l_run[rt] = l_run[rt] * alpha + lsum;
-            m_run[rt] = m_new;
-#pragma unroll
-            for (int n = 0; n < 8; n++) acc[rt][n] *= alpha;
-        }
-
-        // ---- O^T += V^T P'^T, one 16-dim tile n at a time; block b = n / 2
-        const uint32_t vw[8] = {vq[0].x, vq[0].y, vq[0].z, vq[0].w, vq[1].x, vq[1].y, vq[1].z, vq[1].w};
-        const uint32_t dv[2][8] = {{vd[0][0].x, vd[0][0].y, vd[0][0].z, vd[0][0].w, vd[0][1].x, vd[0][1].y, vd[0][1].z, vd[0][1].w},
-                                   {vd[1][0].x, vd[1][0].y, vd[1][0].z, vd[1][0].w, vd[1][1].x, vd[1][1].y, vd[1][1].z, vd[1][1].w}};
-#pragma unroll
-        for (int b = 0; b < 4; b++) {
-            half8 pf[NRT];
-#pragma unroll
-            for (int rt = 0; rt < NRT; rt++) {
-                float e[8];
-#pragma unroll
-                for (int tt = 0; tt < 2; tt++)
-#pragma unroll
-                    for (int v = 0; v < 4; v++) {
-                        const int hi = 4 * v + b;
-                        float scale = (hi & 1) ? h2f_hi(dv[tt][hi >> 1]) : h2f_lo(dv[tt][hi >> 1]);
-                        // masked keys have p = 0 but may sit on garbage scales
-                        e[4 * tt + v] = (p[rt][tt][v] == 0.f) ? 0.f : p[rt][tt][v] * scale;
-                    }
-                pf[rt] = half8{(_Float16)e[0], (_Float16)e[1], (_Float16)e[2], (_Float16)e[3],
-                               (_Float16)e[4], (_Float16)e[5], (_Float16)e[6], (_Float16)e[7]};
-            }
-#pragma unroll
-            for (int nn = 0; nn < 2; nn++) {
-                const int n = 2 * b + nn;
-                half8 vf = q4_to_half8(vw[n]);
-#pragma unroll
-                for (int rt = 0; rt < NRT; rt++) acc[rt][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[rt], acc[rt][n], 0, 0, 0);
-            }
-        }
-    }
-
-    // ---- combine the waves of the workgroup (fixed wave order), write partials
-    float *sm_m = smem;
-    float *sm_l = smem + kWaves * ROWS;
-    float *sm_o = smem + 2 * kWaves * ROWS;
+    // ---- combine the waves of each row tile (fixed wave order), write partials
     constexpr int OS = 132;  // padded row stride
-#pragma unroll
-    for (int rt = 0; rt < NRT; rt++) {
-        float l = l_run[rt];
+    float *sm_m = smem;
+    float *sm_l = smem + kSplitWaves * 16;
+    float *sm_o = smem + 2 * kSplitWaves * 16;
+    {
+        float l = st.l_run;
         l += __shfl_xor(l, 16);
         l += __shfl_xor(l, 32);
-        const int r = rt * 16 + c16;
         if (grp == 0) {
-            sm_m[wave * ROWS + r] = m_run[rt];
-            sm_l[wave * ROWS + r] = l;
+            sm_m[wave * 16 + c16] = st.m_ref;
+            sm_l[wave * 16 + c16] = l;
         }
 #pragma unroll
         for (int n = 0; n < 8; n++)
-            *reinterpret_cast<floatx4 *>(&sm_o[(wave * ROWS + r) * OS + 16 * n + 4 * grp]) = acc[rt][n];
+            *reinterpret_cast<floatx4 *>(&sm_o[(wave * 16 + c16) * OS + 16 * n + 4 * grp]) = st.acc[n];
     }
     __syncthreads();
 
     const uint32_t units = a.W * a.Hq;
-    const uint32_t rows_here = min((uint32_t)ROWS, rows_kv - row0);
+    const uint32_t block_row0 = blockIdx.z * (16 * RT);
+    const uint32_t rows_here = min((uint32_t)(16 * RT), rows_kv - block_row0);
     for (uint32_t idx = threadIdx.x; idx < rows_here * 128; idx += blockDim.x) {
         const uint32_t r = idx >> 7, t = idx & 127;
+        const uint32_t w0 = (r >> 4) * RTW, rr = r & 15;
         float M = kNegInf;
 #pragma unroll
-        for (int w = 0; w < kWaves; w++) M = fmaxf(M, sm_m[w * ROWS + r]);
+        for (int w = 0; w < RTW; w++) M = fmaxf(M, sm_m[(w0 + w) * 16 + rr]);
         float L = 0.f, A = 0.f;
         if (M != kNegInf) {
 #pragma unroll
-            for (int w = 0; w < kWaves; w++) {
-                float f = fast_exp2(sm_m[w * ROWS + r] - M);
-                L += f * sm_l[w * ROWS + r];
-                A += f * sm_o[(w * ROWS + r) * OS + t];
+            for (int w = 0; w < RTW; w++) {
+                const float mw = sm_m[(w0 + w) * 16 + rr];
+                if (mw == kNegInf) continue;
+                const float f = fast_exp2(mw - M);
+                L += f * sm_l[(w0 + w) * 16 + rr];
+                A += f * sm_o[((w0 + w) * 16 + rr) * OS + t];
             }
         }
-        const uint32_t rk = row0 + r;
+        const uint32_t rk = block_row0 + r;
         const uint32_t wq = rk / a.G, hh = rk - wq * a.G;
         const uint32_t unit = wq * a.Hq + kvh * a.G + hh;
         const size_t pu = (size_t)split * units + unit;
@@ -333,28 +441,75 @@ __global__ __launch_bounds__(256) void split_kernel(const SplitArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Merge kernel: one wavefront per (row, query head) unit; lane owns dims
-// 2*lane, 2*lane + 1.  Splits are folded in index order.
+// Merge kernel: one 256-thread workgroup per (row, query head) unit.
+//   1. M = max of the split maxima (splits with l = 0 are empty and skipped)
+//   2. weights w_s = 2^(m_s - M) into LDS, L = sum_s w_s l_s
+//   3. thread (dim t, half h) sums w_s acc_s[t] over splits s = h, h+2, ...
+//      (loads unrolled so many are in flight), the two halves are added
+//      in order and divided by L.
 // ---------------------------------------------------------------------------
+constexpr int kMergeMaxSplits = 4096;
+
 __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
-    const int lane = threadIdx.x & 63;
-    const uint32_t unit = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (unit >= a.units) return;
-    float M = kNegInf, L = 0.f, o0 = 0.f, o1 = 0.f;
-    for (uint32_t s = 0; s < a.n_splits; s++) {
-        const size_t pu = (size_t)s * a.units + unit;
-        const float2 ml = *reinterpret_cast<const float2 *>(a.part_ml + pu * 2);
-        if (!(ml.y > 0.f)) continue;  // empty split
-        const float2 v = *reinterpret_cast<const float2 *>(a.part_o + pu * 128 + 2 * lane);
-        const float Mn = fmaxf(M, ml.x);
-        const float fa = fast_exp2(M - Mn), fb = fast_exp2(ml.x - Mn);
-        L = L * fa + ml.y * fb;
-        o0 = o0 * fa + v.x * fb;
-        o1 = o1 * fa + v.y * fb;
-        M = Mn;
+    __shared__ float sm_w[kMergeMaxSplits];
+    __shared__ float sm_red[256];
+    __shared__ float sm_half[128];
+    const int tid = threadIdx.x;
+    const uint32_t unit = blockIdx.x;
+    const uint32_t S = a.n_splits;
+    const float *ml = a.part_ml + (size_t)unit * 2;
+    const size_t ml_stride = (size_t)a.units * 2;
+
+    float m = kNegInf;
+    for (uint32_t s = tid; s < S; s += 256) {
+        const float2 v = *reinterpret_cast<const float2 *>(ml + s * ml_stride);
+        if (v.y > 0.f) m = fmaxf(m, v.x);
     }
-    const float inv = 1.f / L;
-    *reinterpret_cast<float2 *>(a.out + (size_t)unit * 128 + 2 * lane) = float2{o0 * inv, o1 * inv};
+    sm_red[tid] = m;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (tid < w) sm_red[tid] = fmaxf(sm_red[tid], sm_red[tid + w]);
+        __syncthreads();
+    }
+    const float M = sm_red[0];
+    __syncthreads();
+    float lsum = 0.f;
+    for (uint32_t s = tid; s < S; s += 256) {
+        const float2 v = *reinterpret_cast<const float2 *>(ml + s * ml_stride);
+        const float w = (v.y > 0.f) ? fast_exp2(v.x - M) : 0.f;
+        sm_w[s] = w;
+        lsum += w * v.y;
+    }
+    sm_red[tid] = lsum;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (tid < w) sm_red[tid] += sm_red[tid + w];
+        __syncthreads();
+    }
+    const float L = sm_red[0];
+
+    const int t = tid & 127, half = tid >> 7;
+    const float *po = a.part_o + (size_t)unit * 128 + t;
+    const size_t o_stride = (size_t)a.units * 128;
+    float acc = 0.f;
+    uint32_t s = half;
+    for (; s + 14 < S; s += 16) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; u++) v[u] = po[(size_t)(s + 2 * u) * o_stride];
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+            const float w = sm_w[s + 2 * u];
+            if (w != 0.f) acc += w * v[u];
+        }
+    }
+    for (; s < S; s += 2) {
+        const float w = sm_w[s];
+        if (w != 0.f) acc += w * po[(size_t)s * o_stride];
+    }
+    if (half == 1) sm_half[t] = acc;
+    __syncthreads();
+    if (half == 0) a.out[(size_t)unit * 128 + t] = (acc + sm_half[t]) / L;
 }
 
 // ---------------------------------------------------------------------------
@@ -372,12 +527,28 @@ __global__ void read_page_kernel(const SplitArgs a, uint32_t logical_page, uint8
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-size_t kvattn_split_smem_bytes(int nrt) { return (size_t)kvattn_dev::kWaves * nrt * 16 * (2 + 132) * sizeof(float); }
+size_t kvattn_split_smem_bytes(int rt) {
+    (void)rt;
+    return (size_t)kvattn_dev::kSplitWaves * 16 * (2 + 132) * sizeof(float);
+}
 
-hipError_t kvattn_launch_split(const SplitArgs &a, uint32_t n_items, uint32_t n_row_blocks, int nrt, hipStream_t s) {
-    dim3 grid(n_items, a.Hkv, n_row_blocks), block(256);
-    size_t smem = kvattn_split_smem_bytes(nrt);
-    if (nrt == 1)
+uint32_t kvattn_merge_max_splits() { return kvattn_dev::kMergeMaxSplits; }
+
+hipError_t kvattn_split_setup() {
+    const int bytes = (int)kvattn_split_smem_bytes(1);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kvattn_dev::split_kernel<1>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e != hipSuccess) return e;
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(&kvattn_dev::split_kernel<2>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+// rt: row tiles of 16 per workgroup (1 or 2); n_row_blocks blocks of 16 * rt rows.
+hipError_t kvattn_launch_split(const SplitArgs &a, uint32_t n_items, uint32_t n_row_blocks, int rt, hipStream_t s) {
+    (void)hipGetLastError();  // clear a stale error so the check below reports this launch
+    dim3 grid(n_items, a.Hkv, n_row_blocks), block(64 * kvattn_dev::kSplitWaves);
+    const size_t smem = kvattn_split_smem_bytes(rt);
+    if (rt == 1)
         hipLaunchKernelGGL(kvattn_dev::split_kernel<1>, grid, block, smem, s, a);
     else
         hipLaunchKernelGGL(kvattn_dev::split_kernel<2>, grid, block, smem, s, a);
@@ -385,12 +556,14 @@ hipError_t kvattn_launch_split(const SplitArgs &a, uint32_t n_items, uint32_t n_
 }
 
 hipError_t kvattn_launch_merge(const MergeArgs &a, hipStream_t s) {
-    dim3 grid((a.units + 3) / 4), block(256);
+    (void)hipGetLastError();
+    dim3 grid(a.units), block(256);
     hipLaunchKernelGGL(kvattn_dev::merge_kernel, grid, block, 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t kvattn_launch_read_page(const SplitArgs &a, uint32_t logical_page, uint8_t *dst, hipStream_t s) {
+    (void)hipGetLastError();
     hipLaunchKernelGGL(kvattn_dev::read_page_kernel, dim3(64), dim3(256), 0, s, a, logical_page, dst);
     return hipGetLastError();
 }

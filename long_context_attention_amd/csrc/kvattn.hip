@@ -81,6 +81,10 @@ int check_params(const kvattn_params &p, std::string &why) {
         why = "n_kv_heads too large";
         return KVATTN_E_UNSUPPORTED;
     }
+    if (p.max_pages_per_layer > kvattn_merge_max_splits()) {
+        why = "max_pages_per_layer exceeds the merge kernel's split capacity (4096 pages)";
+        return KVATTN_E_UNSUPPORTED;
+    }
     if (p.n_pool_pages >= 0x80000000u || p.n_ring_slots >= 0x40000000u || p.max_pages_per_layer >= 0x40000000u) {
         why = "pool / ring / page counts exceed the page-table encoding";
         return KVATTN_E_RANGE;
@@ -166,12 +170,18 @@ struct kvattn {
     size_t pool_bytes = 0, ring_bytes = 0, ws_bytes = 0;
     hipStream_t compute = nullptr, copy = nullptr;
     int device = 0;
+    int n_cus = 256;
     hipEvent_t upload_done = nullptr;
     std::vector<LayerState> layers;
     StreamScheduler sched;
     bool any_streamed = false, any_ring_slots = false;
     std::string err;
     float qscale = 0.f;
+    // optional per-launch timing of the split and merge kernels
+    bool profiling = false;
+    std::vector<hipEvent_t> prof_ev;   // pairs: [2i] before, [2i+1] after
+    std::vector<uint8_t> prof_kind;    // 0 split, 1 merge
+    size_t prof_used = 0;
 
     uint32_t *d_table(uint32_t layer) { return reinterpret_cast<uint32_t *>(wsp + ws.tables) + (size_t)layer * p.max_pages_per_layer; }
     uint32_t *d_list(uint32_t layer) { return reinterpret_cast<uint32_t *>(wsp + ws.lists) + (size_t)layer * p.max_pages_per_layer; }
@@ -215,7 +225,7 @@ SplitArgs base_args(kvattn_t h, uint32_t layer, uint32_t W, const float *q) {
     a.Hq = h->p.n_q_heads;
     a.Hkv = h->p.n_kv_heads;
     a.G = h->p.n_q_heads / h->p.n_kv_heads;
-    a.split_pages = 1;
+    a.split_chunks = h->p.page_tokens / 32;
     a.ring_base = 0;
     a.n_ring_slots = std::max<uint32_t>(1, h->p.n_ring_slots);
     a.page_bytes = h->lay.page_bytes;
@@ -229,35 +239,40 @@ SplitArgs base_args(kvattn_t h, uint32_t layer, uint32_t W, const float *q) {
     return a;
 }
 
-// Split plan of a call on an all-resident layer.
+// Split plan of a call on an all-resident layer.  A split is a range of
+// 32-key chunks of one KV head; narrow calls (rows per KV head <= 32) aim at
+// one workgroup per compute unit, wide calls (prefill) at up to 16 splits
+// per 32-row block.  The split count never exceeds the page count, which
+// bounds the partial buffer.
 struct Plan {
-    uint32_t split_pages, n_splits, n_row_blocks;
+    uint32_t split_chunks, n_splits, n_row_blocks;
     int nrt;
 };
 
-Plan plan_resident(const kvattn_params &p, uint32_t n_pages, uint32_t W, bool prefill, int n_cus) {
+Plan plan_resident(const kvattn_params &p, uint32_t n_tokens, uint32_t n_pages, uint32_t W, bool prefill, int n_cus) {
     const uint32_t G = p.n_q_heads / p.n_kv_heads;
     const uint32_t rows = W * G;
+    const uint32_t n_chunks = (n_tokens + 31) / 32;
+    const uint32_t cpp = p.page_tokens / 32;
     Plan pl;
     pl.nrt = rows <= 16 ? 1 : 2;
-    pl.n_row_blocks = (rows + 31) / 32;
-    if (pl.nrt == 1) pl.n_row_blocks = 1;
+    pl.n_row_blocks = pl.nrt == 1 ? 1 : (rows + 31) / 32;
+    const uint64_t cus = (uint64_t)std::max(n_cus, 1);
     if (!prefill && rows <= kNarrowRows) {
-        uint32_t sp = p.split_pages;
-        if (sp == 0) {
-            // enough workgroups to cover every CU about four times
-            const uint64_t target = 4ull * (uint64_t)std::max(n_cus, 1);
-            sp = (uint32_t)std::max<uint64_t>(1, ((uint64_t)n_pages * p.n_kv_heads) / target);
+        if (p.split_pages) {
+            pl.split_chunks = p.split_pages * cpp;
+        } else {
+            uint32_t splits = (uint32_t)std::max<uint64_t>(1, (cus + p.n_kv_heads - 1) / p.n_kv_heads);
+            splits = std::min(splits, n_pages);
+            pl.split_chunks = std::max<uint32_t>((n_chunks + splits - 1) / splits, std::min<uint32_t>(8, n_chunks));
         }
-        pl.split_pages = std::min(sp, n_pages);
     } else {
-        const uint64_t target = 8ull * (uint64_t)std::max(n_cus, 1);
         uint64_t per = (uint64_t)p.n_kv_heads * pl.n_row_blocks;
-        uint32_t splits = (uint32_t)std::min<uint64_t>(kPrefillMaxSplits, std::max<uint64_t>(1, target / per));
+        uint32_t splits = (uint32_t)std::min<uint64_t>(kPrefillMaxSplits, std::max<uint64_t>(1, 8 * cus / per));
         splits = std::min(splits, n_pages);
-        pl.split_pages = (n_pages + splits - 1) / splits;
+        pl.split_chunks = (n_chunks + splits - 1) / splits;
     }
-    pl.n_splits = (n_pages + pl.split_pages - 1) / pl.split_pages;
+    pl.n_splits = (n_chunks + pl.split_chunks - 1) / pl.split_chunks;
     return pl;
 }
 
@@ -272,6 +287,31 @@ int validate_call(kvattn_t h, uint32_t layer, const float *q, uint32_t W, const 
     return KVATTN_OK;
 }
 
+// Brackets a launch with timing events when profiling is on.
+int prof_begin(kvattn_t h, uint8_t kind, size_t *slot) {
+    *slot = SIZE_MAX;
+    if (!h->profiling) return KVATTN_OK;
+    if (h->prof_used >= h->prof_kind.size()) return KVATTN_OK;  // pool full: stop recording
+    *slot = h->prof_used++;
+    h->prof_kind[*slot] = kind;
+    HIP_TRY(h, hipEventRecord(h->prof_ev[2 * *slot], h->compute));
+    return KVATTN_OK;
+}
+
+int prof_end(kvattn_t h, size_t slot) {
+    if (slot == SIZE_MAX) return KVATTN_OK;
+    HIP_TRY(h, hipEventRecord(h->prof_ev[2 * slot + 1], h->compute));
+    return KVATTN_OK;
+}
+
+int launch_split(kvattn_t h, const SplitArgs &a, uint32_t n_items, uint32_t n_row_blocks, int nrt) {
+    size_t slot;
+    int rc = prof_begin(h, 0, &slot);
+    if (rc) return rc;
+    HIP_TRY(h, kvattn_launch_split(a, n_items, n_row_blocks, nrt, h->compute));
+    return prof_end(h, slot);
+}
+
 int run_merge(kvattn_t h, uint32_t W, uint32_t n_splits, float *out) {
     MergeArgs m;
     m.part_o = h->part_o();
@@ -279,8 +319,11 @@ int run_merge(kvattn_t h, uint32_t W, uint32_t n_splits, float *out) {
     m.n_splits = n_splits;
     m.units = W * h->p.n_q_heads;
     m.out = out;
+    size_t slot;
+    int rc = prof_begin(h, 1, &slot);
+    if (rc) return rc;
     HIP_TRY(h, kvattn_launch_merge(m, h->compute));
-    return KVATTN_OK;
+    return prof_end(h, slot);
 }
 
 int n_cus_of(int device) {
@@ -292,10 +335,11 @@ int n_cus_of(int device) {
 // Attention on a layer without streamed pages.
 int attend_resident(kvattn_t h, uint32_t layer, const float *q, uint32_t W, float *out, bool prefill) {
     const LayerState &L = h->layers[layer];
-    Plan pl = plan_resident(h->p, L.n_pages, W, prefill, n_cus_of(h->device));
+    Plan pl = plan_resident(h->p, L.n_tokens, L.n_pages, W, prefill, h->n_cus);
     SplitArgs a = base_args(h, layer, W, q);
-    a.split_pages = pl.split_pages;
-    HIP_TRY(h, kvattn_launch_split(a, pl.n_splits, pl.n_row_blocks, pl.nrt, h->compute));
+    a.split_chunks = pl.split_chunks;
+    int rc = launch_split(h, a, pl.n_splits, pl.n_row_blocks, pl.nrt);
+    if (rc) return rc;
     return run_merge(h, W, pl.n_splits, out);
 }
 
@@ -366,15 +410,15 @@ struct HipExec {
         const LayerState &L = h->layers[layer];
         if (!L.n_resident) return KVATTN_OK;
         a.list_offset = 0;
-        HIP_TRY(h, kvattn_launch_split(a, L.n_resident, 1, nrt, h->compute));
-        return KVATTN_OK;
+        return launch_split(h, a, L.n_resident, 1, nrt);
     }
     int compute(const ChunkRef &c) {
         const LayerState &L = h->layers[c.layer];
         HIP_TRY(h, hipStreamWaitEvent(h->compute, h->sched.ready_event(c.event), 0));
         a.list_offset = L.n_resident + c.first;
         a.ring_base = (uint32_t)(c.ordinal_base % h->p.n_ring_slots);
-        HIP_TRY(h, kvattn_launch_split(a, c.count, 1, nrt, h->compute));
+        int rc = launch_split(h, a, c.count, 1, nrt);
+        if (rc) return rc;
         HIP_TRY(h, hipEventRecord(h->sched.consumed_event(c.event), h->compute));
         return KVATTN_OK;
     }
@@ -387,7 +431,6 @@ int attend_streamed(kvattn_t h, uint32_t layer, const float *q, uint32_t W, floa
         return fail(h, KVATTN_E_UNSUPPORTED, "streamed layers support at most %u rows per KV head (W*G = %u)", kNarrowRows, W * G);
     HipExec x{h, W, q, out, base_args(h, layer, W, q), W * G <= 16 ? 1 : 2};
     x.a.page_list = h->d_list(layer);
-    x.a.split_pages = 1;
     return drive_streamed_layer(h->sched, layer, x);
 }
 
@@ -525,6 +568,8 @@ int kvattn_create(const kvattn_params *params, void *d_pool, size_t pool_bytes, 
     h->layers.resize(p.n_layers);
     hipError_t e = hipGetDevice(&h->device);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&h->upload_done, hipEventDisableTiming);
+    if (e == hipSuccess) h->n_cus = n_cus_of(h->device);
+    if (e == hipSuccess) e = kvattn_split_setup();
     if (e != hipSuccess) {
         int code = fail(nullptr, KVATTN_E_HIP, "device / event setup failed: %s", hipGetErrorString(e));
         delete h;
@@ -658,6 +703,45 @@ int kvattn_debug_read_page(kvattn_t h, uint32_t layer, uint32_t logical_page, vo
     return KVATTN_OK;
 }
 
+int kvattn_profile(kvattn_t h, uint32_t max_launches) {
+    if (!h) return fail(nullptr, KVATTN_E_ARG, "null handle");
+    if (max_launches == 0) {
+        h->profiling = false;
+        return KVATTN_OK;
+    }
+    HIP_TRY(h, hipStreamSynchronize(h->compute));
+    if (h->prof_kind.size() < max_launches) {
+        for (hipEvent_t e : h->prof_ev) (void)hipEventDestroy(e);
+        h->prof_ev.assign(2 * (size_t)max_launches, nullptr);
+        h->prof_kind.assign(max_launches, 0);
+        for (hipEvent_t &e : h->prof_ev) HIP_TRY(h, hipEventCreate(&e));
+    }
+    h->prof_used = 0;
+    h->profiling = true;
+    return KVATTN_OK;
+}
+
+int kvattn_profile_read(kvattn_t h, int reset, double *split_ms, uint32_t *n_split, double *merge_ms, uint32_t *n_merge) {
+    if (!h) return fail(nullptr, KVATTN_E_ARG, "null handle");
+    if (!split_ms || !n_split || !merge_ms || !n_merge) return fail(h, KVATTN_E_ARG, "null output");
+    HIP_TRY(h, hipStreamSynchronize(h->compute));
+    *split_ms = *merge_ms = 0.0;
+    *n_split = *n_merge = 0;
+    for (size_t i = 0; i < h->prof_used; i++) {
+        float ms = 0.f;
+        HIP_TRY(h, hipEventElapsedTime(&ms, h->prof_ev[2 * i], h->prof_ev[2 * i + 1]));
+        if (h->prof_kind[i] == 0) {
+            *split_ms += ms;
+            (*n_split)++;
+        } else {
+            *merge_ms += ms;
+            (*n_merge)++;
+        }
+    }
+    if (reset) h->prof_used = 0;
+    return KVATTN_OK;
+}
+
 int kvattn_destroy(kvattn_t h) {
     if (!h) return KVATTN_OK;
     int rc = KVATTN_OK;
@@ -665,6 +749,8 @@ int kvattn_destroy(kvattn_t h) {
     if (hipStreamSynchronize(h->compute) != hipSuccess) rc = KVATTN_E_HIP;
     h->sched.destroy();
     if (h->upload_done) (void)hipEventDestroy(h->upload_done);
+    for (hipEvent_t e : h->prof_ev)
+        if (e) (void)hipEventDestroy(e);
     delete h;
     return rc;
 }

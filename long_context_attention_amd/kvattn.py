@@ -58,7 +58,8 @@ def make_params(n_layers, n_q_heads, n_kv_heads, n_pool_pages, max_pages_per_lay
 _lib = None
 EXPORTS = ["kvattn_supported", "kvattn_page_bytes", "kvattn_workspace_bytes", "kvattn_create",
            "kvattn_upload_pages", "kvattn_set_layer", "kvattn_decode", "kvattn_verify", "kvattn_prefill_chunk",
-           "kvattn_synchronize", "kvattn_debug_read_page", "kvattn_validate_page_table", "kvattn_sched_simulate", "kvattn_destroy",
+           "kvattn_synchronize", "kvattn_debug_read_page", "kvattn_validate_page_table", "kvattn_sched_simulate",
+           "kvattn_profile", "kvattn_profile_read", "kvattn_destroy",
            "kvattn_last_error", "kvattn_global_error"]
 
 
@@ -99,6 +100,11 @@ def lib():
     L.kvattn_validate_page_table.restype = I
     L.kvattn_sched_simulate.argtypes = [U, U, U, P, P, U, P, U, ctypes.POINTER(U)]
     L.kvattn_sched_simulate.restype = I
+    L.kvattn_profile.argtypes = [P, U]
+    L.kvattn_profile.restype = I
+    L.kvattn_profile_read.argtypes = [P, I, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(U),
+                                      ctypes.POINTER(ctypes.c_double), ctypes.POINTER(U)]
+    L.kvattn_profile_read.restype = I
     L.kvattn_destroy.argtypes = [P]
     L.kvattn_destroy.restype = I
     L.kvattn_last_error.argtypes = [P]
@@ -204,6 +210,17 @@ class Handle:
         out = np.empty(page_bytes(self.params), dtype=np.uint8)
         _check(lib().kvattn_debug_read_page(self.h, layer, logical_page, out.ctypes.data), self.h)
         return out
+
+    def profile(self, max_launches):
+        _check(lib().kvattn_profile(self.h, max_launches), self.h)
+
+    def profile_read(self, reset=True):
+        """(split_ms_total, n_split, merge_ms_total, n_merge) since profile()."""
+        a, b = ctypes.c_double(), ctypes.c_double()
+        na, nb = ctypes.c_uint32(), ctypes.c_uint32()
+        _check(lib().kvattn_profile_read(self.h, int(reset), ctypes.byref(a), ctypes.byref(na), ctypes.byref(b),
+                                         ctypes.byref(nb)), self.h)
+        return a.value, na.value, b.value, nb.value
 
     def destroy(self):
         if self.h:

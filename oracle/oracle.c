@@ -33,7 +33,11 @@
  *       K scales  binary16 H * T * 4
  *       V nibbles uint8   H * T * 64 bytes
  *       V scales  binary16 H * T * 4
- *     Scales are stored [head][token][block].  K codes of head h start at
+ *     K scales are stored [head][token][block].  V scales of head h start at
+ *     h*T*8 bytes into their section, in 32-token tiles of 256 bytes; inside
+ *     a tile, token j (jj = j%32) and block b sit at
+ *         (b*4 + (jj%16)/4)*16 + ((jj/16)*4 + jj%4)*2.
+ *     K codes of head h start at
  *     h*T*128; a 16-token tile occupies 2048 bytes; inside it, the byte of
  *     (token j, dim t) is at
  *         (t/64)*1024 + (((t%32)/8)*16 + j%16)*16 + ((t/32)%2)*8 + t%8.
@@ -108,7 +112,9 @@ double oracle_k_scale(const uint8_t *page, int H, int T, int head, int j, int bl
 }
 
 double oracle_v_scale(const uint8_t *page, int H, int T, int head, int j, int block) {
-    size_t off = sec_v_scales(H, T) + (((size_t)head * T + j) * N_BLOCKS + block) * 2;
+    int jj = j % 32;
+    size_t off = sec_v_scales(H, T) + (size_t)head * T * N_BLOCKS * 2 + (size_t)(j / 32) * 256 +
+                 (size_t)(block * 4 + (jj % 16) / 4) * 16 + (size_t)((jj / 16) * 4 + jj % 4) * 2;
     return oracle_f16_to_f64(read_u16(page + off));
 }
 

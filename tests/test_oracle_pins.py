@@ -381,6 +381,8 @@ MUTATIONS = [
     ("causal mask off by one", "scale, 0, pos + 1, &m, &l, acc);", "scale, 0, pos, &m, &l, acc);"),
     ("K scale block index wrong", "sec_k_scales(H, T) + (((size_t)head * T + j) * N_BLOCKS + block) * 2;",
      "sec_k_scales(H, T) + (((size_t)head * T + j) * N_BLOCKS + (block ^ 1)) * 2;"),
+    ("V scale tile slot wrong", "(size_t)((jj / 16) * 4 + jj % 4) * 2;",
+     "(size_t)((jj / 16) * 4 + (jj + 1) % 4) * 2;"),
     ("V tile stride wrong", "(size_t)head * T * (HEAD_DIM / 2) + (size_t)(j / 32) * 2048;",
      "(size_t)head * T * (HEAD_DIM / 2) + (size_t)(j / 32) * 1024;"),
 ]
