@@ -148,9 +148,12 @@ int kvattn_upload_pages(kvattn_t h, const void *h_pages, const uint32_t *dst, ui
  * twice, names KVATTN_PT_HOST without a host history, or mixes
  * caller-placed ring slots with streamed pages on one handle (the scheduler
  * owns the ring once any page streams).  h_history: the layer's pages in
- * logical order (ceil(n_tokens / page_tokens) pages, pinned host memory),
- * read for KVATTN_PT_HOST entries; may be NULL when there are none.  The
- * table is copied to the device (stream-ordered on the compute stream).
+ * logical order (ceil(n_tokens / page_tokens) pages), read for
+ * KVATTN_PT_HOST entries; may be NULL when there are none.  Pinned history
+ * (hipHostMalloc) is gathered into ring slots by a copy kernel on the copy
+ * stream that reads it over the host link; pageable history is copied with
+ * one hipMemcpyAsync per run of consecutive pages (slower).  The table is
+ * copied to the device.
  */
 int kvattn_set_layer(kvattn_t h, uint32_t layer, const uint32_t *page_table, uint32_t n_tokens,
                      const void *h_history);

@@ -34,7 +34,20 @@ struct MergeArgs {
     float *out;                   // [W][Hq][128]
 };
 
+// Host-to-ring copy of `count` streamed pages: streamed page o (first <= o <
+// first + count) is logical page list[o] of the pinned host history and goes
+// to ring slot (ring_base + o) mod n_slots.
+struct RingCopyArgs {
+    const uint8_t *history;       // device-visible address of the layer's pinned host pages
+    const uint32_t *list;         // the layer's streamed logical pages, in ordinal order
+    uint8_t *ring;
+    uint32_t first, count;
+    uint32_t ring_base, n_slots;
+    size_t page_bytes;
+};
+
 size_t kvattn_split_smem_bytes(int rt);
+hipError_t kvattn_launch_ring_copy(const RingCopyArgs &a, hipStream_t s);
 hipError_t kvattn_split_setup();
 uint32_t kvattn_merge_max_splits();
 // rt: row tiles of 16 rows per workgroup (1 or 2); n_row_blocks blocks of 16 * rt rows

@@ -513,6 +513,34 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Ring copy: the GPU reads the pinned host pages over the host link itself
+// (one launch gathers a whole chunk of scattered pages, which a DMA copy per
+// run of consecutive pages cannot keep busy).  A workgroup copies one slice
+// of one page with four 16-byte loads in flight per thread.
+// ---------------------------------------------------------------------------
+constexpr int kCopySlices = 8;
+
+__global__ __launch_bounds__(256) void ring_copy_kernel(const RingCopyArgs a) {
+    const uint32_t o = a.first + blockIdx.x / kCopySlices;
+    const uint32_t sl = blockIdx.x % kCopySlices;
+    const size_t n16 = a.page_bytes / 16;
+    const size_t per = (n16 + kCopySlices - 1) / kCopySlices;
+    const size_t b = sl * per, e = min(n16, b + per);
+    const uint4 *src = reinterpret_cast<const uint4 *>(a.history + (size_t)a.list[o] * a.page_bytes);
+    uint4 *dst = reinterpret_cast<uint4 *>(a.ring + (size_t)((a.ring_base + o) % a.n_slots) * a.page_bytes);
+    const size_t step = blockDim.x;
+    for (size_t i = b + threadIdx.x; i < e; i += 4 * step) {
+        uint4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++)
+            if (i + u * step < e) v[u] = src[i + u * step];
+#pragma unroll
+        for (int u = 0; u < 4; u++)
+            if (i + u * step < e) dst[i + u * step] = v[u];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Debug page read: copy a logical page's bytes via the kernels' resolver.
 // ---------------------------------------------------------------------------
 __global__ void read_page_kernel(const SplitArgs a, uint32_t logical_page, uint8_t *dst) {
@@ -552,6 +580,12 @@ hipError_t kvattn_launch_split(const SplitArgs &a, uint32_t n_items, uint32_t n_
         hipLaunchKernelGGL(kvattn_dev::split_kernel<1>, grid, block, smem, s, a);
     else
         hipLaunchKernelGGL(kvattn_dev::split_kernel<2>, grid, block, smem, s, a);
+    return hipGetLastError();
+}
+
+hipError_t kvattn_launch_ring_copy(const RingCopyArgs &a, hipStream_t s) {
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(kvattn_dev::ring_copy_kernel, dim3(a.count * kvattn_dev::kCopySlices), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -156,6 +156,7 @@ struct LayerState {
     uint32_t n_resident = 0, n_streamed = 0;
     bool uses_ring_slots = false;
     const uint8_t *history = nullptr;
+    const uint8_t *history_dev = nullptr;  // device-visible alias when the history is pinned
     std::vector<uint32_t> resident;   // logical pages, ascending
     std::vector<uint32_t> streamed;   // logical pages, ascending (ordinal order)
 };
@@ -388,12 +389,27 @@ struct HipExec {
     }
     int internal(const char *what) { return fail(h, KVATTN_E_STATE, "%s", what); }
     void begin(uint32_t) {}
-    // Runs of consecutive logical pages landing in consecutive ring slots
-    // become one hipMemcpyAsync each.
+    // A pinned history is gathered by the ring-copy kernel in one launch;
+    // otherwise runs of consecutive logical pages landing in consecutive
+    // ring slots become one hipMemcpyAsync each.
     int copy(const ChunkRef &c) {
         const LayerState &L = h->layers[c.layer];
         if (c.wait_event >= 0) HIP_TRY(h, hipStreamWaitEvent(h->copy, h->sched.consumed_event(c.wait_event), 0));
         const size_t pb = h->lay.page_bytes;
+        if (L.history_dev) {
+            RingCopyArgs r;
+            r.history = L.history_dev;
+            r.list = h->d_list(c.layer) + L.n_resident;
+            r.ring = h->ring;
+            r.first = c.first;
+            r.count = c.count;
+            r.ring_base = (uint32_t)(c.ordinal_base % h->p.n_ring_slots);
+            r.n_slots = h->p.n_ring_slots;
+            r.page_bytes = pb;
+            HIP_TRY(h, kvattn_launch_ring_copy(r, h->copy));
+            HIP_TRY(h, hipEventRecord(h->sched.ready_event(c.event), h->copy));
+            return KVATTN_OK;
+        }
         uint32_t o = c.first;
         while (o < c.first + c.count) {
             const uint32_t slot = (uint32_t)((c.ordinal_base + o) % h->p.n_ring_slots);
@@ -641,6 +657,14 @@ int kvattn_set_layer(kvattn_t h, uint32_t layer, const uint32_t *page_table, uin
     L.n_tokens = n_tokens;
     L.n_pages = n_pages;
     L.history = static_cast<const uint8_t *>(h_history);
+    if (h_history && chk.n_host) {
+        // pinned (hipHostMalloc) history: the ring-copy kernel reads it in place
+        void *dev = nullptr;
+        if (hipHostGetDevicePointer(&dev, const_cast<void *>(h_history), 0) == hipSuccess)
+            L.history_dev = static_cast<const uint8_t *>(dev);
+        else
+            (void)hipGetLastError();
+    }
     L.uses_ring_slots = chk.n_ring > 0;
     std::vector<uint32_t> dev(n_pages);
     for (uint32_t P = 0; P < n_pages; P++) {

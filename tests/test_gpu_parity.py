@@ -132,12 +132,14 @@ def test_split_count_sweep():
 
 
 # ------------------------------------------------------------------ streaming
-def test_streamed_matches_resident_bitwise():
-    """Layers whose non-resident pages stream from pinned host memory through
-    a small ring give the same bits as all-resident layers at one page per
-    split, for every layer of two passes and an out-of-order call."""
+@pytest.mark.parametrize("pinned", [True, False], ids=["pinned-history", "pageable-history"])
+def test_streamed_matches_resident_bitwise(pinned):
+    """Layers whose non-resident pages stream from host memory through a small
+    ring (gathered by the ring-copy kernel from pinned memory, or copied run by
+    run from pageable memory) give the same bits as all-resident layers at one
+    page per split, for every layer of two passes and an out-of-order call."""
     L, N, Hq, Hkv, W = 3, 20 * 256 + 100, 40, 8, 4
-    say(f"case streamed L={L} N={N} W={W} ring=5 chunk=2")
+    say(f"case streamed L={L} N={N} W={W} ring=5 chunk=2 pinned={pinned}")
     n = -(-N // 256)
     layers = [layer_kv(N, Hkv, wid=70, layer=l) for l in range(L)]
     qs = [inputs.draw_queries(W, Hq, l, 70) for l in range(L)]
@@ -148,7 +150,8 @@ def test_streamed_matches_resident_bitwise():
         res = inputs.resident_subset(n, int(round(0.4 * n)), l, 70)
         table = np.full(n, kv.PT_HOST, dtype=np.uint32)
         table[res] = l * n + np.arange(len(res))
-        host = layers[l].pages.contiguous().pin_memory()
+        host = layers[l].pages.contiguous()
+        host = host.pin_memory() if pinned else host.clone()
         hist.append(host)
         place(hs, l, layers[l], table, history=host)
         place(hr, l, layers[l], l * n + np.arange(n, dtype=np.uint32))
