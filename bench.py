@@ -53,6 +53,11 @@ def parse():
                          "eager: one C-ABI call per layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (testing only)")
+    ap.add_argument("--with-copy-kernel", action="store_true",
+                    help="after timing, run a plain elementwise copy of 256 MiB (read 256 MiB, write 256 MiB) "
+                         "three times: the reference dispatch for scaling HBM traffic counters")
+    ap.add_argument("--h2d-ceiling", action="store_true",
+                    help="only measure the host-to-device ceiling (pinned copies) and print it as JSON")
     return ap.parse_args()
 
 
@@ -113,6 +118,35 @@ def one_pass(h, qs, outs, kind, rows):
             h.prefill_chunk(l, qs[l], rows, outs[l])
 
 
+# --------------------------------------------------------------------------- host link
+def h2d_ceiling(torch, mb=436, reps=3):
+    """Host-to-device copy rates: one large pinned copy (the ceiling) and
+    page-sized pieces (425,984 B) into 64 rotating slots."""
+    n = mb * 1024 * 1024
+    page = 425984
+    host = torch.empty(n, dtype=torch.uint8, pin_memory=True)
+    host[::4096] = 1
+    dev = torch.empty(n, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.Stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = 0.0
+    with torch.cuda.stream(stream):
+        for _ in range(reps):
+            e0.record(stream)
+            dev.copy_(host, non_blocking=True)
+            e1.record(stream)
+            e1.synchronize()
+            best = max(best, n / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+        pieces = n // page
+        e0.record(stream)
+        for i in range(pieces):
+            dev[(i % 64) * page:(i % 64 + 1) * page].copy_(host[i * page:(i + 1) * page], non_blocking=True)
+        e1.record(stream)
+        e1.synchronize()
+        piece_rate = pieces * page / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    return {"contiguous_gbps": round(best, 2), "page_pieces_gbps": round(piece_rate, 2), "bytes": n}
+
+
 # --------------------------------------------------------------------------- cpu baseline
 def cpu_baseline(w, rows, kind, inputs):
     """The oracle (fp64 C, OpenMP over (row, head)) on a bounded sample of the
@@ -155,6 +189,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.h2d_ceiling:
+        print(json.dumps({"h2d_ceiling": h2d_ceiling(torch)}), flush=True)
+        return
     w = inputs.WORKLOADS[args.workload]
     n_layers = args.layers or w.n_layers
     streamed = w.resident_fraction < 1.0
@@ -207,19 +244,17 @@ def main():
     wall = time.perf_counter() - t_start
     elapsed_ms = e0.elapsed_time(e1)
     ms_per_step = elapsed_ms / args.steps
-    kernel_timing = "per-launch HIP events on the compute stream during the timed steps"
     passes_profiled = args.steps
-    if graph is not None:
-        # HIP cannot time events recorded inside a captured graph: time the
-        # same kernels launched eagerly, with per-launch events, over the same
-        # number of passes
-        kernel_timing = "per-launch HIP events on the compute stream, eager passes after the graph-timed steps"
-        h.profile(max(1, args.steps) * launches_per_pass)
-        with torch.cuda.stream(stream):
-            for i in range(args.steps):
-                one_pass(h, qs, outs, kind, rows)
-    split_ms, n_split, merge_ms, n_merge = h.profile_read(reset=True)
-    h.profile(0)
+    if graph is None:
+        kernel_timing = "per-launch HIP events on the compute stream during the timed steps"
+        split_ms, n_split, merge_ms, n_merge = h.profile_read(reset=True)
+        h.profile(0)
+    else:
+        # a resident layer is one kernel launch (the split kernel merges in
+        # its last workgroup), so the HIP events around the timed steps give
+        # the kernel's mean duration (plus the gap between launches)
+        kernel_timing = "HIP events around the timed graph replays on the compute stream / launches"
+        split_ms, n_split, merge_ms, n_merge = elapsed_ms, args.steps * n_layers, 0.0, 0
 
     # ---- figures
     tokens_per_step = rows
@@ -254,7 +289,14 @@ def main():
         n_str = w.n_pages - w.n_resident
         h2d = n_str * w.page_bytes * n_layers / (ms_per_step / 1e3) / 1e9
         result["h2d_gbps"] = round(h2d, 2)
-    if n_split:
+    if streamed:
+        # the pass is bound by the host link: report it against the measured ceiling
+        ceiling = h2d_ceiling(torch)
+        result["h2d_ceiling"] = ceiling
+        c = ceiling["contiguous_gbps"]
+        result["roofline"] = {"bound": "host-link", "achieved": result["h2d_gbps"], "peak": c, "unit": "GB/s",
+                              "frac": round(result["h2d_gbps"] / c, 4), "traffic": None}
+    if n_split and not streamed:
         split_mean_ms = split_ms / n_split
         achieved = kv_bytes_layer * n_layers * passes_profiled / (split_ms / 1e3) / 1e9
         if kind == "prefill":
@@ -266,9 +308,18 @@ def main():
         else:
             result["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                                   "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None}
+    if n_split:
+        split_mean_ms = split_ms / n_split
         result["kernel_ms"] = {"split_mean": round(split_mean_ms, 5), "split_launches": n_split,
                                "merge_mean": round(merge_ms / max(n_merge, 1), 5), "merge_launches": n_merge,
                                "passes_profiled": passes_profiled, "timing": kernel_timing}
+    if args.with_copy_kernel:
+        a = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.neg(a, out=b)
+        torch.cuda.synchronize()
+        result["copy_kernel_bytes"] = {"read": a.numel() * 4, "write": b.numel() * 4}
     if not args.no_cpu_baseline:
         log("bench: timing the oracle on a CPU sample")
         result["cpu_baseline"] = cpu_baseline(w, rows, kind, inputs)

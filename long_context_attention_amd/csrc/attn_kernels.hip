@@ -27,6 +27,7 @@
 //                    (row, key, 32-dim block), rounded to f16 once.
 //   Softmax in fp32 with exp2; row max / sum reduced across the four
 //   16-lane groups of a wavefront.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -261,6 +262,109 @@ __device__ __forceinline__ void chunk_pv(RowState &st, const uint32_t vq[8], con
     }
 }
 
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int k = 32; k >= 1; k >>= 1) x = fmaxf(x, __shfl_xor(x, k));
+    return x;
+}
+
+// Butterfly sum: a + b == b + a, so every lane ends with the same bits.
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int k = 32; k >= 1; k >>= 1) x += __shfl_xor(x, k);
+    return x;
+}
+
+// Block-wide log-sum-exp merge (Flash-Decoding's reduction step) of nrows
+// (row, query head) units over n_splits >= 1 split partials (m, l, acc[128]).
+// For row r (unit unit_of(r)): M = max m_s over splits with l_s > 0,
+// w_s = 2^(m_s - M) (0 for empty splits), L = sum w_s l_s, out[t] =
+// (sum_s w_s acc_s[t]) / L.  One wave per row computes M, w and L (lane j
+// sums splits j, j + 64, ... then a butterfly); dimension t sums splits in
+// order.  The bits depend only on the partials, never on the block size, so
+// the fused merge and the merge kernel agree exactly.
+// Latency: each thread issues its first (m, l) and the first 32 splits of
+// its first two dimensions before anything waits, so up to 32 splits and
+// 2 x blockDim dimensions take one memory round trip.
+// wl: LDS for nrows * n_splits float2; row_ml: LDS for nrows float2.
+constexpr int kMergeBatch = 32;
+
+template <class UnitOf>
+__device__ __forceinline__ void merge_rows(const float *part_ml, const float *part_o, float *out, uint32_t n_splits,
+                                           uint32_t units, uint32_t nrows, UnitOf unit_of, float2 *wl,
+                                           float2 *row_ml) {
+    const uint32_t nt = blockDim.x, tid = threadIdx.x;
+    const size_t mls = (size_t)units * 2, pos = (size_t)units * 128;
+    const uint32_t n_ml = nrows * n_splits, n_items = nrows * 128;
+    auto ml_at = [&](uint32_t i) {
+        const uint32_t r = i / n_splits, s = i - r * n_splits;
+        return *reinterpret_cast<const float2 *>(part_ml + s * mls + (size_t)unit_of(r) * 2);
+    };
+    auto po_of = [&](uint32_t i) { return part_o + (size_t)unit_of(i >> 7) * 128 + (i & 127); };
+    // clamped addresses keep every early load unconditional
+    const float2 ml0 = ml_at(min(tid, n_ml - 1));
+    const float *po0 = po_of(min(tid, n_items - 1)), *po1 = po_of(min(tid + nt, n_items - 1));
+    float o0[kMergeBatch], o1[kMergeBatch];
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; k++) {
+        const size_t off = (size_t)min((uint32_t)k, n_splits - 1) * pos;
+        o0[k] = po0[off];
+        o1[k] = po1[off];
+    }
+    if (tid < n_ml) wl[tid] = ml0;
+    for (uint32_t i = tid + nt; i < n_ml; i += nt) wl[i] = ml_at(i);
+    __syncthreads();
+    const uint32_t lane = tid & 63, nw = nt >> 6;
+    for (uint32_t r = __builtin_amdgcn_readfirstlane(tid >> 6); r < nrows; r += nw) {
+        float2 *row = wl + r * n_splits;
+        float M = kNegInf;
+        for (uint32_t s = lane; s < n_splits; s += 64) {
+            const float2 v = row[s];
+            if (v.y > 0.f) M = fmaxf(M, v.x);
+        }
+        M = wave_max(M);
+        float L = 0.f;
+        for (uint32_t s = lane; s < n_splits; s += 64) {
+            const float2 v = row[s];
+            const float w = v.y > 0.f ? fast_exp2(v.x - M) : 0.f;
+            row[s].x = w;
+            L += w * v.y;
+        }
+        L = wave_sum(L);
+        if (lane == 0) row_ml[r] = make_float2(M, L);
+    }
+    __syncthreads();
+    const uint32_t nb0 = min(n_splits, (uint32_t)kMergeBatch);
+    // dimension i: splits [0, 32) from `first`, the rest loaded here
+    auto finish = [&](uint32_t i, const float(&first)[kMergeBatch]) {
+        const uint32_t r = i >> 7;
+        const float2 *row = wl + r * n_splits;
+        const float *po = po_of(i);
+        float A = 0.f;
+#pragma unroll
+        for (int k = 0; k < kMergeBatch; k++)
+            if ((uint32_t)k < nb0) A += row[k].x * first[k];
+        for (uint32_t s0 = kMergeBatch; s0 < n_splits; s0 += kMergeBatch) {
+            float ob[kMergeBatch];
+#pragma unroll
+            for (int k = 0; k < kMergeBatch; k++) ob[k] = po[(size_t)min(s0 + k, n_splits - 1) * pos];
+#pragma unroll
+            for (int k = 0; k < kMergeBatch; k++)
+                if (s0 + k < n_splits) A += row[s0 + k].x * ob[k];
+        }
+        out[(size_t)unit_of(r) * 128 + (i & 127)] = A / row_ml[r].y;
+    };
+    if (tid < n_items) finish(tid, o0);
+    if (tid + nt < n_items) finish(tid + nt, o1);
+    for (uint32_t i = tid + 2 * nt; i < n_items; i += nt) {
+        const float *po = po_of(i);
+        float ob[kMergeBatch];
+#pragma unroll
+        for (int k = 0; k < kMergeBatch; k++) ob[k] = po[(size_t)min((uint32_t)k, n_splits - 1) * pos];
+        finish(i, ob);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Split kernel.  A workgroup of 8 waves handles one split (a range of 32-key
 // chunks) of one KV head for RT tiles of 16 query rows; 8 / RT waves share a
@@ -270,6 +374,8 @@ __device__ __forceinline__ void chunk_pv(RowState &st, const uint32_t vq[8], con
 // Q.K^T with chunk i-1's P.V, whose operands it carries over.
 // ---------------------------------------------------------------------------
 constexpr int kSplitWaves = 8;
+// dynamic LDS of the split kernel: per wave 16 m, 16 l and 16 x 132 acc
+constexpr int kSplitLdsFloats = kSplitWaves * 16 * (2 + 132);
 
 template <int RT>
 __global__ __launch_bounds__(64 * kSplitWaves, 1) void split_kernel(const SplitArgs a) {
@@ -438,78 +544,56 @@ __global__ __launch_bounds__(64 * kSplitWaves, 1) void split_kernel(const SplitA
             a.part_ml[pu * 2 + 1] = L;
         }
     }
+
+    // ---- fused merge: the last workgroup of this (KV head, row block) folds
+    // every split of its rows, in split order, into the output
+    if (a.counters) {
+        // One thread fences for the whole workgroup: every wave waits for its
+        // partial stores to complete, the barrier orders them before that
+        // thread's device-scope release (an L2 write-back on this chip), and
+        // its acquire (an L2 invalidate) before the merge's loads.  Eight waves each fencing would flush and
+        // invalidate the XCD's L2 eight times per workgroup.
+        __shared__ uint32_t sm_last;
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have reached L2
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint32_t *cnt = a.counters + (size_t)kvh * gridDim.z + blockIdx.z;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const bool last = (old == a.n_splits - 1);
+            if (last) {
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                *cnt = 0;  // ready for the next call on the stream
+            }
+            sm_last = last;
+        }
+        __syncthreads();
+        if (!sm_last) return;
+        __shared__ float2 sm_row_ml[16 * RT];
+        const uint32_t G = a.G, Hq = a.Hq;
+        merge_rows(
+            a.part_ml, a.part_o, a.out, a.n_splits, units, rows_here,
+            [=](uint32_t r) {
+                const uint32_t rk = block_row0 + r;
+                const uint32_t wq = rk / G, hh = rk - wq * G;
+                return wq * Hq + kvh * G + hh;
+            },
+            reinterpret_cast<float2 *>(smem), sm_row_ml);
+    }
 }
 
 // ---------------------------------------------------------------------------
-// Merge kernel: one 256-thread workgroup per (row, query head) unit.
-//   1. M = max of the split maxima (splits with l = 0 are empty and skipped)
-//   2. weights w_s = 2^(m_s - M) into LDS, L = sum_s w_s l_s
-//   3. thread (dim t, half h) sums w_s acc_s[t] over splits s = h, h+2, ...
-//      (loads unrolled so many are in flight), the two halves are added
-//      in order and divided by L.
+// Merge kernel (layers with streamed pages, whose splits come from several
+// launches): one 128-thread workgroup per (row, query head) unit, thread t
+// folds dimension t with the same arithmetic as the fused merge.
 // ---------------------------------------------------------------------------
 constexpr int kMergeMaxSplits = 4096;
 
-__global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
-    __shared__ float sm_w[kMergeMaxSplits];
-    __shared__ float sm_red[256];
-    __shared__ float sm_half[128];
-    const int tid = threadIdx.x;
+__global__ __launch_bounds__(128) void merge_kernel(const MergeArgs a) {
+    __shared__ float2 wl[kMergeMaxSplits];
+    __shared__ float2 row_ml[1];
     const uint32_t unit = blockIdx.x;
-    const uint32_t S = a.n_splits;
-    const float *ml = a.part_ml + (size_t)unit * 2;
-    const size_t ml_stride = (size_t)a.units * 2;
-
-    float m = kNegInf;
-    for (uint32_t s = tid; s < S; s += 256) {
-        const float2 v = *reinterpret_cast<const float2 *>(ml + s * ml_stride);
-        if (v.y > 0.f) m = fmaxf(m, v.x);
-    }
-    sm_red[tid] = m;
-    __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
-        if (tid < w) sm_red[tid] = fmaxf(sm_red[tid], sm_red[tid + w]);
-        __syncthreads();
-    }
-    const float M = sm_red[0];
-    __syncthreads();
-    float lsum = 0.f;
-    for (uint32_t s = tid; s < S; s += 256) {
-        const float2 v = *reinterpret_cast<const float2 *>(ml + s * ml_stride);
-        const float w = (v.y > 0.f) ? fast_exp2(v.x - M) : 0.f;
-        sm_w[s] = w;
-        lsum += w * v.y;
-    }
-    sm_red[tid] = lsum;
-    __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
-        if (tid < w) sm_red[tid] += sm_red[tid + w];
-        __syncthreads();
-    }
-    const float L = sm_red[0];
-
-    const int t = tid & 127, half = tid >> 7;
-    const float *po = a.part_o + (size_t)unit * 128 + t;
-    const size_t o_stride = (size_t)a.units * 128;
-    float acc = 0.f;
-    uint32_t s = half;
-    for (; s + 14 < S; s += 16) {
-        float v[8];
-#pragma unroll
-        for (int u = 0; u < 8; u++) v[u] = po[(size_t)(s + 2 * u) * o_stride];
-#pragma unroll
-        for (int u = 0; u < 8; u++) {
-            const float w = sm_w[s + 2 * u];
-            if (w != 0.f) acc += w * v[u];
-        }
-    }
-    for (; s < S; s += 2) {
-        const float w = sm_w[s];
-        if (w != 0.f) acc += w * po[(size_t)s * o_stride];
-    }
-    if (half == 1) sm_half[t] = acc;
-    __syncthreads();
-    if (half == 0) a.out[(size_t)unit * 128 + t] = (acc + sm_half[t]) / L;
+    merge_rows(a.part_ml, a.part_o, a.out, a.n_splits, a.units, 1, [=](uint32_t) { return unit; }, wl, row_ml);
 }
 
 // ---------------------------------------------------------------------------
@@ -557,10 +641,11 @@ __global__ void read_page_kernel(const SplitArgs a, uint32_t logical_page, uint8
 // ---------------------------------------------------------------------------
 size_t kvattn_split_smem_bytes(int rt) {
     (void)rt;
-    return (size_t)kvattn_dev::kSplitWaves * 16 * (2 + 132) * sizeof(float);
+    return (size_t)kvattn_dev::kSplitLdsFloats * sizeof(float);
 }
 
 uint32_t kvattn_merge_max_splits() { return kvattn_dev::kMergeMaxSplits; }
+uint32_t kvattn_fused_merge_max_entries() { return kvattn_dev::kSplitLdsFloats / 2; }
 
 hipError_t kvattn_split_setup() {
     const int bytes = (int)kvattn_split_smem_bytes(1);
@@ -572,14 +657,23 @@ hipError_t kvattn_split_setup() {
 }
 
 // rt: row tiles of 16 per workgroup (1 or 2); n_row_blocks blocks of 16 * rt rows.
-hipError_t kvattn_launch_split(const SplitArgs &a, uint32_t n_items, uint32_t n_row_blocks, int rt, hipStream_t s) {
+// With events, the launch records them at the dispatch's own start and end
+// (timing without extra stream packets).
+hipError_t kvattn_launch_split(const SplitArgs &a, uint32_t n_items, uint32_t n_row_blocks, int rt, hipStream_t s,
+                               hipEvent_t ev_start, hipEvent_t ev_stop) {
     (void)hipGetLastError();  // clear a stale error so the check below reports this launch
     dim3 grid(n_items, a.Hkv, n_row_blocks), block(64 * kvattn_dev::kSplitWaves);
-    const size_t smem = kvattn_split_smem_bytes(rt);
-    if (rt == 1)
+    const uint32_t smem = (uint32_t)kvattn_split_smem_bytes(rt);
+    if (ev_start) {
+        if (rt == 1)
+            hipExtLaunchKernelGGL(kvattn_dev::split_kernel<1>, grid, block, smem, s, ev_start, ev_stop, 0, a);
+        else
+            hipExtLaunchKernelGGL(kvattn_dev::split_kernel<2>, grid, block, smem, s, ev_start, ev_stop, 0, a);
+    } else if (rt == 1) {
         hipLaunchKernelGGL(kvattn_dev::split_kernel<1>, grid, block, smem, s, a);
-    else
+    } else {
         hipLaunchKernelGGL(kvattn_dev::split_kernel<2>, grid, block, smem, s, a);
+    }
     return hipGetLastError();
 }
 
@@ -589,10 +683,13 @@ hipError_t kvattn_launch_ring_copy(const RingCopyArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t kvattn_launch_merge(const MergeArgs &a, hipStream_t s) {
+hipError_t kvattn_launch_merge(const MergeArgs &a, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
     (void)hipGetLastError();
-    dim3 grid(a.units), block(256);
-    hipLaunchKernelGGL(kvattn_dev::merge_kernel, grid, block, 0, s, a);
+    dim3 grid(a.units), block(128);
+    if (ev_start)
+        hipExtLaunchKernelGGL(kvattn_dev::merge_kernel, grid, block, 0, s, ev_start, ev_stop, 0, a);
+    else
+        hipLaunchKernelGGL(kvattn_dev::merge_kernel, grid, block, 0, s, a);
     return hipGetLastError();
 }
 

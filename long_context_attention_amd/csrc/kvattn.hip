@@ -105,8 +105,14 @@ size_t partial_units(const kvattn_params &p) {
     return (size_t)std::max(narrow, wide);
 }
 
+// Fused-merge counters: one per (KV head, row block of up to 32 rows).
+size_t counter_count(const kvattn_params &p) {
+    const uint64_t rows = (uint64_t)p.max_rows * (p.n_q_heads / p.n_kv_heads);
+    return (size_t)p.n_kv_heads * (size_t)((rows + 15) / 16);
+}
+
 struct WsLayout {
-    size_t tables, lists, staging, part_ml, part_o, total;
+    size_t tables, lists, staging, counters, part_ml, part_o, total;
 };
 
 WsLayout workspace_layout(const kvattn_params &p) {
@@ -116,7 +122,8 @@ WsLayout workspace_layout(const kvattn_params &p) {
     w.tables = 0;
     w.lists = align_up(ents);
     w.staging = w.lists + align_up(ents);
-    w.part_ml = w.staging + align_up(page_layout(p.n_kv_heads, p.page_tokens).page_bytes);
+    w.counters = w.staging + align_up(page_layout(p.n_kv_heads, p.page_tokens).page_bytes);
+    w.part_ml = w.counters + align_up(counter_count(p) * sizeof(uint32_t));
     w.part_o = w.part_ml + align_up(units * 2 * sizeof(float));
     w.total = w.part_o + align_up(units * kHeadDim * sizeof(float));
     return w;
@@ -187,6 +194,7 @@ struct kvattn {
     uint32_t *d_table(uint32_t layer) { return reinterpret_cast<uint32_t *>(wsp + ws.tables) + (size_t)layer * p.max_pages_per_layer; }
     uint32_t *d_list(uint32_t layer) { return reinterpret_cast<uint32_t *>(wsp + ws.lists) + (size_t)layer * p.max_pages_per_layer; }
     float *part_ml() { return reinterpret_cast<float *>(wsp + ws.part_ml); }
+    uint32_t *counters() { return reinterpret_cast<uint32_t *>(wsp + ws.counters); }
     float *part_o() { return reinterpret_cast<float *>(wsp + ws.part_o); }
 };
 
@@ -237,6 +245,9 @@ SplitArgs base_args(kvattn_t h, uint32_t layer, uint32_t W, const float *q) {
     a.q = q;
     a.part_o = h->part_o();
     a.part_ml = h->part_ml();
+    a.counters = nullptr;
+    a.n_splits = 0;
+    a.out = nullptr;
     return a;
 }
 
@@ -288,29 +299,22 @@ int validate_call(kvattn_t h, uint32_t layer, const float *q, uint32_t W, const 
     return KVATTN_OK;
 }
 
-// Brackets a launch with timing events when profiling is on.
-int prof_begin(kvattn_t h, uint8_t kind, size_t *slot) {
-    *slot = SIZE_MAX;
-    if (!h->profiling) return KVATTN_OK;
-    if (h->prof_used >= h->prof_kind.size()) return KVATTN_OK;  // pool full: stop recording
-    *slot = h->prof_used++;
-    h->prof_kind[*slot] = kind;
-    HIP_TRY(h, hipEventRecord(h->prof_ev[2 * *slot], h->compute));
-    return KVATTN_OK;
-}
-
-int prof_end(kvattn_t h, size_t slot) {
-    if (slot == SIZE_MAX) return KVATTN_OK;
-    HIP_TRY(h, hipEventRecord(h->prof_ev[2 * slot + 1], h->compute));
-    return KVATTN_OK;
+// Timing events for the next launch when profiling is on (recorded by the
+// dispatch itself at its start and end).
+void prof_slot(kvattn_t h, uint8_t kind, hipEvent_t *start, hipEvent_t *stop) {
+    *start = *stop = nullptr;
+    if (!h->profiling || h->prof_used >= h->prof_kind.size()) return;  // pool full: stop recording
+    const size_t slot = h->prof_used++;
+    h->prof_kind[slot] = kind;
+    *start = h->prof_ev[2 * slot];
+    *stop = h->prof_ev[2 * slot + 1];
 }
 
 int launch_split(kvattn_t h, const SplitArgs &a, uint32_t n_items, uint32_t n_row_blocks, int nrt) {
-    size_t slot;
-    int rc = prof_begin(h, 0, &slot);
-    if (rc) return rc;
-    HIP_TRY(h, kvattn_launch_split(a, n_items, n_row_blocks, nrt, h->compute));
-    return prof_end(h, slot);
+    hipEvent_t e0, e1;
+    prof_slot(h, 0, &e0, &e1);
+    HIP_TRY(h, kvattn_launch_split(a, n_items, n_row_blocks, nrt, h->compute, e0, e1));
+    return KVATTN_OK;
 }
 
 int run_merge(kvattn_t h, uint32_t W, uint32_t n_splits, float *out) {
@@ -320,11 +324,10 @@ int run_merge(kvattn_t h, uint32_t W, uint32_t n_splits, float *out) {
     m.n_splits = n_splits;
     m.units = W * h->p.n_q_heads;
     m.out = out;
-    size_t slot;
-    int rc = prof_begin(h, 1, &slot);
-    if (rc) return rc;
-    HIP_TRY(h, kvattn_launch_merge(m, h->compute));
-    return prof_end(h, slot);
+    hipEvent_t e0, e1;
+    prof_slot(h, 1, &e0, &e1);
+    HIP_TRY(h, kvattn_launch_merge(m, h->compute, e0, e1));
+    return KVATTN_OK;
 }
 
 int n_cus_of(int device) {
@@ -339,9 +342,16 @@ int attend_resident(kvattn_t h, uint32_t layer, const float *q, uint32_t W, floa
     Plan pl = plan_resident(h->p, L.n_tokens, L.n_pages, W, prefill, h->n_cus);
     SplitArgs a = base_args(h, layer, W, q);
     a.split_chunks = pl.split_chunks;
-    int rc = launch_split(h, a, pl.n_splits, pl.n_row_blocks, pl.nrt);
-    if (rc) return rc;
-    return run_merge(h, W, pl.n_splits, out);
+    if ((uint64_t)16 * pl.nrt * pl.n_splits > kvattn_fused_merge_max_entries()) {
+        // too many splits to stage in LDS: partials, then the merge kernel
+        int rc = launch_split(h, a, pl.n_splits, pl.n_row_blocks, pl.nrt);
+        return rc != KVATTN_OK ? rc : run_merge(h, W, pl.n_splits, out);
+    }
+    // one launch: the last workgroup of each (KV head, row block) merges
+    a.counters = h->counters();
+    a.n_splits = pl.n_splits;
+    a.out = out;
+    return launch_split(h, a, pl.n_splits, pl.n_row_blocks, pl.nrt);
 }
 
 // One streamed layer's enqueue sequence, shared by the HIP path and the CPU
@@ -586,6 +596,7 @@ int kvattn_create(const kvattn_params *params, void *d_pool, size_t pool_bytes, 
     if (e == hipSuccess) e = hipEventCreateWithFlags(&h->upload_done, hipEventDisableTiming);
     if (e == hipSuccess) h->n_cus = n_cus_of(h->device);
     if (e == hipSuccess) e = kvattn_split_setup();
+    if (e == hipSuccess) e = hipMemset(static_cast<uint8_t *>(d_workspace) + ws.counters, 0, counter_count(p) * sizeof(uint32_t));
     if (e != hipSuccess) {
         int code = fail(nullptr, KVATTN_E_HIP, "device / event setup failed: %s", hipGetErrorString(e));
         delete h;
