@@ -24,12 +24,6 @@ struct SplitArgs {
     const float *q;               // [W][Hq][128]
     float *part_o;                // [splits][W*Hq][128]
     float *part_ml;               // [splits][W*Hq][2]
-    // Fused merge (optional): the last workgroup of each (KV head, row block)
-    // to finish merges all splits of its rows into out.  counters has
-    // Hkv * row blocks entries, zero on entry and left zero.
-    uint32_t *counters;           // nullptr = no fused merge (separate merge kernel)
-    uint32_t n_splits;            // splits of this call (all launches)
-    float *out;                   // [W][Hq][128]
 };
 
 struct MergeArgs {
@@ -56,8 +50,6 @@ size_t kvattn_split_smem_bytes(int rt);
 hipError_t kvattn_launch_ring_copy(const RingCopyArgs &a, hipStream_t s);
 hipError_t kvattn_split_setup();
 uint32_t kvattn_merge_max_splits();
-// Largest (rows per row block) x (split count) the fused merge can stage.
-uint32_t kvattn_fused_merge_max_entries();
 // rt: row tiles of 16 rows per workgroup (1 or 2); n_row_blocks blocks of 16 * rt rows
 hipError_t kvattn_launch_split(const SplitArgs &a, uint32_t n_items, uint32_t n_row_blocks, int rt, hipStream_t s,
                                hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);

@@ -84,39 +84,94 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 //   0x80000000 | s (bit 30 0) ring slot s placed by the caller
 //   0xC0000000 | o            streamed page with per-layer ordinal o: ring
 //                             slot (ring_base + o) mod n_ring_slots
+// The entry index is wave-uniform, so the entry comes through a scalar load.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ const uint8_t *resolve_page(const SplitArgs &a, uint32_t logical_page) {
-    uint32_t e = a.page_table[logical_page];
+__device__ __forceinline__ const uint8_t *page_base(const SplitArgs &a, uint32_t e) {
     if (e < 0x80000000u) return a.pool + (size_t)e * a.page_bytes;
     uint32_t v = e & 0x3FFFFFFFu;
     if (e & 0x40000000u) v = (a.ring_base + v) % a.n_ring_slots;  // both < 2^30: no overflow
     return a.ring + (size_t)v * a.page_bytes;
 }
 
-// ---------------------------------------------------------------------------
-// One 32-key chunk of one KV head.
-// In flight (registers): the lane's code bytes and 8 bytes of scales.
-//   kq[16]  K codes of 16-key tile tt (dwords 8tt .. 8tt+7): blocks 2k, 2k+1
-//           of load k, 8 codes each
-//   vq[8]   V codes, one dword per 16-dim tile
-//   sc      lanes 0-31: K scales of the chunk's 32 keys ([key][block], 256
-//           bytes); lanes 32-63: the chunk's V-scale tile (256 bytes)
-// The scales are shared by the 16 lanes of a group, so they go through a
-// 512-byte LDS slot per wave instead of being loaded 16 times.
-// ---------------------------------------------------------------------------
-struct ChunkG {
-    uint32_t kq[16];
-    uint32_t vq[8];
-    uint2 sc;
-};
+// Page-table and page-list reads through the constant address space: the
+// tables do not change during a launch, so wave-uniform reads become scalar
+// loads even after the loads the compiler cannot see (direct-to-LDS asm).
+typedef __attribute__((address_space(4))) const uint32_t const_u32;
+__device__ __forceinline__ uint32_t table_at(const uint32_t *t, uint32_t i) {
+    return reinterpret_cast<const_u32 *>(reinterpret_cast<uintptr_t>(t))[i];
+}
 
-// Scales of one chunk as the lane uses them.
-//   kd[16]  [tt][8]: binary16 pairs, key 4g + v of tile tt, block b at half 4v + b
-//   vd[16]  [b][4]: binary16 pairs of block b, operand slots 2i, 2i + 1
-struct ChunkS {
-    uint32_t kd[16];
-    uint32_t vd[16];
-};
+__device__ __forceinline__ const uint8_t *resolve_page(const SplitArgs &a, uint32_t logical_page) {
+    return page_base(a, table_at(a.page_table, logical_page));
+}
+
+// ---------------------------------------------------------------------------
+// One 32-key chunk of one KV head as staged in LDS (6656 bytes; each section
+// keeps the page's byte order):
+//   [0, 4096)     K codes, two 16-key tiles of 2048 bytes; a 64-lane read of
+//                 16 bytes per lane covers one 1024-byte quarter
+//   [4096, 6144)  V codes, two quarters
+//   [6144, 6400)  K scales, [key][block] binary16
+//   [6400, 6656)  the chunk's V-scale tile
+// Every wave owns a ring of kStages such buffers, filled by direct-to-LDS
+// loads (global_load_lds_dwordx4: 16 bytes per lane, no registers), so
+// kStages - 1 chunks stay in flight while the wave computes on another.
+// ---------------------------------------------------------------------------
+constexpr int kChunkBytes = 6656;
+constexpr int kOffV = 4096, kOffKS = 6144, kOffVS = 6400;
+constexpr int kStages = 3;
+constexpr int kDmaPerChunk = 7;  // 4 K, 2 V, 1 scales
+constexpr int kWaveRingBytes = kStages * kChunkBytes;
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 16 bytes per lane from g to LDS bytes [lds + 16 lane, +16).  m0 holds the
+// wave's LDS destination; one wait state separates its write from the load.
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// The compiler does not track the loads above, so the waits are explicit
+// (and are compiler barriers for memory accesses).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Wait until at most `newer` chunks (issued after the one needed) are in flight.
+__device__ __forceinline__ void wait_chunk(uint32_t newer) {
+    static_assert(kStages == 3, "wait_chunk covers up to two newer chunks");
+    if (newer >= 2)
+        wait_vmcnt<2 * kDmaPerChunk>();
+    else if (newer == 1)
+        wait_vmcnt<kDmaPerChunk>();
+    else
+        wait_vmcnt<0>();
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
+}
+
+// Issue the direct-to-LDS loads of chunk `chunk` of KV head kvh (page base
+// `base`) into the buffer at LDS address dst.
+__device__ __forceinline__ void issue_chunk(const SplitArgs &a, const uint8_t *base, uint32_t kvh, uint32_t jj0,
+                                            int lane, uint32_t dst) {
+    const size_t kv = (size_t)kvh * a.T + jj0;  // first key of the chunk in the head's section
+    const uint8_t *kc = base + kv * 128 + lane * 16;
+    const uint8_t *vc = base + a.sec_vc + kv * 64 + lane * 16;
+#pragma unroll
+    for (int q = 0; q < 4; q++) dma16(kc + 1024 * q, dst + 1024 * q);
+#pragma unroll
+    for (int q = 0; q < 2; q++) dma16(vc + 1024 * q, dst + kOffV + 1024 * q);
+    if (lane < 32) {
+        const uint8_t *sp = lane < 16 ? base + a.sec_kd + kv * 8 + lane * 16
+                                      : base + a.sec_vd + (size_t)kvh * a.T * 8 + (size_t)(jj0 >> 5) * 256 + (lane - 16) * 16;
+        dma16(sp, dst + kOffKS);
+    }
+}
 
 __device__ __forceinline__ void put4(uint32_t *d, const uint4 &x) {
     d[0] = x.x;
@@ -125,41 +180,34 @@ __device__ __forceinline__ void put4(uint32_t *d, const uint4 &x) {
     d[3] = x.w;
 }
 
-__device__ __forceinline__ void load_chunk(const SplitArgs &a, uint32_t kvh, uint32_t chunk, int lane, ChunkG &r) {
-    const uint32_t cpp = a.T >> 5;  // chunks per page
-    const uint32_t page = chunk / cpp;
-    const uint32_t jj0 = (chunk - page * cpp) << 5;
-    const uint8_t *base = resolve_page(a, page);
-    const size_t T = a.T;
-    const uint4 *kcp = reinterpret_cast<const uint4 *>(base + (size_t)kvh * T * 128 + (size_t)(jj0 >> 4) * 2048) + lane;
-    const uint4 *vcp = reinterpret_cast<const uint4 *>(base + a.sec_vc + (size_t)kvh * T * 64 + (size_t)(jj0 >> 5) * 2048) + lane;
-    const uint8_t *scp = lane < 32 ? base + a.sec_kd + ((size_t)kvh * T + jj0) * 8 + lane * 8
-                                   : base + a.sec_vd + (size_t)kvh * T * 8 + (size_t)(jj0 >> 5) * 256 + (lane - 32) * 8;
-    put4(r.kq + 0, kcp[0]);
-    put4(r.kq + 4, kcp[64]);
-    put4(r.kq + 8, kcp[128]);
-    put4(r.kq + 12, kcp[192]);
-    put4(r.vq + 0, vcp[0]);
-    put4(r.vq + 4, vcp[64]);
-    r.sc = *reinterpret_cast<const uint2 *>(scp);
-}
-
-// Stage the chunk's scales through the wave's LDS slot (64 x uint2) and read
-// back the lane's K scales; the V scales are read when the P' operands are
-// formed (read_vscales), so they do not occupy registers during Q.K^T.
-__device__ __forceinline__ void stage_scales(uint2 *slot, const ChunkG &g, int lane, int grp, ChunkS &s) {
-    slot[lane] = g.sc;
-    const uint4 *k4 = reinterpret_cast<const uint4 *>(slot);  // K scales: key j at bytes 8j
-    put4(s.kd + 0, k4[2 * grp]);                              // keys 4g .. 4g+3
-    put4(s.kd + 4, k4[2 * grp + 1]);
-    put4(s.kd + 8, k4[8 + 2 * grp]);                          // keys 16 + 4g ..
-    put4(s.kd + 12, k4[8 + 2 * grp + 1]);
-}
-
-__device__ __forceinline__ void read_vscales(const uint2 *slot, int grp, ChunkS &s) {
-    const uint4 *v4 = reinterpret_cast<const uint4 *>(slot + 32);  // V tile
+// K codes of the lane: kq[8tt + ...] = dwords of 16-key tile tt (blocks 2k,
+// 2k + 1 of quarter k, 8 codes each).
+__device__ __forceinline__ void read_kcodes(const uint8_t *stg, int lane, uint32_t kq[16]) {
 #pragma unroll
-    for (int b = 0; b < 4; b++) put4(s.vd + 4 * b, v4[b * 4 + grp]);
+    for (int q = 0; q < 4; q++) put4(kq + 4 * q, *reinterpret_cast<const uint4 *>(stg + 1024 * q + 16 * lane));
+}
+
+// K scales as the lane uses them: kd[8tt + ...] binary16 pairs, key 4g + v
+// of tile tt, block b at half 4v + b.
+__device__ __forceinline__ void read_kscales(const uint8_t *stg, int grp, uint32_t kd[16]) {
+    const uint4 *k4 = reinterpret_cast<const uint4 *>(stg + kOffKS);  // key j at bytes 8j
+    put4(kd + 0, k4[2 * grp]);
+    put4(kd + 4, k4[2 * grp + 1]);
+    put4(kd + 8, k4[8 + 2 * grp]);
+    put4(kd + 12, k4[8 + 2 * grp + 1]);
+}
+
+// V scales: vd[4b + ...] binary16 pairs of block b, operand slots 2i, 2i + 1.
+__device__ __forceinline__ void read_vscales(const uint8_t *stg, int grp, uint32_t vd[16]) {
+    const uint4 *v4 = reinterpret_cast<const uint4 *>(stg + kOffVS);
+#pragma unroll
+    for (int b = 0; b < 4; b++) put4(vd + 4 * b, v4[b * 4 + grp]);
+}
+
+// V codes of the lane: one dword per 16-dim tile.
+__device__ __forceinline__ void read_vcodes(const uint8_t *stg, int lane, uint32_t vq[8]) {
+#pragma unroll
+    for (int q = 0; q < 2; q++) put4(vq + 4 * q, *reinterpret_cast<const uint4 *>(stg + kOffV + 1024 * q + 16 * lane));
 }
 
 // binary16 half `i` of a packed array (lo half = even index)
@@ -172,7 +220,7 @@ __device__ __forceinline__ float half_of(const uint32_t *w, int i) { return (i &
 // the reference it used.
 constexpr float kRescale = 8.0f;
 
-// Per-wave state: one tile of 16 query rows (the lane's row is c16).
+// Per-wave state of one tile of 16 query rows (the lane's row is c16).
 struct RowState {
     half8 qf[4];     // B operand of S^T = K Q^T, block b
     int row_pos;     // position of the lane's row; -1 = padding row
@@ -181,40 +229,64 @@ struct RowState {
     floatx4 acc[8];  // O^T tile n: dims 16n + 4g + v of the lane's row
 };
 
-// Scores of one chunk: s[4tt + v] is key 16tt + 4g + v of the chunk,
-// log2-scaled.  One MFMA per 32-dim block, scaled by that block's d_K.
-template <bool MASK>
-__device__ __forceinline__ void chunk_scores(const RowState &st, const ChunkG &r, const ChunkS &sc, uint32_t kpos0,
-                                             int grp, float s[8]) {
+// Scores of one chunk for NT row tiles: s[t][4tt + v] is key 16tt + 4g + v
+// of the chunk for tile t, log2-scaled.  Each K fragment is dequantised once
+// and feeds one MFMA per tile and 32-dim block, scaled by that block's d_K.
+template <int NT>
+__device__ __forceinline__ void chunk_scores(const RowState (&st)[NT], const uint32_t kq[16], const uint32_t kd[16],
+                                             float (&s)[NT][8]) {
 #pragma unroll
     for (int tt = 0; tt < 2; tt++) {
 #pragma unroll
         for (int b = 0; b < 4; b++) {
-            const uint32_t *w = r.kq + 8 * tt + 4 * (b >> 1) + 2 * (b & 1);
+            const uint32_t *w = kq + 8 * tt + 4 * (b >> 1) + 2 * (b & 1);
             const half8 kf = q8_to_half8(w[0], w[1]);
-            const floatx4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, st.qf[b], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-            for (int v = 0; v < 4; v++) {
-                // fma with the binary16 operand read in place (v_fma_mix_f32)
-                const float dk = half_of(sc.kd + 8 * tt, 4 * v + b);
-                s[4 * tt + v] = __builtin_fmaf(dk, d[v], b == 0 ? 0.0f : s[4 * tt + v]);
+            for (int t = 0; t < NT; t++) {
+                const floatx4 d =
+                    __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, st[t].qf[b], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+                for (int v = 0; v < 4; v++) {
+                    // fma with the binary16 operand read in place (v_fma_mix_f32)
+                    const float dk = half_of(kd + 8 * tt, 4 * v + b);
+                    s[t][4 * tt + v] = __builtin_fmaf(dk, d[v], b == 0 ? 0.0f : s[t][4 * tt + v]);
+                }
             }
-        }
-    }
-    if (MASK) {
-#pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const int key = (int)(kpos0 + 16 * (i >> 2) + 4 * grp + (i & 3));
-            if (key > st.row_pos) s[i] = kNegInf;
         }
     }
 }
 
-// Softmax step of one chunk: lazy reference update (rescaling the
-// accumulators, which already hold every earlier chunk), probabilities, the
-// denominator, and the P' operands P * d_V of the four value blocks.
-template <bool MASK>
-__device__ __forceinline__ void chunk_probs(RowState &st, const float s[8], const uint2 *slot, int grp, half8 pf[4]) {
+// Causal mask of a chunk holding keys past some row's position.
+template <int NT>
+__device__ __forceinline__ void mask_scores(const RowState (&st)[NT], uint32_t kpos0, int grp, float (&s)[NT][8]) {
+#pragma unroll
+    for (int t = 0; t < NT; t++)
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const int key = (int)(kpos0 + 16 * (i >> 2) + 4 * grp + (i & 3));
+            if (key > st[t].row_pos) s[t][i] = kNegInf;
+        }
+}
+
+// Keys at or past the history length sit on page padding whose V scales may
+// be anything (NaN included); zero them in the staged tile so P * d_V is 0
+// for those keys (their P is 0).  Lane l owns tile bytes 4l .. 4l + 3:
+// block l / 16, keys 16 hi + 4 q + r with q = (l / 4) mod 4, hi = (l mod 4) / 2,
+// r = 2 (l mod 2) + i for the dword's half i.
+__device__ __forceinline__ void sanitize_vscales(uint8_t *stg, int lane, uint32_t n_valid) {
+    uint32_t *w = reinterpret_cast<uint32_t *>(stg + kOffVS) + lane;
+    const uint32_t key0 = 16 * ((lane & 3) >> 1) + 4 * ((lane >> 2) & 3) + 2 * (lane & 1);
+    uint32_t v = *w;
+    if (key0 >= n_valid) v &= 0xFFFF0000u;
+    if (key0 + 1 >= n_valid) v &= 0x0000FFFFu;
+    *w = v;
+}
+
+// Softmax step of one chunk for one row tile: lazy reference update
+// (rescaling the accumulators, which already hold every earlier chunk),
+// probabilities, the denominator, and the P' operands P * d_V of the four
+// value blocks.
+__device__ __forceinline__ void chunk_probs(RowState &st, const float s[8], const uint32_t vd[16], half8 pf[4]) {
     float m = s[0];
 #pragma unroll
     for (int i = 1; i < 8; i++) m = fmaxf(m, s[i]);
@@ -237,31 +309,218 @@ __device__ __forceinline__ void chunk_probs(RowState &st, const float s[8], cons
         lsum += p[i];
     }
     st.l_run += lsum;
-    ChunkS sc;
-    read_vscales(slot, grp, sc);
 #pragma unroll
     for (int b = 0; b < 4; b++) {
         float e[8];
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const float pd = __builtin_fmaf(p[i], half_of(sc.vd + 4 * b, i), 0.0f);
-            // masked keys have p = 0 but may sit on garbage (NaN) scales
-            e[i] = MASK ? ((p[i] == 0.f) ? 0.f : pd) : pd;
-        }
+        for (int i = 0; i < 8; i++) e[i] = __builtin_fmaf(p[i], half_of(vd + 4 * b, i), 0.0f);
         pf[b] = half8{(_Float16)e[0], (_Float16)e[1], (_Float16)e[2], (_Float16)e[3],
                       (_Float16)e[4], (_Float16)e[5], (_Float16)e[6], (_Float16)e[7]};
     }
 }
 
-// O^T += V^T P'^T for one chunk: dim tile n = 2b + nn of value block b.
-__device__ __forceinline__ void chunk_pv(RowState &st, const uint32_t vq[8], const half8 pf[4]) {
+// O^T += V^T P'^T for one chunk and NT row tiles: dim tile n = 2b + nn of
+// value block b; each V fragment is dequantised once.
+template <int NT>
+__device__ __forceinline__ void chunk_pv(RowState (&st)[NT], const uint32_t vq[8], const half8 (&pf)[NT][4]) {
 #pragma unroll
     for (int n = 0; n < 8; n++) {
         const half8 vf = q4_to_half8(vq[n]);
-        st.acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[n >> 1], st.acc[n], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < NT; t++)
+            st[t].acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[t][n >> 1], st[t].acc[n], 0, 0, 0);
     }
 }
 
+// ---------------------------------------------------------------------------
+// Split kernel.  A workgroup of 8 waves handles one split (a range of 32-key
+// chunks) of one KV head for a block of 16 * NT query rows; the waves take
+// the split's chunks round robin and each computes every row of the block,
+// so a chunk is loaded and dequantised once per block.  Rows of a KV head
+// are ordered (w, hh): r = w * G + hh, hh < G.
+// Each wave streams its chunks through its own LDS ring and overlaps chunk
+// i's Q.K^T with chunk i-1's P.V, whose operands it carries over.
+// ---------------------------------------------------------------------------
+constexpr int kSplitWaves = 8;
+constexpr int kSplitLdsBytes = kSplitWaves * kWaveRingBytes;
+
+template <int NT>
+__global__ __launch_bounds__(64 * kSplitWaves, 1) void split_kernel(const SplitArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // rings; reused by the combine and merge
+
+    const int lane = threadIdx.x & 63;
+    // wave index, made visibly uniform so chunk bookkeeping stays scalar
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int grp = lane >> 4;  // 16-lane group
+    const int c16 = lane & 15;
+    const uint32_t kvh = blockIdx.y;
+    const uint32_t block_row0 = blockIdx.z * (16 * NT);
+    const uint32_t rows_kv = a.W * a.G;
+    const uint32_t n_chunks_all = (a.n_tokens + 31) >> 5;
+    const uint32_t cpp = a.T >> 5;  // chunks per page
+
+    // ---- split -> chunk range
+    uint32_t split, c_begin, c_end;
+    if (a.page_list) {
+        split = table_at(a.page_list, a.list_offset + blockIdx.x);
+        c_begin = split * cpp;
+        c_end = min(c_begin + cpp, n_chunks_all);
+    } else {
+        split = blockIdx.x;
+        c_begin = blockIdx.x * a.split_chunks;
+        c_end = min(c_begin + a.split_chunks, n_chunks_all);
+    }
+    // chunks whose keys every row sees (keys <= n_tokens - W) need no mask
+    const uint32_t clean_end = (a.n_tokens - a.W + 1) >> 5;
+    // this wave's chunks: first + kSplitWaves * k, k < n_local
+    const uint32_t first = c_begin + wave;
+    const uint32_t n_local = first < c_end ? (c_end - 1 - first) / kSplitWaves + 1 : 0;
+
+    uint8_t *ring = smem + wave * kWaveRingBytes;
+    const uint32_t ring_lds = lds_addr(ring);
+    auto chunk_page = [&](uint32_t k) { return (first + kSplitWaves * k) / cpp; };
+    auto issue = [&](uint32_t k, uint32_t entry, uint32_t stage) {
+        const uint32_t chunk = first + kSplitWaves * k;
+        const uint32_t jj0 = (chunk - (chunk / cpp) * cpp) << 5;
+        issue_chunk(a, page_base(a, entry), kvh, jj0, lane, ring_lds + stage * kChunkBytes);
+    };
+
+    // ---- raw query loads first; their latency overlaps the ring prologue
+    RowState st[NT];
+    float4 qraw[NT][8];
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+        st[t].row_pos = -1;
+        st[t].m_ref = kNegInf;
+        st[t].l_run = 0.f;
+#pragma unroll
+        for (int n = 0; n < 8; n++) st[t].acc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 8; i++) qraw[t][i] = float4{0.f, 0.f, 0.f, 0.f};
+        const uint32_t r = block_row0 + 16 * t + c16;
+        if (r < rows_kv) {
+            const uint32_t w = r / a.G, hh = r - w * a.G;
+            const uint32_t h = kvh * a.G + hh;
+            st[t].row_pos = (int)(a.n_tokens - a.W + w);
+            const float4 *qp = reinterpret_cast<const float4 *>(a.q + ((size_t)w * a.Hq + h) * 128 + 8 * grp);
+#pragma unroll
+            for (int b = 0; b < 4; b++) {
+                qraw[t][2 * b] = qp[8 * b];
+                qraw[t][2 * b + 1] = qp[8 * b + 1];
+            }
+        }
+    }
+
+    // ---- ring prologue: chunks 0 .. kStages - 2 in flight; page entries
+    // (scalar loads) run one chunk ahead of their use
+    uint32_t entry_next = 0;
+    if (n_local > 0) {
+        issue(0, table_at(a.page_table, chunk_page(0)), 0);
+        if (n_local > 1) issue(1, table_at(a.page_table, chunk_page(1)), 1);
+        if (n_local > kStages - 1) entry_next = table_at(a.page_table, chunk_page(kStages - 1));
+    }
+
+    // ---- query fragments: lane (row c16, group g) holds dims 32b + 8g .. +8
+    // of block b, pre-scaled by softmax_scale * log2(e)
+#pragma unroll
+    for (int t = 0; t < NT; t++)
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+            const float4 x = qraw[t][2 * b], y = qraw[t][2 * b + 1];
+            st[t].qf[b] = half8{(_Float16)(x.x * a.qscale), (_Float16)(x.y * a.qscale), (_Float16)(x.z * a.qscale),
+                                (_Float16)(x.w * a.qscale), (_Float16)(y.x * a.qscale), (_Float16)(y.y * a.qscale),
+                                (_Float16)(y.z * a.qscale), (_Float16)(y.w * a.qscale)};
+        }
+
+    if (n_local > 0) {
+        uint32_t pv_vq[8];
+        half8 pv_pf[NT][4];
+        uint32_t stage = 0;
+        for (uint32_t k = 0; k < n_local; k++) {
+            // refill the buffer chunk k - 1 used (its reads are complete)
+            if (k + kStages - 1 < n_local) {
+                wait_lgkmcnt0();
+                issue(k + kStages - 1, entry_next, stage == 0 ? kStages - 1 : stage - 1);
+                if (k + kStages < n_local) entry_next = table_at(a.page_table, chunk_page(k + kStages));
+            }
+            wait_chunk(min((uint32_t)(kStages - 1), n_local - 1 - k));
+            const uint8_t *stg = ring + stage * kChunkBytes;
+            const uint32_t c = first + kSplitWaves * k;
+            uint32_t kq[16], kd[16], vd[16];
+            float s[NT][8];
+            read_kcodes(stg, lane, kq);
+            read_kscales(stg, grp, kd);
+            chunk_scores<NT>(st, kq, kd, s);
+            if (c >= clean_end) mask_scores<NT>(st, 32 * c, grp, s);
+            if (k > 0) chunk_pv<NT>(st, pv_vq, pv_pf);
+            if (32 * c + 32 > a.n_tokens) sanitize_vscales(ring + stage * kChunkBytes, lane, a.n_tokens - 32 * c);
+            read_vscales(stg, grp, vd);
+#pragma unroll
+            for (int t = 0; t < NT; t++) chunk_probs(st[t], s[t], vd, pv_pf[t]);
+            read_vcodes(stg, lane, pv_vq);
+            stage = stage == kStages - 1 ? 0 : stage + 1;
+        }
+        chunk_pv<NT>(st, pv_vq, pv_pf);
+    }
+
+    // ---- combine the waves (fixed wave order) and write the partials; the
+    // rings are reused once every wave is done with its own
+    wait_vmcnt<0>();
+    __syncthreads();
+    constexpr int R = 16 * NT;  // rows per block
+    constexpr int OS = 132;     // padded row stride
+    float *sm_m = reinterpret_cast<float *>(smem);
+    float *sm_l = sm_m + kSplitWaves * R;
+    float *sm_o = sm_l + kSplitWaves * R;
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+        float l = st[t].l_run;
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        const int row = 16 * t + c16;
+        if (grp == 0) {
+            sm_m[wave * R + row] = st[t].m_ref;
+            sm_l[wave * R + row] = l;
+        }
+#pragma unroll
+        for (int n = 0; n < 8; n++)
+            *reinterpret_cast<floatx4 *>(&sm_o[(wave * R + row) * OS + 16 * n + 4 * grp]) = st[t].acc[n];
+    }
+    __syncthreads();
+
+    const uint32_t units = a.W * a.Hq;
+    const uint32_t rows_here = min((uint32_t)R, rows_kv - block_row0);
+    for (uint32_t idx = threadIdx.x; idx < rows_here * 128; idx += blockDim.x) {
+        const uint32_t r = idx >> 7, t = idx & 127;
+        float M = kNegInf;
+#pragma unroll
+        for (int w = 0; w < kSplitWaves; w++) M = fmaxf(M, sm_m[w * R + r]);
+        float L = 0.f, A = 0.f;
+        if (M != kNegInf) {
+#pragma unroll
+            for (int w = 0; w < kSplitWaves; w++) {
+                const float mw = sm_m[w * R + r];
+                if (mw == kNegInf) continue;
+                const float f = fast_exp2(mw - M);
+                L += f * sm_l[w * R + r];
+                A += f * sm_o[(w * R + r) * OS + t];
+            }
+        }
+        const uint32_t rk = block_row0 + r;
+        const uint32_t wq = rk / a.G, hh = rk - wq * a.G;
+        const uint32_t unit = wq * a.Hq + kvh * a.G + hh;
+        const size_t pu = (size_t)split * units + unit;
+        a.part_o[pu * 128 + t] = A;
+        if (t == 0) {
+            a.part_ml[pu * 2] = M;
+            a.part_ml[pu * 2 + 1] = L;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Merge
+// ---------------------------------------------------------------------------
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
     for (int k = 32; k >= 1; k >>= 1) x = fmaxf(x, __shfl_xor(x, k));
@@ -281,8 +540,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 // w_s = 2^(m_s - M) (0 for empty splits), L = sum w_s l_s, out[t] =
 // (sum_s w_s acc_s[t]) / L.  One wave per row computes M, w and L (lane j
 // sums splits j, j + 64, ... then a butterfly); dimension t sums splits in
-// order.  The bits depend only on the partials, never on the block size, so
-// the fused merge and the merge kernel agree exactly.
+// order.
 // Latency: each thread issues its first (m, l) and the first 32 splits of
 // its first two dimensions before anything waits, so up to 32 splits and
 // 2 x blockDim dimensions take one memory round trip.
@@ -365,228 +623,7 @@ __device__ __forceinline__ void merge_rows(const float *part_ml, const float *pa
     }
 }
 
-// ---------------------------------------------------------------------------
-// Split kernel.  A workgroup of 8 waves handles one split (a range of 32-key
-// chunks) of one KV head for RT tiles of 16 query rows; 8 / RT waves share a
-// row tile and take its chunks round robin.  Rows of a KV head are ordered
-// (w, hh): r = w * G + hh, hh < G.
-// Each wave keeps the next chunk's loads in flight and overlaps chunk i's
-// Q.K^T with chunk i-1's P.V, whose operands it carries over.
-// ---------------------------------------------------------------------------
-constexpr int kSplitWaves = 8;
-// dynamic LDS of the split kernel: per wave 16 m, 16 l and 16 x 132 acc
-constexpr int kSplitLdsFloats = kSplitWaves * 16 * (2 + 132);
-
-template <int RT>
-__global__ __launch_bounds__(64 * kSplitWaves, 1) void split_kernel(const SplitArgs a) {
-    constexpr int RTW = kSplitWaves / RT;  // waves per row tile
-    extern __shared__ float smem[];        // [waves][16] m, [waves][16] l, [waves][16][132] acc
-    __shared__ uint2 sc_slot[kSplitWaves][64];
-
-    const int lane = threadIdx.x & 63;
-    // wave index, made visibly uniform so chunk bookkeeping stays scalar
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int rt = wave / RTW, cw = wave - rt * RTW;
-    const int grp = lane >> 4;  // 16-lane group
-    const int c16 = lane & 15;
-    const uint32_t kvh = blockIdx.y;
-    const uint32_t row0 = blockIdx.z * (16 * RT) + 16 * rt;  // first row of this wave's tile
-    const uint32_t rows_kv = a.W * a.G;
-    const uint32_t n_chunks_all = (a.n_tokens + 31) >> 5;
-
-    // ---- split -> chunk range
-    uint32_t split, c_begin, c_end;
-    if (a.page_list) {
-        split = a.page_list[a.list_offset + blockIdx.x];
-        c_begin = split * (a.T >> 5);
-        c_end = min(c_begin + (a.T >> 5), n_chunks_all);
-    } else {
-        split = blockIdx.x;
-        c_begin = blockIdx.x * a.split_chunks;
-        c_end = min(c_begin + a.split_chunks, n_chunks_all);
-    }
-    // chunks whose keys every row sees (keys <= n_tokens - W) need no mask
-    const uint32_t clean_end = (a.n_tokens - a.W + 1) >> 5;
-
-    // ---- row state and raw query loads (issued first: their latency then
-    // overlaps the chunk loads issued next)
-    RowState st;
-    float4 qraw[8];
-    st.row_pos = -1;
-    st.m_ref = kNegInf;
-    st.l_run = 0.f;
-#pragma unroll
-    for (int n = 0; n < 8; n++) st.acc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < 8; i++) qraw[i] = float4{0.f, 0.f, 0.f, 0.f};
-    {
-        const uint32_t r = row0 + c16;
-        if (r < rows_kv) {
-            const uint32_t w = r / a.G, hh = r - w * a.G;
-            const uint32_t h = kvh * a.G + hh;
-            st.row_pos = (int)(a.n_tokens - a.W + w);
-            const float4 *qp = reinterpret_cast<const float4 *>(a.q + ((size_t)w * a.Hq + h) * 128 + 8 * grp);
-#pragma unroll
-            for (int b = 0; b < 4; b++) {
-                qraw[2 * b] = qp[8 * b];
-                qraw[2 * b + 1] = qp[8 * b + 1];
-            }
-        }
-    }
-
-    uint2 *slot = sc_slot[wave];
-    uint32_t c = c_begin + cw;
-    // this wave's last chunk; the prefetch past it reloads that chunk (an L2
-    // hit) so every iteration issues the same loads and the wait for the
-    // current chunk never covers the next one
-    const uint32_t c_last = c < c_end ? c + ((c_end - 1 - c) / RTW) * RTW : c;
-    ChunkG ga, gb;
-    if (c < c_end) load_chunk(a, kvh, c, lane, ga);
-
-    // ---- query fragments: lane (row c16, group g) holds dims 32b + 8g .. +8
-    // of block b, pre-scaled by softmax_scale * log2(e)
-#pragma unroll
-    for (int b = 0; b < 4; b++) {
-        const float4 x = qraw[2 * b], y = qraw[2 * b + 1];
-        st.qf[b] = half8{(_Float16)(x.x * a.qscale), (_Float16)(x.y * a.qscale), (_Float16)(x.z * a.qscale),
-                         (_Float16)(x.w * a.qscale), (_Float16)(y.x * a.qscale), (_Float16)(y.y * a.qscale),
-                         (_Float16)(y.z * a.qscale), (_Float16)(y.w * a.qscale)};
-    }
-
-    if (c < c_end) {
-        ChunkS cs;
-        float s[8];
-        uint32_t pv_vq[8];
-        half8 pv_pf[4];
-        // first chunk: scores and probabilities only
-        load_chunk(a, kvh, min(c + RTW, c_last), lane, gb);
-        stage_scales(slot, ga, lane, grp, cs);
-        if (c < clean_end) {
-            chunk_scores<false>(st, ga, cs, 32 * c, grp, s);
-            chunk_probs<false>(st, s, slot, grp, pv_pf);
-        } else {
-            chunk_scores<true>(st, ga, cs, 32 * c, grp, s);
-            chunk_probs<true>(st, s, slot, grp, pv_pf);
-        }
-#pragma unroll
-        for (int i = 0; i < 8; i++) pv_vq[i] = ga.vq[i];
-        c += RTW;
-        // steady state: scores of chunk c, values of the chunk before it
-#define KVATTN_STEP(CUR, NXT)                                                   \
-    if (c >= c_end) break;                                                      \
-    load_chunk(a, kvh, min(c + RTW, c_last), lane, NXT);                        \
-    stage_scales(slot, CUR, lane, grp, cs);                                     \
-    if (c < clean_end) {                                                        \
-        chunk_scores<false>(st, CUR, cs, 32 * c, grp, s);                       \
-        chunk_pv(st, pv_vq, pv_pf);                                             \
-        chunk_probs<false>(st, s, slot, grp, pv_pf);                                   \
-    } else {                                                                    \
-        chunk_scores<true>(st, CUR, cs, 32 * c, grp, s);                        \
-        chunk_pv(st, pv_vq, pv_pf);                                             \
-        chunk_probs<true>(st, s, slot, grp, pv_pf);                                    \
-    }                                                                           \
-    for (int i = 0; i < 8; i++) pv_vq[i] = CUR.vq[i];                           \
-    c += RTW;
-        while (true) {
-            KVATTN_STEP(gb, ga)
-            KVATTN_STEP(ga, gb)
-        }
-#undef KVATTN_STEP
-        chunk_pv(st, pv_vq, pv_pf);
-    }
-
-    // ---- combine the waves of each row tile (fixed wave order), write partials
-    constexpr int OS = 132;  // padded row stride
-    float *sm_m = smem;
-    float *sm_l = smem + kSplitWaves * 16;
-    float *sm_o = smem + 2 * kSplitWaves * 16;
-    {
-        float l = st.l_run;
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
-        if (grp == 0) {
-            sm_m[wave * 16 + c16] = st.m_ref;
-            sm_l[wave * 16 + c16] = l;
-        }
-#pragma unroll
-        for (int n = 0; n < 8; n++)
-            *reinterpret_cast<floatx4 *>(&sm_o[(wave * 16 + c16) * OS + 16 * n + 4 * grp]) = st.acc[n];
-    }
-    __syncthreads();
-
-    const uint32_t units = a.W * a.Hq;
-    const uint32_t block_row0 = blockIdx.z * (16 * RT);
-    const uint32_t rows_here = min((uint32_t)(16 * RT), rows_kv - block_row0);
-    for (uint32_t idx = threadIdx.x; idx < rows_here * 128; idx += blockDim.x) {
-        const uint32_t r = idx >> 7, t = idx & 127;
-        const uint32_t w0 = (r >> 4) * RTW, rr = r & 15;
-        float M = kNegInf;
-#pragma unroll
-        for (int w = 0; w < RTW; w++) M = fmaxf(M, sm_m[(w0 + w) * 16 + rr]);
-        float L = 0.f, A = 0.f;
-        if (M != kNegInf) {
-#pragma unroll
-            for (int w = 0; w < RTW; w++) {
-                const float mw = sm_m[(w0 + w) * 16 + rr];
-                if (mw == kNegInf) continue;
-                const float f = fast_exp2(mw - M);
-                L += f * sm_l[(w0 + w) * 16 + rr];
-                A += f * sm_o[((w0 + w) * 16 + rr) * OS + t];
-            }
-        }
-        const uint32_t rk = block_row0 + r;
-        const uint32_t wq = rk / a.G, hh = rk - wq * a.G;
-        const uint32_t unit = wq * a.Hq + kvh * a.G + hh;
-        const size_t pu = (size_t)split * units + unit;
-        a.part_o[pu * 128 + t] = A;
-        if (t == 0) {
-            a.part_ml[pu * 2] = M;
-            a.part_ml[pu * 2 + 1] = L;
-        }
-    }
-
-    // ---- fused merge: the last workgroup of this (KV head, row block) folds
-    // every split of its rows, in split order, into the output
-    if (a.counters) {
-        // One thread fences for the whole workgroup: every wave waits for its
-        // partial stores to complete, the barrier orders them before that
-        // thread's device-scope release (an L2 write-back on this chip), and
-        // its acquire (an L2 invalidate) before the merge's loads.  Eight waves each fencing would flush and
-        // invalidate the XCD's L2 eight times per workgroup.
-        __shared__ uint32_t sm_last;
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have reached L2
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            uint32_t *cnt = a.counters + (size_t)kvh * gridDim.z + blockIdx.z;
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-            const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const bool last = (old == a.n_splits - 1);
-            if (last) {
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-                *cnt = 0;  // ready for the next call on the stream
-            }
-            sm_last = last;
-        }
-        __syncthreads();
-        if (!sm_last) return;
-        __shared__ float2 sm_row_ml[16 * RT];
-        const uint32_t G = a.G, Hq = a.Hq;
-        merge_rows(
-            a.part_ml, a.part_o, a.out, a.n_splits, units, rows_here,
-            [=](uint32_t r) {
-                const uint32_t rk = block_row0 + r;
-                const uint32_t wq = rk / G, hh = rk - wq * G;
-                return wq * Hq + kvh * G + hh;
-            },
-            reinterpret_cast<float2 *>(smem), sm_row_ml);
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Merge kernel (layers with streamed pages, whose splits come from several
-// launches): one 128-thread workgroup per (row, query head) unit, thread t
-// folds dimension t with the same arithmetic as the fused merge.
-// ---------------------------------------------------------------------------
+// One 128-thread workgroup per (row, query head) unit.
 constexpr int kMergeMaxSplits = 4096;
 
 __global__ __launch_bounds__(128) void merge_kernel(const MergeArgs a) {
@@ -641,11 +678,10 @@ __global__ void read_page_kernel(const SplitArgs a, uint32_t logical_page, uint8
 // ---------------------------------------------------------------------------
 size_t kvattn_split_smem_bytes(int rt) {
     (void)rt;
-    return (size_t)kvattn_dev::kSplitLdsFloats * sizeof(float);
+    return (size_t)kvattn_dev::kSplitLdsBytes;
 }
 
 uint32_t kvattn_merge_max_splits() { return kvattn_dev::kMergeMaxSplits; }
-uint32_t kvattn_fused_merge_max_entries() { return kvattn_dev::kSplitLdsFloats / 2; }
 
 hipError_t kvattn_split_setup() {
     const int bytes = (int)kvattn_split_smem_bytes(1);

@@ -105,14 +105,8 @@ size_t partial_units(const kvattn_params &p) {
     return (size_t)std::max(narrow, wide);
 }
 
-// Fused-merge counters: one per (KV head, row block of up to 32 rows).
-size_t counter_count(const kvattn_params &p) {
-    const uint64_t rows = (uint64_t)p.max_rows * (p.n_q_heads / p.n_kv_heads);
-    return (size_t)p.n_kv_heads * (size_t)((rows + 15) / 16);
-}
-
 struct WsLayout {
-    size_t tables, lists, staging, counters, part_ml, part_o, total;
+    size_t tables, lists, staging, part_ml, part_o, total;
 };
 
 WsLayout workspace_layout(const kvattn_params &p) {
@@ -122,8 +116,7 @@ WsLayout workspace_layout(const kvattn_params &p) {
     w.tables = 0;
     w.lists = align_up(ents);
     w.staging = w.lists + align_up(ents);
-    w.counters = w.staging + align_up(page_layout(p.n_kv_heads, p.page_tokens).page_bytes);
-    w.part_ml = w.counters + align_up(counter_count(p) * sizeof(uint32_t));
+    w.part_ml = w.staging + align_up(page_layout(p.n_kv_heads, p.page_tokens).page_bytes);
     w.part_o = w.part_ml + align_up(units * 2 * sizeof(float));
     w.total = w.part_o + align_up(units * kHeadDim * sizeof(float));
     return w;
@@ -194,7 +187,6 @@ struct kvattn {
     uint32_t *d_table(uint32_t layer) { return reinterpret_cast<uint32_t *>(wsp + ws.tables) + (size_t)layer * p.max_pages_per_layer; }
     uint32_t *d_list(uint32_t layer) { return reinterpret_cast<uint32_t *>(wsp + ws.lists) + (size_t)layer * p.max_pages_per_layer; }
     float *part_ml() { return reinterpret_cast<float *>(wsp + ws.part_ml); }
-    uint32_t *counters() { return reinterpret_cast<uint32_t *>(wsp + ws.counters); }
     float *part_o() { return reinterpret_cast<float *>(wsp + ws.part_o); }
 };
 
@@ -245,9 +237,6 @@ SplitArgs base_args(kvattn_t h, uint32_t layer, uint32_t W, const float *q) {
     a.q = q;
     a.part_o = h->part_o();
     a.part_ml = h->part_ml();
-    a.counters = nullptr;
-    a.n_splits = 0;
-    a.out = nullptr;
     return a;
 }
 
@@ -342,16 +331,10 @@ int attend_resident(kvattn_t h, uint32_t layer, const float *q, uint32_t W, floa
     Plan pl = plan_resident(h->p, L.n_tokens, L.n_pages, W, prefill, h->n_cus);
     SplitArgs a = base_args(h, layer, W, q);
     a.split_chunks = pl.split_chunks;
-    if ((uint64_t)16 * pl.nrt * pl.n_splits > kvattn_fused_merge_max_entries()) {
-        // too many splits to stage in LDS: partials, then the merge kernel
-        int rc = launch_split(h, a, pl.n_splits, pl.n_row_blocks, pl.nrt);
-        return rc != KVATTN_OK ? rc : run_merge(h, W, pl.n_splits, out);
-    }
-    // one launch: the last workgroup of each (KV head, row block) merges
-    a.counters = h->counters();
-    a.n_splits = pl.n_splits;
-    a.out = out;
-    return launch_split(h, a, pl.n_splits, pl.n_row_blocks, pl.nrt);
+    // partials, then the merge: a separate launch is cheaper than a device-
+    // wide release / counter / acquire handshake at the end of the split kernel
+    int rc = launch_split(h, a, pl.n_splits, pl.n_row_blocks, pl.nrt);
+    return rc != KVATTN_OK ? rc : run_merge(h, W, pl.n_splits, out);
 }
 
 // One streamed layer's enqueue sequence, shared by the HIP path and the CPU
@@ -596,7 +579,6 @@ int kvattn_create(const kvattn_params *params, void *d_pool, size_t pool_bytes, 
     if (e == hipSuccess) e = hipEventCreateWithFlags(&h->upload_done, hipEventDisableTiming);
     if (e == hipSuccess) h->n_cus = n_cus_of(h->device);
     if (e == hipSuccess) e = kvattn_split_setup();
-    if (e == hipSuccess) e = hipMemset(static_cast<uint8_t *>(d_workspace) + ws.counters, 0, counter_count(p) * sizeof(uint32_t));
     if (e != hipSuccess) {
         int code = fail(nullptr, KVATTN_E_HIP, "device / event setup failed: %s", hipGetErrorString(e));
         delete h;
