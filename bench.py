@@ -9,10 +9,12 @@ scattered over the pool by a seeded permutation.  Inputs are resident in HBM
 before timing starts.
 
 Prints one JSON line: throughput (tokens/s = query rows per pass x passes/s),
-the roofline of the dominant kernel (the split-KV attention kernel: quantised
-K+V bytes it must read per launch / its mean device time, from HIP events
-recorded around each launch on the compute stream during the timed region),
-and the fp64 CPU oracle timed on a bounded sample of the same workload.
+the roofline of the dominant kernel (the split-KV attention kernel with its
+log-sum-exp merge: the quantised K+V bytes a layer must read / the mean
+device time per layer, from HIP events on the compute stream around the
+timed graph replays; the HBM bytes the counters saw per layer, when the
+committed counter summary matches the kernel source), and the fp64 CPU
+oracle timed on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--workload decode-40k|verify-160k|stream-256k|prefill-120k]
@@ -118,6 +120,26 @@ def one_pass(h, qs, outs, kind, rows):
             h.prefill_chunk(l, qs[l], rows, outs[l])
 
 
+# --------------------------------------------------------------------------- traffic
+def measured_traffic(workload, rows):
+    """HBM bytes per layer call (split + merge kernels) from the committed
+    FETCH_SIZE / WRITE_SIZE counter summary of this workload, if it was taken
+    on the current kernel source (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_w{rows}.txt")
+    src = os.path.join(ROOT, "long_context_attention_amd", "csrc", "attn_kernels.hip")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        with open(src, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != sha:
+        return None
+    return rec.get("traffic_bytes_per_layer")
+
+
 # --------------------------------------------------------------------------- host link
 def h2d_ceiling(torch, mb=436, reps=3):
     """Host-to-device copy rates: one large pinned copy (the ceiling) and
@@ -148,31 +170,35 @@ def h2d_ceiling(torch, mb=436, reps=3):
 
 
 # --------------------------------------------------------------------------- cpu baseline
-def cpu_baseline(w, rows, kind, inputs):
+def cpu_baseline(w, rows, kind, inputs, budget_s=10.0):
     """The oracle (fp64 C, OpenMP over (row, head)) on a bounded sample of the
-    same workload, scaled to tokens/s of the full 64-layer pass."""
+    same workload: whole layers (a seeded sample of rows for prefill) until
+    about budget_s seconds of CPU work, scaled to tokens/s of the full
+    64-layer pass."""
     import oracle
     threads = max(1, min(16, os.cpu_count() or 1))
-    layer = 0
-    kvl = inputs.draw_layer(w.n_tokens, w.n_kv_heads, layer, w.wid, device="cuda")
-    pages = kvl.pages.cpu().numpy()
-    q = inputs.draw_queries(rows, w.n_q_heads, layer, w.wid, device="cuda").cpu().numpy()
     if kind == "prefill":
         # a sample of rows: first, last and 6 seeded others
         rng = np.random.default_rng(7)
         sample_rows = sorted({0, rows - 1, *rng.choice(rows, 6, replace=False).tolist()})
     else:
         sample_rows = list(range(rows))
-    t0 = time.perf_counter()
-    oracle.attend_paged(np.arange(pages.shape[0], dtype=np.uint32), w.n_tokens, 256, w.n_q_heads, w.n_kv_heads, q,
-                        inputs.scale_for(), pool=pages, rows=sample_rows, n_threads=threads)
-    dt = time.perf_counter() - t0
-    # full pass = n_layers layers x rows rows; sample = 1 layer x len(sample_rows) rows
-    pass_s = dt * w.n_layers * rows / len(sample_rows)
+    spent, layers = 0.0, 0
+    while layers < w.n_layers and spent < budget_s:
+        kvl = inputs.draw_layer(w.n_tokens, w.n_kv_heads, layers, w.wid, device="cuda")
+        pages = kvl.pages.cpu().numpy()
+        q = inputs.draw_queries(rows, w.n_q_heads, layers, w.wid, device="cuda").cpu().numpy()
+        del kvl
+        t0 = time.perf_counter()
+        oracle.attend_paged(np.arange(pages.shape[0], dtype=np.uint32), w.n_tokens, 256, w.n_q_heads,
+                            w.n_kv_heads, q, inputs.scale_for(), pool=pages, rows=sample_rows, n_threads=threads)
+        spent += time.perf_counter() - t0
+        layers += 1
+    # full pass = n_layers layers x rows rows; sample = `layers` layers x len(sample_rows) rows
+    pass_s = spent * (w.n_layers / layers) * rows / len(sample_rows)
     return {"value": rows / pass_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"1 layer of {w.name} ({w.n_tokens} keys, {w.n_q_heads} query heads, "
-                      f"{len(sample_rows)} of {rows} rows), {dt:.2f} s measured, scaled x{w.n_layers} layers"
-                      + ("" if len(sample_rows) == rows else f" x{rows / len(sample_rows):.0f} rows")}
+            "sample": f"{layers} of {w.n_layers} layers of {w.name} ({w.n_tokens} keys, {w.n_q_heads} query heads, "
+                      f"{len(sample_rows)} of {rows} rows), {spent:.1f} s measured, scaled to the full pass"}
 
 
 # --------------------------------------------------------------------------- main
@@ -244,17 +270,20 @@ def main():
     wall = time.perf_counter() - t_start
     elapsed_ms = e0.elapsed_time(e1)
     ms_per_step = elapsed_ms / args.steps
-    passes_profiled = args.steps
     if graph is None:
         kernel_timing = "per-launch HIP events on the compute stream during the timed steps"
         split_ms, n_split, merge_ms, n_merge = h.profile_read(reset=True)
         h.profile(0)
+        layer_ms = split_ms + merge_ms
     else:
-        # a resident layer is one kernel launch (the split kernel merges in
-        # its last workgroup), so the HIP events around the timed steps give
-        # the kernel's mean duration (plus the gap between launches)
-        kernel_timing = "HIP events around the timed graph replays on the compute stream / launches"
-        split_ms, n_split, merge_ms, n_merge = elapsed_ms, args.steps * n_layers, 0.0, 0
+        # a resident layer is the split kernel then its merge kernel, back to
+        # back in the graph; HIP events around the timed replays give their
+        # mean per layer (gaps included)
+        kernel_timing = ("HIP events on the compute stream around the timed graph replays, per layer "
+                         "(split kernel + merge kernel)")
+        split_ms, n_split, merge_ms, n_merge = 0.0, 0, 0.0, 0
+        layer_ms = elapsed_ms
+    n_layer_calls = args.steps * n_layers
 
     # ---- figures
     tokens_per_step = rows
@@ -296,23 +325,24 @@ def main():
         c = ceiling["contiguous_gbps"]
         result["roofline"] = {"bound": "host-link", "achieved": result["h2d_gbps"], "peak": c, "unit": "GB/s",
                               "frac": round(result["h2d_gbps"] / c, 4), "traffic": None}
-    if n_split and not streamed:
-        split_mean_ms = split_ms / n_split
-        achieved = kv_bytes_layer * n_layers * passes_profiled / (split_ms / 1e3) / 1e9
+    if not streamed:
+        # the split kernel and its merge read the layer's quantised K/V once
+        achieved = kv_bytes_layer * n_layer_calls / (layer_ms / 1e3) / 1e9
         if kind == "prefill":
-            tflops = flops_layer * n_layers * passes_profiled / (split_ms / 1e3) / 1e12
+            tflops = flops_layer * n_layer_calls / (layer_ms / 1e3) / 1e12
             result["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                                   "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
                                   "traffic": None}
-            result["split_kv_gbps"] = round(achieved, 1)
+            result["kv_gbps_kernels"] = round(achieved, 1)
         else:
             result["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                                  "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None}
-    if n_split:
-        split_mean_ms = split_ms / n_split
-        result["kernel_ms"] = {"split_mean": round(split_mean_ms, 5), "split_launches": n_split,
-                               "merge_mean": round(merge_ms / max(n_merge, 1), 5), "merge_launches": n_merge,
-                               "passes_profiled": passes_profiled, "timing": kernel_timing}
+                                  "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                                  "traffic": measured_traffic(w.name, rows)}
+        result["kernel_ms"] = {"layer_mean": round(layer_ms / n_layer_calls, 5), "timing": kernel_timing}
+        if n_split:
+            result["kernel_ms"].update({"split_mean": round(split_ms / n_split, 5), "split_launches": n_split,
+                                        "merge_mean": round(merge_ms / max(n_merge, 1), 5),
+                                        "merge_launches": n_merge})
     if args.with_copy_kernel:
         a = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device="cuda")
         b = torch.empty_like(a)

@@ -237,22 +237,26 @@ __device__ __forceinline__ void chunk_scores(const RowState (&st)[NT], const uin
                                              float (&s)[NT][8]) {
 #pragma unroll
     for (int tt = 0; tt < 2; tt++) {
+        // all MFMAs of the key tile first, so none waits on the one before
+        floatx4 d[4][NT];
 #pragma unroll
         for (int b = 0; b < 4; b++) {
             const uint32_t *w = kq + 8 * tt + 4 * (b >> 1) + 2 * (b & 1);
             const half8 kf = q8_to_half8(w[0], w[1]);
 #pragma unroll
-            for (int t = 0; t < NT; t++) {
-                const floatx4 d =
-                    __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, st[t].qf[b], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-#pragma unroll
-                for (int v = 0; v < 4; v++) {
-                    // fma with the binary16 operand read in place (v_fma_mix_f32)
-                    const float dk = half_of(kd + 8 * tt, 4 * v + b);
-                    s[t][4 * tt + v] = __builtin_fmaf(dk, d[v], b == 0 ? 0.0f : s[t][4 * tt + v]);
-                }
-            }
+            for (int t = 0; t < NT; t++)
+                d[b][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, st[t].qf[b], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
         }
+#pragma unroll
+        for (int t = 0; t < NT; t++)
+#pragma unroll
+            for (int v = 0; v < 4; v++) {
+                // fma with the binary16 operand read in place (v_fma_mix_f32)
+                float acc = half_of(kd + 8 * tt, 4 * v) * d[0][t][v];
+#pragma unroll
+                for (int b = 1; b < 4; b++) acc = __builtin_fmaf(half_of(kd + 8 * tt, 4 * v + b), d[b][t][v], acc);
+                s[t][4 * tt + v] = acc;
+            }
     }
 }
 
