@@ -389,7 +389,9 @@ __global__ __launch_bounds__(64 * kSplitWaves, 1) void split_kernel(const SplitA
         issue_chunk(a, page_base(a, entry), kvh, jj0, lane, ring_lds + stage * kChunkBytes);
     };
 
-    // ---- raw query loads first; their latency overlaps the ring prologue
+    // ---- query loads and the first page entries, one round trip together;
+    // the queries are converted before the ring prologue, so no wait on them
+    // (the compiler's vmcnt counts only its own loads) covers the ring loads
     RowState st[NT];
     float4 qraw[NT][8];
 #pragma unroll
@@ -414,15 +416,9 @@ __global__ __launch_bounds__(64 * kSplitWaves, 1) void split_kernel(const SplitA
             }
         }
     }
-
-    // ---- ring prologue: chunks 0 .. kStages - 2 in flight; page entries
-    // (scalar loads) run one chunk ahead of their use
-    uint32_t entry_next = 0;
-    if (n_local > 0) {
-        issue(0, table_at(a.page_table, chunk_page(0)), 0);
-        if (n_local > 1) issue(1, table_at(a.page_table, chunk_page(1)), 1);
-        if (n_local > kStages - 1) entry_next = table_at(a.page_table, chunk_page(kStages - 1));
-    }
+    uint32_t entry0[kStages];
+#pragma unroll
+    for (uint32_t k = 0; k < kStages; k++) entry0[k] = k < n_local ? table_at(a.page_table, chunk_page(k)) : 0u;
 
     // ---- query fragments: lane (row c16, group g) holds dims 32b + 8g .. +8
     // of block b, pre-scaled by softmax_scale * log2(e)
@@ -435,6 +431,19 @@ __global__ __launch_bounds__(64 * kSplitWaves, 1) void split_kernel(const SplitA
                                 (_Float16)(x.w * a.qscale), (_Float16)(y.x * a.qscale), (_Float16)(y.y * a.qscale),
                                 (_Float16)(y.z * a.qscale), (_Float16)(y.w * a.qscale)};
         }
+
+    // the fragments exist before the first ring load is issued
+#pragma unroll
+    for (int t = 0; t < NT; t++)
+#pragma unroll
+        for (int b = 0; b < 4; b++) asm volatile("" ::"v"(st[t].qf[b]) : "memory");
+
+    // ---- ring prologue: chunks 0 .. kStages - 2 in flight; page entries
+    // (scalar loads) run one chunk ahead of their use
+#pragma unroll
+    for (uint32_t k = 0; k < kStages - 1; k++)
+        if (k < n_local) issue(k, entry0[k], k);
+    uint32_t entry_next = entry0[kStages - 1];
 
     if (n_local > 0) {
         uint32_t pv_vq[8];

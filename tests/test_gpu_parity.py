@@ -199,3 +199,75 @@ def test_full_size_decode_sampled_layers():
         say(f"  layer {17 + l}: max-abs err {err:.3e}")
         assert err <= TOL
     h.destroy()
+
+
+def test_full_size_verify_w6():
+    """The all-resident verify workload at full size (163,840 tokens, W = 6,
+    causal tail) with the automatic split plan the benchmark uses; one seeded
+    layer, every output element against the oracle."""
+    w = inputs.WORKLOADS["verify-160k"]
+    W = 6
+    say(f"case full-size {w.name} W={W}: 1 layer")
+    n = w.n_pages
+    h = handle(w.n_q_heads, w.n_kv_heads, n, n, 8)
+    kvl = inputs.draw_layer(w.n_tokens, w.n_kv_heads, 5, w.wid, device="cuda")
+    place(h, 0, kvl, inputs.seeded_permutation(n, 5, w.wid))
+    q = inputs.draw_queries(W, w.n_q_heads, 5, w.wid, device="cuda")
+    got = run(h, 0, q, W, "verify")
+    ref = oracle_out(kvl, q, w.n_q_heads, w.n_kv_heads)
+    err = np.max(np.abs(got - ref))
+    say(f"  max-abs err {err:.3e}")
+    assert err <= TOL
+    h.destroy()
+
+
+def test_full_size_prefill_sampled_rows():
+    """The 256-row prefill chunk over a 123,136-token history at full size;
+    eight seeded rows (first and last included) checked against the oracle,
+    and every output finite."""
+    w = inputs.WORKLOADS["prefill-120k"]
+    R = w.prefill_rows
+    say(f"case full-size {w.name} R={R}: 1 layer, 8 sampled rows")
+    n = w.n_pages
+    h = handle(w.n_q_heads, w.n_kv_heads, n, n, R)
+    kvl = inputs.draw_layer(w.n_tokens, w.n_kv_heads, 3, w.wid, device="cuda")
+    place(h, 0, kvl, inputs.seeded_permutation(n, 3, w.wid))
+    q = inputs.draw_queries(R, w.n_q_heads, 3, w.wid, device="cuda")
+    got = run(h, 0, q, R, "prefill")
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(11)
+    rows = sorted({0, R - 1, *rng.choice(R, 6, replace=False).tolist()})
+    ref = oracle_out(kvl, q, w.n_q_heads, w.n_kv_heads, rows=rows)
+    err = np.max(np.abs(got[rows] - ref))
+    say(f"  rows {rows}: max-abs err {err:.3e}")
+    assert err <= TOL
+    h.destroy()
+
+
+def test_full_size_streamed_layer():
+    """The streamed workload at full size: 262,144 tokens, 410 resident pages,
+    614 streamed from a pinned history through a 64-slot ring (default chunk
+    size), W = 4, two layers called in order; every output element against the
+    oracle reading the same bytes."""
+    w = inputs.WORKLOADS["stream-256k"]
+    W, L = 4, 2
+    say(f"case full-size {w.name} W={W}: {L} layers")
+    n = w.n_pages
+    h = handle(w.n_q_heads, w.n_kv_heads, L * w.n_resident, n, 8, n_ring=w.ring_slots, n_layers=L)
+    pb = kv.page_bytes(h.params)
+    for l in range(L):
+        kvl = inputs.draw_layer(w.n_tokens, w.n_kv_heads, l, w.wid, device="cuda")
+        res = inputs.resident_subset(n, w.n_resident, l, w.wid)
+        table = np.full(n, kv.PT_HOST, dtype=np.uint32)
+        table[res] = l * w.n_resident + np.arange(len(res))
+        host = torch.empty((n, pb), dtype=torch.uint8, pin_memory=True)
+        host.copy_(kvl.pages)
+        place(h, l, kvl, table, history=host)
+        q = inputs.draw_queries(W, w.n_q_heads, l, w.wid, device="cuda")
+        got = run(h, l, q, W, "verify")
+        ref = oracle_out(kvl, q, w.n_q_heads, w.n_kv_heads)
+        err = np.max(np.abs(got - ref))
+        say(f"  layer {l}: max-abs err {err:.3e}")
+        assert err <= TOL
+        del kvl, host
+    h.destroy()
