@@ -241,25 +241,29 @@ SplitArgs base_args(kvattn_t h, uint32_t layer, uint32_t W, const float *q) {
 }
 
 // Split plan of a call on an all-resident layer.  A split is a range of
-// 32-key chunks of one KV head; narrow calls (rows per KV head <= 32) aim at
-// one workgroup per compute unit, wide calls (prefill) at up to 16 splits
-// per 32-row block.  The split count never exceeds the page count, which
-// bounds the partial buffer.
+// 32-key chunks of one KV head.  Narrow calls (rows per KV head <= 32) run
+// the split kernel and aim at one workgroup per compute unit (or honour
+// split_pages); wide calls (prefill chunks) run the wide kernel on 256-row
+// blocks with as many splits as fill the compute units once, at most 16.
+// The split count never exceeds the page count, which bounds the partial
+// buffer.
 struct Plan {
     uint32_t split_chunks, n_splits, n_row_blocks;
-    int nrt;
+    int nrt;    // split kernel: 16-row tiles per workgroup
+    bool wide;  // wide kernel
 };
 
-Plan plan_resident(const kvattn_params &p, uint32_t n_tokens, uint32_t n_pages, uint32_t W, bool prefill, int n_cus) {
+Plan plan_resident(const kvattn_params &p, uint32_t n_tokens, uint32_t n_pages, uint32_t W, int n_cus) {
     const uint32_t G = p.n_q_heads / p.n_kv_heads;
     const uint32_t rows = W * G;
     const uint32_t n_chunks = (n_tokens + 31) / 32;
     const uint32_t cpp = p.page_tokens / 32;
-    Plan pl;
-    pl.nrt = rows <= 16 ? 1 : 2;
-    pl.n_row_blocks = pl.nrt == 1 ? 1 : (rows + 31) / 32;
     const uint64_t cus = (uint64_t)std::max(n_cus, 1);
-    if (!prefill && rows <= kNarrowRows) {
+    Plan pl;
+    pl.wide = rows > kNarrowRows;
+    if (!pl.wide) {
+        pl.nrt = rows <= 16 ? 1 : 2;
+        pl.n_row_blocks = 1;
         if (p.split_pages) {
             pl.split_chunks = p.split_pages * cpp;
         } else {
@@ -268,8 +272,10 @@ Plan plan_resident(const kvattn_params &p, uint32_t n_tokens, uint32_t n_pages, 
             pl.split_chunks = std::max<uint32_t>((n_chunks + splits - 1) / splits, std::min<uint32_t>(8, n_chunks));
         }
     } else {
-        uint64_t per = (uint64_t)p.n_kv_heads * pl.n_row_blocks;
-        uint32_t splits = (uint32_t)std::min<uint64_t>(kPrefillMaxSplits, std::max<uint64_t>(1, 8 * cus / per));
+        pl.nrt = 2;
+        pl.n_row_blocks = (rows + kvattn_wide_rows() - 1) / kvattn_wide_rows();
+        const uint64_t per = (uint64_t)p.n_kv_heads * pl.n_row_blocks;
+        uint32_t splits = (uint32_t)std::min<uint64_t>(kPrefillMaxSplits, std::max<uint64_t>(1, cus / per));
         splits = std::min(splits, n_pages);
         pl.split_chunks = (n_chunks + splits - 1) / splits;
     }
@@ -306,6 +312,13 @@ int launch_split(kvattn_t h, const SplitArgs &a, uint32_t n_items, uint32_t n_ro
     return KVATTN_OK;
 }
 
+int launch_wide(kvattn_t h, const SplitArgs &a, uint32_t n_splits, uint32_t n_row_blocks) {
+    hipEvent_t e0, e1;
+    prof_slot(h, 0, &e0, &e1);
+    HIP_TRY(h, kvattn_launch_wide(a, n_splits, n_row_blocks, h->compute, e0, e1));
+    return KVATTN_OK;
+}
+
 int run_merge(kvattn_t h, uint32_t W, uint32_t n_splits, float *out) {
     MergeArgs m;
     m.part_o = h->part_o();
@@ -325,15 +338,16 @@ int n_cus_of(int device) {
     return v;
 }
 
-// Attention on a layer without streamed pages.
-int attend_resident(kvattn_t h, uint32_t layer, const float *q, uint32_t W, float *out, bool prefill) {
+// Attention on a layer without streamed pages: partials, then the merge (a
+// separate launch measured cheaper than a device-wide release / counter /
+// acquire handshake at the end of the split kernel).
+int attend_resident(kvattn_t h, uint32_t layer, const float *q, uint32_t W, float *out) {
     const LayerState &L = h->layers[layer];
-    Plan pl = plan_resident(h->p, L.n_tokens, L.n_pages, W, prefill, h->n_cus);
+    Plan pl = plan_resident(h->p, L.n_tokens, L.n_pages, W, h->n_cus);
     SplitArgs a = base_args(h, layer, W, q);
     a.split_chunks = pl.split_chunks;
-    // partials, then the merge: a separate launch is cheaper than a device-
-    // wide release / counter / acquire handshake at the end of the split kernel
-    int rc = launch_split(h, a, pl.n_splits, pl.n_row_blocks, pl.nrt);
+    const int rc = pl.wide ? launch_wide(h, a, pl.n_splits, pl.n_row_blocks)
+                           : launch_split(h, a, pl.n_splits, pl.n_row_blocks, pl.nrt);
     return rc != KVATTN_OK ? rc : run_merge(h, W, pl.n_splits, out);
 }
 
@@ -508,7 +522,7 @@ int attend(kvattn_t h, uint32_t layer, const float *q, uint32_t W, float *out, b
         if (prefill) return fail(h, KVATTN_E_UNSUPPORTED, "prefill chunks need an all-resident layer (layer %u streams %u pages)", layer, L.n_streamed);
         return attend_streamed(h, layer, q, W, out);
     }
-    return attend_resident(h, layer, q, W, out, prefill);
+    return attend_resident(h, layer, q, W, out);
 }
 
 }  // namespace
