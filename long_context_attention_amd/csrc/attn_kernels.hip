@@ -119,9 +119,8 @@ __device__ __forceinline__ const uint8_t *resolve_page(const SplitArgs &a, uint3
 // ---------------------------------------------------------------------------
 constexpr int kChunkBytes = 6656;
 constexpr int kOffV = 4096, kOffKS = 6144, kOffVS = 6400;
-constexpr int kStages = 3;
+constexpr int kStages = 3;  // raw-chunk ring of the wide kernel
 constexpr int kDmaPerChunk = 7;  // 4 K, 2 V, 1 scales
-constexpr int kWaveRingBytes = kStages * kChunkBytes;
 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
@@ -140,12 +139,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// Wait until at most `newer` chunks (issued after the one needed) are in flight.
+// Wait until at most `newer` (< S) chunks issued after the one needed are in
+// flight, for a ring of S stages.
+template <int S>
 __device__ __forceinline__ void wait_chunk(uint32_t newer) {
-    static_assert(kStages == 3, "wait_chunk covers up to two newer chunks");
-    if (newer >= 2)
+    static_assert(S == 2 || S == 3, "rings of two or three stages");
+    if (S == 3 && newer >= 2)
         wait_vmcnt<2 * kDmaPerChunk>();
-    else if (newer == 1)
+    else if (newer >= 1)
         wait_vmcnt<kDmaPerChunk>();
     else
         wait_vmcnt<0>();
@@ -355,11 +356,23 @@ __device__ __forceinline__ void chunk_pv(RowState (&st)[NT], const uint32_t vq[8
 // Each wave streams its chunks through its own LDS ring and overlaps chunk
 // i's Q.K^T with chunk i-1's P.V, whose operands it carries over.
 // ---------------------------------------------------------------------------
-constexpr int kSplitWaves = 8;
-constexpr int kSplitLdsBytes = kSplitWaves * kWaveRingBytes;
+// Shape per row-tile count: one tile (<= 16 rows per KV head) needs few
+// registers, so 12 waves (three per SIMD) with two-stage rings; two tiles
+// need about 250 registers, so 8 waves with three-stage rings.  Both fill
+// 159,744 bytes of LDS.
+template <int NT>
+struct SplitCfg {
+    static constexpr int waves = NT == 1 ? 12 : 8;
+    static constexpr int stages = NT == 1 ? 2 : 3;
+    static constexpr int ring_bytes = stages * kChunkBytes;
+    static constexpr int lds_bytes = waves * ring_bytes;
+};
 
 template <int NT>
-__global__ __launch_bounds__(64 * kSplitWaves, 1) void split_kernel(const SplitArgs a) {
+__global__ __launch_bounds__(64 * SplitCfg<NT>::waves, 1) void split_kernel(const SplitArgs a) {
+    constexpr int kSplitWaves = SplitCfg<NT>::waves;
+    constexpr int kStages = SplitCfg<NT>::stages;
+    constexpr int kWaveRingBytes = SplitCfg<NT>::ring_bytes;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // rings; reused by the combine and merge
 
     const int lane = threadIdx.x & 63;
@@ -466,7 +479,7 @@ __global__ __launch_bounds__(64 * kSplitWaves, 1) void split_kernel(const SplitA
                 issue(k + kStages - 1, entry_next, stage == 0 ? kStages - 1 : stage - 1);
                 if (k + kStages < n_local) entry_next = table_at(a.page_table, chunk_page(k + kStages));
             }
-            wait_chunk(min((uint32_t)(kStages - 1), n_local - 1 - k));
+            wait_chunk<kStages>(min((uint32_t)(kStages - 1), n_local - 1 - k));
             const uint8_t *stg = ring + stage * kChunkBytes;
             const uint32_t c = first + kSplitWaves * k;
             uint32_t kq[16], kd[16], vd[16];
@@ -905,14 +918,21 @@ __device__ __forceinline__ void merge_rows(const float *part_ml, const float *pa
     }
 }
 
-// One 128-thread workgroup per (row, query head) unit.
+// U (row, query head) units per workgroup of 128 U threads: U = 4 while the
+// splits fit 512 per unit in LDS (prefill chunks have thousands of units),
+// else one unit per workgroup for up to 4096 splits.
 constexpr int kMergeMaxSplits = 4096;
+constexpr int kMergeWideUnits = 4, kMergeWideSplits = 512;
 
-__global__ __launch_bounds__(128) void merge_kernel(const MergeArgs a) {
-    __shared__ float2 wl[kMergeMaxSplits];
-    __shared__ float2 row_ml[1];
-    const uint32_t unit = blockIdx.x;
-    merge_rows(a.part_ml, a.part_o, a.out, a.n_splits, a.units, 1, [=](uint32_t) { return unit; }, wl, row_ml);
+template <int U>
+__global__ __launch_bounds__(128 * U) void merge_kernel(const MergeArgs a) {
+    constexpr int kSplits = U == 1 ? kMergeMaxSplits : kMergeWideSplits;
+    __shared__ float2 wl[U * kSplits];
+    __shared__ float2 row_ml[U];
+    const uint32_t unit0 = blockIdx.x * U;
+    const uint32_t nrows = min((uint32_t)U, a.units - unit0);
+    merge_rows(a.part_ml, a.part_o, a.out, a.n_splits, a.units, nrows, [=](uint32_t r) { return unit0 + r; }, wl,
+               row_ml);
 }
 
 // ---------------------------------------------------------------------------
@@ -959,19 +979,18 @@ __global__ void read_page_kernel(const SplitArgs a, uint32_t logical_page, uint8
 // Launchers
 // ---------------------------------------------------------------------------
 size_t kvattn_split_smem_bytes(int rt) {
-    (void)rt;
-    return (size_t)kvattn_dev::kSplitLdsBytes;
+    return rt == 1 ? (size_t)kvattn_dev::SplitCfg<1>::lds_bytes : (size_t)kvattn_dev::SplitCfg<2>::lds_bytes;
 }
 
 uint32_t kvattn_merge_max_splits() { return kvattn_dev::kMergeMaxSplits; }
 
 hipError_t kvattn_split_setup() {
-    const int bytes = (int)kvattn_split_smem_bytes(1);
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kvattn_dev::split_kernel<1>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kvattn_split_smem_bytes(1));
     if (e != hipSuccess) return e;
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(&kvattn_dev::split_kernel<2>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kvattn_dev::split_kernel<2>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kvattn_split_smem_bytes(2));
+    return e;
 }
 
 // rt: row tiles of 16 per workgroup (1 or 2); n_row_blocks blocks of 16 * rt rows.
@@ -980,7 +999,8 @@ hipError_t kvattn_split_setup() {
 hipError_t kvattn_launch_split(const SplitArgs &a, uint32_t n_items, uint32_t n_row_blocks, int rt, hipStream_t s,
                                hipEvent_t ev_start, hipEvent_t ev_stop) {
     (void)hipGetLastError();  // clear a stale error so the check below reports this launch
-    dim3 grid(n_items, a.Hkv, n_row_blocks), block(64 * kvattn_dev::kSplitWaves);
+    dim3 grid(n_items, a.Hkv, n_row_blocks);
+    dim3 block(64 * (rt == 1 ? kvattn_dev::SplitCfg<1>::waves : kvattn_dev::SplitCfg<2>::waves));
     const uint32_t smem = (uint32_t)kvattn_split_smem_bytes(rt);
     if (ev_start) {
         if (rt == 1)
@@ -1016,11 +1036,20 @@ hipError_t kvattn_launch_ring_copy(const RingCopyArgs &a, hipStream_t s) {
 
 hipError_t kvattn_launch_merge(const MergeArgs &a, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
     (void)hipGetLastError();
-    dim3 grid(a.units), block(128);
-    if (ev_start)
-        hipExtLaunchKernelGGL(kvattn_dev::merge_kernel, grid, block, 0, s, ev_start, ev_stop, 0, a);
-    else
-        hipLaunchKernelGGL(kvattn_dev::merge_kernel, grid, block, 0, s, a);
+    if (a.n_splits <= kvattn_dev::kMergeWideSplits) {
+        constexpr int U = kvattn_dev::kMergeWideUnits;
+        dim3 grid((a.units + U - 1) / U), block(128 * U);
+        if (ev_start)
+            hipExtLaunchKernelGGL(kvattn_dev::merge_kernel<U>, grid, block, 0, s, ev_start, ev_stop, 0, a);
+        else
+            hipLaunchKernelGGL(kvattn_dev::merge_kernel<U>, grid, block, 0, s, a);
+    } else {
+        dim3 grid(a.units), block(128);
+        if (ev_start)
+            hipExtLaunchKernelGGL(kvattn_dev::merge_kernel<1>, grid, block, 0, s, ev_start, ev_stop, 0, a);
+        else
+            hipLaunchKernelGGL(kvattn_dev::merge_kernel<1>, grid, block, 0, s, a);
+    }
     return hipGetLastError();
 }
 
