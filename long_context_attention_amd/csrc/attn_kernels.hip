@@ -1,32 +1,33 @@
 // attn_kernels.hip -- gfx950 kernels for paged Q8_0-K / Q4_0-V attention.
 //
-// Two kernels:
-//   kvattn_split_kernel   one workgroup per (split of logical pages, KV head,
-//                         32-row block).  Dequantises Q8_0 / Q4_0 codes in
-//                         registers from 16-byte loads, runs Q.K^T and P.V on
-//                         the matrix cores (v_mfma_f32_16x16x32_f16), keeps an
-//                         online softmax per query row, and writes one
-//                         un-normalised partial (m, l, acc[128]) per split and
-//                         row ("troed's fork of Raymond's adaptive KV
-//                         streaming", section "Keep the stock attention
-//                         order": per-span partials, then one final reduction;
-//                         "Block KV cache streaming ...", maintainer review:
-//                         kernels with a partial-output mode followed by a
-//                         combine).
-//   kvattn_merge_kernel   log-sum-exp merge of the split partials in logical
-//                         split order; splits with l = 0 are skipped (the zero
-//                         guard the review finds missing in the chunk
-//                         normaliser).
+//   split_kernel  calls with up to 32 rows per KV head (decode, verify): one
+//                 workgroup per (split of 32-key chunks, KV head); every wave
+//                 streams its own chunks into an LDS ring with direct-to-LDS
+//                 loads and computes all rows of the block.
+//   wide_kernel   calls with more rows (prefill chunks): one workgroup per
+//                 (split, KV head, 256-row block); each chunk is turned into
+//                 an f16 view of K and V once and shared by all 256 rows.
+//   merge_kernel  log-sum-exp merge of the split partials in split order;
+//                 splits with l = 0 are skipped (the zero guard the review
+//                 finds missing in the chunk normaliser).
+// Both attention kernels write one un-normalised partial (m, l, acc[128]) per
+// split and row ("troed's fork of Raymond's adaptive KV streaming", section
+// "Keep the stock attention order": per-span partials, then one final
+// reduction; "Block KV cache streaming ...", maintainer review: kernels with a
+// partial-output mode followed by a combine).
 //
-// Arithmetic (per KV head, 16 keys x 16 query rows per matrix-core tile):
-//   S^T = K . Q^T    A = K codes (int8 -> f16, exact), one MFMA per 32-dim
-//                    block, so each block's fp32 dot is scaled by its own
-//                    binary16 d_K before the blocks are summed.
-//                    B = Q * softmax_scale * log2(e), rounded to f16.
-//   O^T += V^T . P'^T  A = V codes (n - 8 -> f16, exact), B = P * d_V per
-//                    (row, key, 32-dim block), rounded to f16 once.
-//   Softmax in fp32 with exp2; row max / sum reduced across the four
-//   16-lane groups of a wavefront.
+// Arithmetic (per KV head, 16 keys x 16 query rows per matrix-core tile,
+// v_mfma_f32_16x16x32_f16, fp32 accumulation).  Split kernel:
+//   S^T = K . Q^T     A = K codes (int8 -> exact f16 by a byte permute), one
+//                     MFMA per 32-dim block, each block's fp32 dot scaled by
+//                     its own binary16 d_K before the blocks are summed;
+//                     B = Q * softmax_scale * log2(e), rounded to f16.
+//   O^T += V^T . P'^T A = V codes (n - 8, exact f16), B = P * d_V per (row,
+//                     key, 32-dim block), rounded to f16 once.
+// Wide kernel: K' = c * d_K and V' = (n - 8) * d_V rounded to binary16 once
+// each (the f16 working view), P rounded to f16.
+// Softmax in fp32 with exp2 and a lazily moved per-row reference; row max and
+// sum reduced across the four 16-lane groups of a wavefront.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
