@@ -196,9 +196,21 @@ def cpu_baseline(w, rows, kind, inputs, budget_s=10.0):
         layers += 1
     # full pass = n_layers layers x rows rows; sample = `layers` layers x len(sample_rows) rows
     pass_s = spent * (w.n_layers / layers) * rows / len(sample_rows)
+    # one core: the first sampled row of one layer (the oracle is linear in rows and layers)
+    kvl = inputs.draw_layer(w.n_tokens, w.n_kv_heads, 0, w.wid, device="cuda")
+    pages = kvl.pages.cpu().numpy()
+    q = inputs.draw_queries(rows, w.n_q_heads, 0, w.wid, device="cuda").cpu().numpy()
+    del kvl
+    t0 = time.perf_counter()
+    oracle.attend_paged(np.arange(pages.shape[0], dtype=np.uint32), w.n_tokens, 256, w.n_q_heads, w.n_kv_heads, q,
+                        inputs.scale_for(), pool=pages, rows=sample_rows[:1], n_threads=1)
+    one = time.perf_counter() - t0
+    one_pass_s = one * w.n_layers * rows
     return {"value": rows / pass_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{layers} of {w.n_layers} layers of {w.name} ({w.n_tokens} keys, {w.n_q_heads} query heads, "
-                      f"{len(sample_rows)} of {rows} rows), {spent:.1f} s measured, scaled to the full pass"}
+                      f"{len(sample_rows)} of {rows} rows), {spent:.1f} s measured, scaled to the full pass",
+            "one_core": {"value": rows / one_pass_s, "unit": "tokens/s",
+                         "sample": f"1 row of 1 layer, {one:.2f} s measured, scaled to the full pass"}}
 
 
 # --------------------------------------------------------------------------- main
@@ -285,6 +297,17 @@ def main():
         layer_ms = elapsed_ms
     n_layer_calls = args.steps * n_layers
 
+    # spread: the same K steps again, one event between steps (outside the
+    # timed region above, whose figures stand alone)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    with torch.cuda.stream(stream):
+        marks[0].record(stream)
+        for i in range(args.steps):
+            step()
+            marks[i + 1].record(stream)
+    torch.cuda.synchronize()
+    step_ms = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
+
     # ---- figures
     tokens_per_step = rows
     value = tokens_per_step / (ms_per_step / 1e3)
@@ -313,6 +336,10 @@ def main():
         "kv_gbps": round(kv_gbps, 1),
         "kv_frac_hbm_peak": round(kv_gbps / HBM_PEAK_GBPS, 4),
         "wall_s": round(wall, 3),
+        "step_ms_spread": {"median": round(float(np.median(step_ms)), 4),
+                           "p10": round(float(np.percentile(step_ms, 10)), 4),
+                           "p90": round(float(np.percentile(step_ms, 90)), 4),
+                           "how": "a second run of the same steps with an event between steps"},
     }
     if streamed:
         n_str = w.n_pages - w.n_resident
@@ -338,6 +365,10 @@ def main():
             result["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                                   "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                                   "traffic": measured_traffic(w.name, rows)}
+            # the contraction runs on the matrix cores at every width: its rate
+            tflops = flops_layer * n_layer_calls / (layer_ms / 1e3) / 1e12
+            result["mfma_tflops"] = round(tflops, 2)
+            result["mfma_frac"] = round(tflops / MFMA_F16_PEAK_TFLOPS, 4)
         result["kernel_ms"] = {"layer_mean": round(layer_ms / n_layer_calls, 5), "timing": kernel_timing}
         if n_split:
             result["kernel_ms"].update({"split_mean": round(split_ms / n_split, 5), "split_launches": n_split,

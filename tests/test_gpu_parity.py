@@ -201,22 +201,42 @@ def test_full_size_decode_sampled_layers():
     h.destroy()
 
 
-def test_full_size_verify_w6():
-    """The all-resident verify workload at full size (163,840 tokens, W = 6,
-    causal tail) with the automatic split plan the benchmark uses; one seeded
-    layer, every output element against the oracle."""
+@pytest.mark.parametrize("W,layer", [(6, 5), (1, 6)])
+def test_full_size_verify(W, layer):
+    """The all-resident verify workload at full size (163,840 tokens, causal
+    tail) with the automatic split plan the benchmark uses; two seeded layers
+    (W = 6 and W = 1), every output element against the oracle."""
     w = inputs.WORKLOADS["verify-160k"]
-    W = 6
-    say(f"case full-size {w.name} W={W}: 1 layer")
+    say(f"case full-size {w.name} W={W}: layer {layer}")
     n = w.n_pages
     h = handle(w.n_q_heads, w.n_kv_heads, n, n, 8)
-    kvl = inputs.draw_layer(w.n_tokens, w.n_kv_heads, 5, w.wid, device="cuda")
-    place(h, 0, kvl, inputs.seeded_permutation(n, 5, w.wid))
-    q = inputs.draw_queries(W, w.n_q_heads, 5, w.wid, device="cuda")
+    kvl = inputs.draw_layer(w.n_tokens, w.n_kv_heads, layer, w.wid, device="cuda")
+    place(h, 0, kvl, inputs.seeded_permutation(n, layer, w.wid))
+    q = inputs.draw_queries(W, w.n_q_heads, layer, w.wid, device="cuda")
     got = run(h, 0, q, W, "verify")
     ref = oracle_out(kvl, q, w.n_q_heads, w.n_kv_heads)
     err = np.max(np.abs(got - ref))
     say(f"  max-abs err {err:.3e}")
+    assert err <= TOL
+    h.destroy()
+
+
+def test_wide_verify_w49():
+    """A wide speculative verify (49 rows, an n-gram draft width) over 20,000
+    tokens: 245 rows per KV head run on the wide kernel; every element
+    against the oracle."""
+    N, Hq, Hkv, W = 20000, 40, 8, 49
+    say(f"case wide verify N={N} W={W}")
+    kvl = layer_kv(N, Hkv, wid=80, pad="garbage")
+    q = inputs.draw_queries(W, Hq, 0, 80)
+    n = kvl.pages.shape[0]
+    h = handle(Hq, Hkv, n, n, W)
+    place(h, 0, kvl, perm_table(n, 80))
+    got = run(h, 0, q, W, "verify")
+    ref = oracle_out(kvl, q, Hq, Hkv)
+    err = np.max(np.abs(got - ref))
+    say(f"  max-abs err {err:.3e}")
+    assert np.isfinite(got).all()
     assert err <= TOL
     h.destroy()
 
