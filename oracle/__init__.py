@@ -31,6 +31,7 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 HEAD_DIM = 128
+BLOCK = 32
 HOST_ENTRY = 0xFFFFFFFF
 RING_FLAG = 0x80000000
 
@@ -73,6 +74,14 @@ def _load():
         lib.oracle_split_partials.restype = I
         lib.oracle_merge.argtypes = [P, P, P, I, I, P]
         lib.oracle_merge.restype = I
+        lib.oracle_f32_to_f16.argtypes = [ctypes.c_float]
+        lib.oracle_f32_to_f16.restype = ctypes.c_uint16
+        lib.oracle_quantize_q8_0.argtypes = [P, I, P, P]
+        lib.oracle_quantize_q8_0.restype = None
+        lib.oracle_quantize_q4_0.argtypes = [P, I, P, P]
+        lib.oracle_quantize_q4_0.restype = None
+        lib.oracle_unpack_page.argtypes = [P, I, I, P, P, P, P]
+        lib.oracle_unpack_page.restype = None
         _lib = lib
     return _lib
 
@@ -223,3 +232,46 @@ def merge(m, l, acc):
     if rc != 0:
         raise ValueError("oracle_merge: a unit has no visible key")
     return out
+
+
+def f32_to_f16(x: float) -> int:
+    """binary32 -> binary16 bits, round to nearest even (the oracle's own
+    conversion from the formats' definitions)."""
+    return int(_load().oracle_f32_to_f16(ctypes.c_float(x)))
+
+
+def quantize_q8_0(x):
+    """fp32 [..., 32 k] -> (int8 codes [..., 32 k], binary16 bits [..., k]):
+    d = amax / 127 rounded to binary16, code = round-half-even(x / d) clamped
+    to +-127 (binary32 arithmetic); d = 0 gives codes 0."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    n = x.size // BLOCK
+    codes = np.empty(x.shape, dtype=np.int8)
+    scales = np.empty(x.shape[:-1] + (x.shape[-1] // BLOCK,), dtype=np.uint16)
+    _load().oracle_quantize_q8_0(_ptr(x), n, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def quantize_q4_0(x):
+    """fp32 [..., 32 k] -> (codes 0..15 uint8 [..., 32 k], binary16 bits
+    [..., k]): m = the element of largest magnitude (first on ties), d = m / -8
+    rounded to binary16, code = round-half-even(x / d) + 8 clamped to [0, 15];
+    d = 0 gives codes 8."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    n = x.size // BLOCK
+    codes = np.empty(x.shape, dtype=np.uint8)
+    scales = np.empty(x.shape[:-1] + (x.shape[-1] // BLOCK,), dtype=np.uint16)
+    _load().oracle_quantize_q4_0(_ptr(x), n, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def unpack_page(page, H, T):
+    """Codes and scales of one page in logical order: kc int8 [T][H][128],
+    kd uint16 [T][H][4], vc uint8 [T][H][128] (0..15), vd uint16 [T][H][4]."""
+    page, p = _page_arg(page)
+    kc = np.empty((T, H, HEAD_DIM), dtype=np.int8)
+    vc = np.empty((T, H, HEAD_DIM), dtype=np.uint8)
+    kd = np.empty((T, H, HEAD_DIM // BLOCK), dtype=np.uint16)
+    vd = np.empty((T, H, HEAD_DIM // BLOCK), dtype=np.uint16)
+    _load().oracle_unpack_page(p, H, T, _ptr(kc), _ptr(kd), _ptr(vc), _ptr(vd))
+    return kc, kd, vc, vd

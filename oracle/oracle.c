@@ -1,6 +1,7 @@
 /*
  * oracle.c -- plain, slow fp64 reference for attention over a block-paged
- * KV cache whose keys are Q8_0 and whose values are Q4_0.
+ * KV cache whose keys are Q8_0 and whose values are Q4_0, and the reference
+ * quantiser of the KV writer (binary32 decisions, see its section below).
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
  * CPU-baseline leg of the benchmark may load this file's library.  It shares
@@ -106,16 +107,24 @@ int oracle_v_code(const uint8_t *page, int H, int T, int head, int j, int t) {
     return jj < 16 ? (byte & 0x0F) : (byte >> 4);
 }
 
-double oracle_k_scale(const uint8_t *page, int H, int T, int head, int j, int block) {
+static uint16_t k_scale_bits(const uint8_t *page, int H, int T, int head, int j, int block) {
     size_t off = sec_k_scales(H, T) + (((size_t)head * T + j) * N_BLOCKS + block) * 2;
-    return oracle_f16_to_f64(read_u16(page + off));
+    return read_u16(page + off);
 }
 
-double oracle_v_scale(const uint8_t *page, int H, int T, int head, int j, int block) {
+static uint16_t v_scale_bits(const uint8_t *page, int H, int T, int head, int j, int block) {
     int jj = j % 32;
     size_t off = sec_v_scales(H, T) + (size_t)head * T * N_BLOCKS * 2 + (size_t)(j / 32) * 256 +
                  (size_t)(block * 4 + (jj % 16) / 4) * 16 + (size_t)((jj / 16) * 4 + jj % 4) * 2;
-    return oracle_f16_to_f64(read_u16(page + off));
+    return read_u16(page + off);
+}
+
+double oracle_k_scale(const uint8_t *page, int H, int T, int head, int j, int block) {
+    return oracle_f16_to_f64(k_scale_bits(page, H, T, head, j, block));
+}
+
+double oracle_v_scale(const uint8_t *page, int H, int T, int head, int j, int block) {
+    return oracle_f16_to_f64(v_scale_bits(page, H, T, head, j, block));
 }
 
 /* Dequantised key / value element (exact in fp64). */
@@ -311,4 +320,122 @@ int oracle_merge(const double *m, const double *l, const double *acc, int n_spli
         for (int t = 0; t < HEAD_DIM; t++) out[(size_t)u * HEAD_DIM + t] = o[t] / L;
     }
     return 0;
+}
+
+/* ------------------------------------------------------------------------
+ * KV writer reference: quantise fp32 rows into Q8_0 / Q4_0 blocks.
+ *
+ * The pages name the block types and say the KV writer quantises the new
+ * rows before attention reads them ("troed's fork ...", section "KV data
+ * movement and attention"); they do not spell out the quantiser.  Reading
+ * (the common one for these block types):
+ *   Q8_0: d = amax / 127 rounded to binary16; code = round-half-even(x / d)
+ *         clamped to [-127, 127]; d = 0 gives codes 0.
+ *   Q4_0: m = the element of largest magnitude (first on ties, sign kept);
+ *         d = m / -8 rounded to binary16; code = round-half-even(x / d) + 8
+ *         clamped to [0, 15]; d = 0 gives codes 8.
+ * The code of each element is a decision taken in binary32 arithmetic (the
+ * division x / d and the rounding), so this reference takes it in binary32
+ * too; the scale is the binary32 quotient amax / 127 (or m / -8) rounded to
+ * binary16.
+ * ---------------------------------------------------------------------- */
+
+/* binary32 -> binary16, round to nearest, ties to even, from the two
+ * formats' bit definitions (IEEE 754): 1 + 5 + 10 bits, exponent bias 15,
+ * subnormals of 2^-24 units, overflow to infinity, NaN stays NaN. */
+uint16_t oracle_f32_to_f16(float x) {
+    uint32_t f;
+    memcpy(&f, &x, 4);
+    const uint32_t sign = (f >> 16) & 0x8000u;
+    const uint32_t a = f & 0x7FFFFFFFu;
+    if (a >= 0x7F800000u) return (uint16_t)(sign | (a > 0x7F800000u ? 0x7E00u : 0x7C00u));
+    if (a >= 0x477FF000u) return (uint16_t)(sign | 0x7C00u); /* >= 65520: past the largest finite */
+    if (a >= 0x38800000u) {                                 /* >= 2^-14: a normal binary16 */
+        const uint32_t e = (a >> 23) - 127 + 15;
+        const uint32_t m = a & 0x7FFFFFu;
+        uint32_t h = (e << 10) | (m >> 13);
+        const uint32_t rest = m & 0x1FFFu;
+        if (rest > 0x1000u || (rest == 0x1000u && (h & 1u))) h++; /* a carry moves into the exponent */
+        return (uint16_t)(sign | h);
+    }
+    if (a <= 0x33000000u) return (uint16_t)sign; /* <= 2^-25: rounds to zero (2^-25 is a tie, to even) */
+    /* subnormal binary16: value = M * 2^(E - 150); units of 2^-24 */
+    const uint32_t E = a >> 23;
+    const uint32_t M = (a & 0x7FFFFFu) | 0x800000u;
+    const uint32_t shift = 126 - E; /* 14 .. 24 here */
+    uint32_t q = M >> shift;
+    const uint32_t rem = M & ((1u << shift) - 1u), half = 1u << (shift - 1);
+    if (rem > half || (rem == half && (q & 1u))) q++;
+    return (uint16_t)(sign | q);
+}
+
+static float f16_to_f32_exact(uint16_t h) { return (float)oracle_f16_to_f64(h); }
+
+/* n_blocks blocks of 32 values: codes[32 * n], scales[n] (binary16 bits). */
+void oracle_quantize_q8_0(const float *x, int n_blocks, int8_t *codes, uint16_t *scales) {
+    for (int b = 0; b < n_blocks; b++) {
+        const float *xb = x + (size_t)b * BLOCK;
+        float amax = 0.0f;
+        for (int i = 0; i < BLOCK; i++) {
+            const float v = fabsf(xb[i]);
+            if (v > amax) amax = v;
+        }
+        const uint16_t d16 = oracle_f32_to_f16(amax / 127.0f);
+        const float d = f16_to_f32_exact(d16);
+        scales[b] = d16;
+        for (int i = 0; i < BLOCK; i++) {
+            float c = 0.0f;
+            if (d != 0.0f) {
+                c = rintf(xb[i] / d);
+                if (c > 127.0f) c = 127.0f;
+                if (c < -127.0f) c = -127.0f;
+            }
+            codes[(size_t)b * BLOCK + i] = (int8_t)c;
+        }
+    }
+}
+
+/* codes are the 4-bit values 0..15, one per byte. */
+void oracle_quantize_q4_0(const float *x, int n_blocks, uint8_t *codes, uint16_t *scales) {
+    for (int b = 0; b < n_blocks; b++) {
+        const float *xb = x + (size_t)b * BLOCK;
+        int imax = 0;
+        float amax = fabsf(xb[0]);
+        for (int i = 1; i < BLOCK; i++) {
+            if (fabsf(xb[i]) > amax) {
+                amax = fabsf(xb[i]);
+                imax = i;
+            }
+        }
+        const uint16_t d16 = oracle_f32_to_f16(xb[imax] / -8.0f);
+        const float d = f16_to_f32_exact(d16);
+        scales[b] = d16;
+        for (int i = 0; i < BLOCK; i++) {
+            float c = 8.0f;
+            if (d != 0.0f) {
+                c = rintf(xb[i] / d) + 8.0f;
+                if (c > 15.0f) c = 15.0f;
+                if (c < 0.0f) c = 0.0f;
+            }
+            codes[(size_t)b * BLOCK + i] = (uint8_t)c;
+        }
+    }
+}
+
+/* Every code and scale of one page, in logical order:
+ * kc int8 [T][H][128], kd binary16 [T][H][4], vc 0..15 [T][H][128],
+ * vd binary16 [T][H][4]. */
+void oracle_unpack_page(const uint8_t *page, int H, int T, int8_t *kc, uint16_t *kd, uint8_t *vc, uint16_t *vd) {
+    for (int j = 0; j < T; j++)
+        for (int h = 0; h < H; h++) {
+            const size_t row = (size_t)j * H + h;
+            for (int t = 0; t < HEAD_DIM; t++) {
+                kc[row * HEAD_DIM + t] = (int8_t)oracle_k_code(page, H, T, h, j, t);
+                vc[row * HEAD_DIM + t] = (uint8_t)oracle_v_code(page, H, T, h, j, t);
+            }
+            for (int b = 0; b < N_BLOCKS; b++) {
+                kd[row * N_BLOCKS + b] = k_scale_bits(page, H, T, h, j, b);
+                vd[row * N_BLOCKS + b] = v_scale_bits(page, H, T, h, j, b);
+            }
+        }
 }
