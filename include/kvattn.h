@@ -179,6 +179,37 @@ int kvattn_verify(kvattn_t h, uint32_t layer, const float *d_q, uint32_t W, floa
  */
 int kvattn_prefill_chunk(kvattn_t h, uint32_t layer, const float *d_q, uint32_t R, float *d_out);
 
+/*
+ * KV writer: quantise R new token rows of `layer` into the page cache and
+ * grow the layer's history from n_tokens to n_tokens + R (positions
+ * n_tokens .. n_tokens + R - 1).  The writer runs before attention on every
+ * decode, verify and prefill step and quantises the new rows into the tail
+ * page ("troed's fork ...", section "KV data movement and attention").
+ * d_k, d_v: fp32 [R][n_kv_heads][128], device memory, the new keys and
+ * values in position order.  K becomes Q8_0: d = amax / 127 rounded to
+ * binary16, code = round-half-even(x / d) clamped to [-127, 127], zero scale
+ * gives codes 0.  V becomes Q4_0: m = the element of largest magnitude
+ * (first on ties, sign kept), d = m / -8 rounded to binary16, code =
+ * round-half-even(x / d) + 8 clamped to [0, 15], zero scale gives codes 8.
+ * Every decision is taken in binary32 arithmetic.
+ * new_pages / n_new: the pool pages (ids < 0x80000000, unused by the layer)
+ * for the logical pages the growth adds, ceil((n_tokens + R) / page_tokens)
+ * - ceil(n_tokens / page_tokens) of them (else KVATTN_E_ARG); host memory,
+ * read during the call.  The pages the new rows land in must be resident
+ * (pool pages or caller-placed ring slots): a streamed page there gives
+ * KVATTN_E_UNSUPPORTED.  Other bytes of those pages (earlier rows, padding
+ * past the new end) are left as they are.
+ * h_publish: NULL, or host memory of ceil((n_tokens + R) / page_tokens)
+ * pages in logical order (typically the layer's host history): after the
+ * write, every page the new rows landed in is copied there (device to host
+ * on the compute stream), so a host history stays authoritative.
+ * Asynchronous on the compute stream, except that a call adding pages first
+ * drains both streams to install the grown page table.  On KVATTN_E_HIP the
+ * layer's state is undefined: set it again.
+ */
+int kvattn_append(kvattn_t h, uint32_t layer, const float *d_k, const float *d_v, uint32_t R,
+                  const uint32_t *new_pages, uint32_t n_new, void *h_publish);
+
 /* Block the host until both streams have finished the handle's work. */
 int kvattn_synchronize(kvattn_t h);
 

@@ -46,7 +46,21 @@ struct RingCopyArgs {
     size_t page_bytes;
 };
 
+// KV writer: quantise R new token rows (positions n_old .. n_old + R - 1) of
+// one layer into their pages.  k, v: fp32 [R][Hkv][128].
+struct WriterArgs {
+    uint8_t *pool;
+    uint8_t *ring;
+    const uint32_t *page_table;   // the layer's device entries (resident pages only are written)
+    const float *k, *v;
+    uint32_t n_old, R, T, Hkv;
+    uint32_t ring_base, n_ring_slots;
+    size_t page_bytes;
+    size_t sec_kd, sec_vc, sec_vd;
+};
+
 size_t kvattn_split_smem_bytes(int rt);
+hipError_t kvattn_launch_writer(const WriterArgs &a, hipStream_t s);
 hipError_t kvattn_launch_ring_copy(const RingCopyArgs &a, hipStream_t s);
 hipError_t kvattn_split_setup();
 uint32_t kvattn_merge_max_splits();

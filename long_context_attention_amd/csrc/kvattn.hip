@@ -159,6 +159,7 @@ struct LayerState {
     const uint8_t *history_dev = nullptr;  // device-visible alias when the history is pinned
     std::vector<uint32_t> resident;   // logical pages, ascending
     std::vector<uint32_t> streamed;   // logical pages, ascending (ordinal order)
+    std::vector<uint32_t> table;      // the caller's entries, per logical page
 };
 
 }  // namespace
@@ -638,24 +639,11 @@ int kvattn_upload_pages(kvattn_t h, const void *h_pages, const uint32_t *dst, ui
     return KVATTN_OK;
 }
 
-int kvattn_set_layer(kvattn_t h, uint32_t layer, const uint32_t *page_table, uint32_t n_tokens, const void *h_history) {
-    if (!h) return fail(nullptr, KVATTN_E_ARG, "null handle");
-    if (layer >= h->p.n_layers) return fail(h, KVATTN_E_RANGE, "layer %u out of range (n_layers %u)", layer, h->p.n_layers);
-    PlanCheck chk;
-    uint32_t n_pages = 0;
-    int rc = validate_table(h, h->p, page_table, n_tokens, h_history != nullptr, &chk, &n_pages);
-    if (rc) return rc;
-    // the ring is either caller-placed or scheduler-owned on one handle
-    bool other_ring = false, other_stream = false;
-    for (uint32_t l = 0; l < h->p.n_layers; l++) {
-        if (l == layer || !h->layers[l].set) continue;
-        other_ring |= h->layers[l].uses_ring_slots;
-        other_stream |= h->layers[l].n_streamed > 0;
-    }
-    if ((chk.n_ring && (chk.n_host || other_stream)) || (chk.n_host && other_ring))
-        return fail(h, KVATTN_E_PLAN, "caller-placed ring slots and streamed pages cannot share the ring");
-
-    // drain: copies in flight may read the old history or table
+namespace {
+// Install a validated table: drain both streams (copies in flight may read
+// the old history or table), rebuild the layer's lists and device tables.
+int install_layer(kvattn_t h, uint32_t layer, const uint32_t *page_table, uint32_t n_tokens, uint32_t n_pages,
+                  const void *h_history, const PlanCheck &chk) {
     HIP_TRY(h, hipStreamSynchronize(h->copy));
     HIP_TRY(h, hipStreamSynchronize(h->compute));
 
@@ -663,6 +651,7 @@ int kvattn_set_layer(kvattn_t h, uint32_t layer, const uint32_t *page_table, uin
     L = LayerState();
     L.n_tokens = n_tokens;
     L.n_pages = n_pages;
+    L.table.assign(page_table, page_table + n_pages);
     L.history = static_cast<const uint8_t *>(h_history);
     if (h_history && chk.n_host) {
         // pinned (hipHostMalloc) history: the ring-copy kernel reads it in place
@@ -699,6 +688,91 @@ int kvattn_set_layer(kvattn_t h, uint32_t layer, const uint32_t *page_table, uin
         counts[l] = h->layers[l].set ? h->layers[l].n_streamed : 0;
     }
     if (h->p.n_ring_slots) h->sched.set_layer_counts(counts);
+    return KVATTN_OK;
+}
+}  // namespace
+
+int kvattn_set_layer(kvattn_t h, uint32_t layer, const uint32_t *page_table, uint32_t n_tokens, const void *h_history) {
+    if (!h) return fail(nullptr, KVATTN_E_ARG, "null handle");
+    if (layer >= h->p.n_layers) return fail(h, KVATTN_E_RANGE, "layer %u out of range (n_layers %u)", layer, h->p.n_layers);
+    PlanCheck chk;
+    uint32_t n_pages = 0;
+    int rc = validate_table(h, h->p, page_table, n_tokens, h_history != nullptr, &chk, &n_pages);
+    if (rc) return rc;
+    // the ring is either caller-placed or scheduler-owned on one handle
+    bool other_ring = false, other_stream = false;
+    for (uint32_t l = 0; l < h->p.n_layers; l++) {
+        if (l == layer || !h->layers[l].set) continue;
+        other_ring |= h->layers[l].uses_ring_slots;
+        other_stream |= h->layers[l].n_streamed > 0;
+    }
+    if ((chk.n_ring && (chk.n_host || other_stream)) || (chk.n_host && other_ring))
+        return fail(h, KVATTN_E_PLAN, "caller-placed ring slots and streamed pages cannot share the ring");
+
+    return install_layer(h, layer, page_table, n_tokens, n_pages, h_history, chk);
+}
+
+int kvattn_append(kvattn_t h, uint32_t layer, const float *d_k, const float *d_v, uint32_t R,
+                  const uint32_t *new_pages, uint32_t n_new, void *h_publish) {
+    if (!h) return fail(nullptr, KVATTN_E_ARG, "null handle");
+    if (layer >= h->p.n_layers) return fail(h, KVATTN_E_RANGE, "layer %u out of range (n_layers %u)", layer, h->p.n_layers);
+    LayerState &L = h->layers[layer];
+    if (!L.set) return fail(h, KVATTN_E_STATE, "layer %u has no history (kvattn_set_layer first)", layer);
+    if (!d_k || !d_v || R == 0) return fail(h, KVATTN_E_ARG, "null rows or zero row count");
+    const uint32_t T = h->p.page_tokens;
+    const uint64_t n_after = (uint64_t)L.n_tokens + R;
+    if (n_after > (uint64_t)h->p.max_pages_per_layer * T)
+        return fail(h, KVATTN_E_NOSPACE, "%llu tokens exceed max_pages_per_layer x page_tokens", (unsigned long long)n_after);
+    const uint32_t pages_after = (uint32_t)((n_after + T - 1) / T);
+    const uint32_t need = pages_after - L.n_pages;
+    if (n_new != need) return fail(h, KVATTN_E_ARG, "%u rows need %u new pages, %u given", R, need, n_new);
+    if (need && !new_pages) return fail(h, KVATTN_E_ARG, "null new_pages");
+    for (uint32_t i = 0; i < need; i++)
+        if (new_pages[i] & KVATTN_PT_RING_FLAG) return fail(h, KVATTN_E_ARG, "new page %u must be a pool page", i);
+    std::vector<uint32_t> table(L.table);
+    table.insert(table.end(), new_pages, new_pages + need);
+    const uint32_t P0 = L.n_tokens / T, P1 = (uint32_t)((n_after - 1) / T);
+    for (uint32_t P = P0; P <= P1; P++)
+        if (table[P] == KVATTN_PT_HOST)
+            return fail(h, KVATTN_E_UNSUPPORTED, "logical page %u streams from the host; new rows go to resident pages", P);
+    const uint32_t n_old = L.n_tokens;
+    if (need) {
+        PlanCheck chk;
+        uint32_t n_pages = 0;
+        int rc = validate_table(h, h->p, table.data(), (uint32_t)n_after, L.history != nullptr, &chk, &n_pages);
+        if (rc) return rc;
+        // the new pages enter the device tables before the writer runs
+        rc = install_layer(h, layer, table.data(), (uint32_t)n_after, n_pages, L.history, chk);
+        if (rc) return rc;
+    } else {
+        L.n_tokens = (uint32_t)n_after;
+    }
+    WriterArgs w;
+    w.pool = h->pool;
+    w.ring = h->ring;
+    w.page_table = h->d_table(layer);
+    w.k = d_k;
+    w.v = d_v;
+    w.n_old = n_old;
+    w.R = R;
+    w.T = T;
+    w.Hkv = h->p.n_kv_heads;
+    w.ring_base = 0;
+    w.n_ring_slots = h->p.n_ring_slots;
+    w.page_bytes = h->lay.page_bytes;
+    w.sec_kd = h->lay.sec_kd;
+    w.sec_vc = h->lay.sec_vc;
+    w.sec_vd = h->lay.sec_vd;
+    HIP_TRY(h, kvattn_launch_writer(w, h->compute));
+    if (h_publish) {
+        const size_t pb = h->lay.page_bytes;
+        for (uint32_t P = P0; P <= P1; P++) {
+            const uint32_t e = table[P];
+            const uint8_t *src = (e & KVATTN_PT_RING_FLAG) ? h->ring + (size_t)(e & 0x7FFFFFFFu) * pb : h->pool + (size_t)e * pb;
+            HIP_TRY(h, hipMemcpyAsync(static_cast<uint8_t *>(h_publish) + (size_t)P * pb, src, pb, hipMemcpyDeviceToHost,
+                                      h->compute));
+        }
+    }
     return KVATTN_OK;
 }
 

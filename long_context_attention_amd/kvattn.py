@@ -58,6 +58,7 @@ def make_params(n_layers, n_q_heads, n_kv_heads, n_pool_pages, max_pages_per_lay
 _lib = None
 EXPORTS = ["kvattn_supported", "kvattn_page_bytes", "kvattn_workspace_bytes", "kvattn_create",
            "kvattn_upload_pages", "kvattn_set_layer", "kvattn_decode", "kvattn_verify", "kvattn_prefill_chunk",
+           "kvattn_append",
            "kvattn_synchronize", "kvattn_debug_read_page", "kvattn_validate_page_table", "kvattn_sched_simulate",
            "kvattn_profile", "kvattn_profile_read", "kvattn_destroy",
            "kvattn_last_error", "kvattn_global_error"]
@@ -92,6 +93,8 @@ def lib():
     L.kvattn_verify.restype = I
     L.kvattn_prefill_chunk.argtypes = [P, U, P, U, P]
     L.kvattn_prefill_chunk.restype = I
+    L.kvattn_append.argtypes = [P, U, P, P, U, P, U, P]
+    L.kvattn_append.restype = ctypes.c_int
     L.kvattn_synchronize.argtypes = [P]
     L.kvattn_synchronize.restype = I
     L.kvattn_debug_read_page.argtypes = [P, U, U, P]
@@ -202,6 +205,17 @@ class Handle:
 
     def prefill_chunk(self, layer, q, R, out):
         _check(lib().kvattn_prefill_chunk(self.h, layer, _addr(q), R, _addr(out)), self.h)
+
+    def append(self, layer, k, v, R, new_pages=None, publish=None):
+        """Quantise R new rows (k, v: device fp32 [R][Hkv][128]) into the
+        layer's pages; new_pages: pool ids for the pages the growth adds;
+        publish: host buffer that receives the written pages (or None)."""
+        n = 0 if new_pages is None else len(new_pages)
+        np_ = np.ascontiguousarray(new_pages if new_pages is not None else [], dtype=np.uint32)
+        if publish is not None:
+            self._keep.append(publish)
+        _check(lib().kvattn_append(self.h, layer, _addr(k), _addr(v), R, np_.ctypes.data if n else None, n,
+                                   _addr(publish)), self.h)
 
     def synchronize(self):
         _check(lib().kvattn_synchronize(self.h), self.h)
