@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--with-copy-kernel", action="store_true",
                     help="after timing, run a plain elementwise copy of 256 MiB (read 256 MiB, write 256 MiB) "
                          "three times: the reference dispatch for scaling HBM traffic counters")
+    ap.add_argument("--writer", action="store_true",
+                    help="also time the KV writer: one captured graph of one kvattn_append of the step's rows per "
+                         "layer (decode / verify workloads)")
     ap.add_argument("--h2d-ceiling", action="store_true",
                     help="only measure the host-to-device ceiling (pinned copies) and print it as JSON")
     return ap.parse_args()
@@ -138,6 +141,42 @@ def measured_traffic(workload, rows):
     if rec.get("kernel_source_sha256") != sha:
         return None
     return rec.get("traffic_bytes_per_layer")
+
+
+# --------------------------------------------------------------------------- KV writer
+def time_writer(h, w, rows, n_layers, steps, torch, inputs, stream):
+    """Each layer's history is shortened by two steps' rows, then one pass of
+    kvattn_append (the step's rows, one call per layer) warms up and one is
+    captured; replays of the captured pass rewrite the same positions, the
+    same work as a real step's writer.  Returns microseconds per call."""
+    g = torch.Generator(device="cuda").manual_seed(inputs.derive_seed(inputs.BASE_SEED, w.wid, 0, 99))
+    ks = [torch.randn(rows, w.n_kv_heads, 128, device="cuda", generator=g) for _ in range(n_layers)]
+    vs = [torch.randn(rows, w.n_kv_heads, 128, device="cuda", generator=g) for _ in range(n_layers)]
+    for l in range(n_layers):
+        table = np.asarray(h.layer_table(l), dtype=np.uint32)
+        h.set_layer(l, table, w.n_tokens - 2 * rows)
+    with torch.cuda.stream(stream):
+        for l in range(n_layers):
+            h.append(l, ks[l], vs[l], rows)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for l in range(n_layers):
+            h.append(l, ks[l], vs[l], rows)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        graph.replay()
+        e0.record(stream)
+        for _ in range(steps):
+            graph.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (steps * n_layers)
+    bytes_per_call = rows * w.n_kv_heads * BYTES_PER_TOKEN_HEAD
+    return {"us_per_call": round(us, 3), "rows_per_call": rows,
+            "quantised_bytes_per_call": bytes_per_call,
+            "timing": "HIP events around replays of a captured pass of one append per layer"}
 
 
 # --------------------------------------------------------------------------- host link
@@ -308,6 +347,10 @@ def main():
     torch.cuda.synchronize()
     step_ms = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
 
+    writer = None
+    if args.writer and kind != "prefill" and not streamed:
+        writer = time_writer(h, w, rows, n_layers, args.steps, torch, inputs, stream)
+
     # ---- figures
     tokens_per_step = rows
     value = tokens_per_step / (ms_per_step / 1e3)
@@ -374,6 +417,8 @@ def main():
             result["kernel_ms"].update({"split_mean": round(split_ms / n_split, 5), "split_launches": n_split,
                                         "merge_mean": round(merge_ms / max(n_merge, 1), 5),
                                         "merge_launches": n_merge})
+    if writer is not None:
+        result["writer"] = writer
     if args.with_copy_kernel:
         a = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device="cuda")
         b = torch.empty_like(a)

@@ -919,9 +919,9 @@ __device__ __forceinline__ void merge_rows(const float *part_ml, const float *pa
     }
 }
 
-// U (row, query head) units per workgroup of 128 U threads: U = 4 while the
-// splits fit 512 per unit in LDS (prefill chunks have thousands of units),
-// else one unit per workgroup for up to 4096 splits.
+// U (row, query head) units per workgroup of 128 U threads: U = 4 for calls
+// with thousands of units (prefill chunks) while the splits fit 512 per unit
+// in LDS, else one unit per workgroup for up to 4096 splits.
 constexpr int kMergeMaxSplits = 4096;
 constexpr int kMergeWideUnits = 4, kMergeWideSplits = 512;
 
@@ -1159,7 +1159,9 @@ hipError_t kvattn_launch_ring_copy(const RingCopyArgs &a, hipStream_t s) {
 
 hipError_t kvattn_launch_merge(const MergeArgs &a, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
     (void)hipGetLastError();
-    if (a.n_splits <= kvattn_dev::kMergeWideSplits) {
+    // few units (decode, verify): one per workgroup, the most parallel
+    // latency; thousands (prefill chunks): four per workgroup
+    if (a.units >= 1024 && a.n_splits <= kvattn_dev::kMergeWideSplits) {
         constexpr int U = kvattn_dev::kMergeWideUnits;
         dim3 grid((a.units + U - 1) / U), block(128 * U);
         if (ev_start)

@@ -185,6 +185,7 @@ class Handle:
         _check(rc)
         self.h = h
         self._hist = {}
+        self._tables = {}
 
     # -- marshalling wrappers (same names as the C entry points)
     def upload_pages(self, host_pages, dst):
@@ -196,6 +197,11 @@ class Handle:
         pt = np.ascontiguousarray(page_table, dtype=np.uint32)
         self._hist[layer] = history
         _check(lib().kvattn_set_layer(self.h, layer, pt.ctypes.data, n_tokens, _addr(history)), self.h)
+        self._tables[layer] = pt
+
+    def layer_table(self, layer):
+        """The page table last passed to set_layer for `layer` (host copy)."""
+        return self._tables[layer]
 
     def decode(self, layer, q, out):
         _check(lib().kvattn_decode(self.h, layer, _addr(q), _addr(out)), self.h)
