@@ -127,16 +127,20 @@ def one_pass(h, qs, outs, kind, rows):
 def measured_traffic(workload, rows):
     """HBM bytes per layer call (split + merge kernels) from the committed
     FETCH_SIZE / WRITE_SIZE counter summary of this workload, if it was taken
-    on the current kernel source (else None)."""
+    on the current kernel sources (the record names them and their hash;
+    else None)."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}_w{rows}.txt")
-    src = os.path.join(ROOT, "long_context_attention_amd", "csrc", "attn_kernels.hip")
+    csrc = os.path.join(ROOT, "long_context_attention_amd", "csrc")
     try:
         with open(path) as f:
             rec = json.load(f)
-        with open(src, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
-    except (OSError, ValueError):
+        h = hashlib.sha256()
+        for name in rec.get("kernel_sources", []):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(f.read())
+        sha = h.hexdigest()
+    except (OSError, ValueError, TypeError):
         return None
     if rec.get("kernel_source_sha256") != sha:
         return None

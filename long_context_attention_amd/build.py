@@ -8,8 +8,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvattn.so")
-SOURCES = ["kvattn.hip", "attn_kernels.hip"]
-HEADERS = ["attn_kernels.h", "sched.h"]
+SOURCES = ["kvattn.hip", "split_kernel.hip", "wide_kernel.hip", "writer_kernel.hip", "copy_kernels.hip"]
+HEADERS = ["attn_kernels.h", "kernels_common.h", "sched.h"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

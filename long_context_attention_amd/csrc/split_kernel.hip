@@ -1,0 +1,397 @@
+// split_kernel.hip -- the split-KV kernel for calls with up to 32 rows per KV
+// head (decode, verify) and the log-sum-exp merge of the split partials.
+#include "kernels_common.h"
+
+namespace kvattn_dev {
+
+// ---------------------------------------------------------------------------
+// Split kernel.  A workgroup of 8 waves handles one split (a range of 32-key
+// chunks) of one KV head for a block of 16 * NT query rows; the waves take
+// the split's chunks round robin and each computes every row of the block,
+// so a chunk is loaded and dequantised once per block.  Rows of a KV head
+// are ordered (w, hh): r = w * G + hh, hh < G.
+// Each wave streams its chunks through its own LDS ring and overlaps chunk
+// i's Q.K^T with chunk i-1's P.V, whose operands it carries over.
+// ---------------------------------------------------------------------------
+// Shape per row-tile count: one tile (<= 16 rows per KV head) needs few
+// registers, so 12 waves (three per SIMD) with two-stage rings; two tiles
+// need about 250 registers, so 8 waves with three-stage rings.  Both fill
+// 159,744 bytes of LDS.
+template <int NT>
+struct SplitCfg {
+    static constexpr int waves = NT == 1 ? 12 : 8;
+    static constexpr int stages = NT == 1 ? 2 : 3;
+    static constexpr int ring_bytes = stages * kChunkBytes;
+    static constexpr int lds_bytes = waves * ring_bytes;
+};
+
+template <int NT>
+__global__ __launch_bounds__(64 * SplitCfg<NT>::waves, 1) void split_kernel(const SplitArgs a) {
+    constexpr int kSplitWaves = SplitCfg<NT>::waves;
+    constexpr int kStages = SplitCfg<NT>::stages;
+    constexpr int kWaveRingBytes = SplitCfg<NT>::ring_bytes;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // rings; reused by the combine and merge
+
+    const int lane = threadIdx.x & 63;
+    // wave index, made visibly uniform so chunk bookkeeping stays scalar
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int grp = lane >> 4;  // 16-lane group
+    const int c16 = lane & 15;
+    const uint32_t kvh = blockIdx.y;
+    const uint32_t block_row0 = blockIdx.z * (16 * NT);
+    const uint32_t rows_kv = a.W * a.G;
+    const uint32_t n_chunks_all = (a.n_tokens + 31) >> 5;
+    const uint32_t cpp = a.T >> 5;  // chunks per page
+
+    // ---- split -> chunk range
+    uint32_t split, c_begin, c_end;
+    if (a.page_list) {
+        split = table_at(a.page_list, a.list_offset + blockIdx.x);
+        c_begin = split * cpp;
+        c_end = min(c_begin + cpp, n_chunks_all);
+    } else {
+        split = blockIdx.x;
+        c_begin = blockIdx.x * a.split_chunks;
+        c_end = min(c_begin + a.split_chunks, n_chunks_all);
+    }
+    // chunks whose keys every row sees (keys <= n_tokens - W) need no mask
+    const uint32_t clean_end = (a.n_tokens - a.W + 1) >> 5;
+    // this wave's chunks: first + kSplitWaves * k, k < n_local
+    const uint32_t first = c_begin + wave;
+    const uint32_t n_local = first < c_end ? (c_end - 1 - first) / kSplitWaves + 1 : 0;
+
+    uint8_t *ring = smem + wave * kWaveRingBytes;
+    const uint32_t ring_lds = lds_addr(ring);
+    auto chunk_page = [&](uint32_t k) { return (first + kSplitWaves * k) / cpp; };
+    auto issue = [&](uint32_t k, uint32_t entry, uint32_t stage) {
+        const uint32_t chunk = first + kSplitWaves * k;
+        const uint32_t jj0 = (chunk - (chunk / cpp) * cpp) << 5;
+        issue_chunk(a, page_base(a, entry), kvh, jj0, lane, ring_lds + stage * kChunkBytes);
+    };
+
+    // ---- query loads and the first page entries, one round trip together;
+    // the queries are converted before the ring prologue, so no wait on them
+    // (the compiler's vmcnt counts only its own loads) covers the ring loads
+    RowState st[NT];
+    float4 qraw[NT][8];
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+        st[t].row_pos = -1;
+        st[t].m_ref = kNegInf;
+        st[t].l_run = 0.f;
+#pragma unroll
+        for (int n = 0; n < 8; n++) st[t].acc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 8; i++) qraw[t][i] = float4{0.f, 0.f, 0.f, 0.f};
+        const uint32_t r = block_row0 + 16 * t + c16;
+        if (r < rows_kv) {
+            const uint32_t w = r / a.G, hh = r - w * a.G;
+            const uint32_t h = kvh * a.G + hh;
+            st[t].row_pos = (int)(a.n_tokens - a.W + w);
+            const float4 *qp = reinterpret_cast<const float4 *>(a.q + ((size_t)w * a.Hq + h) * 128 + 8 * grp);
+#pragma unroll
+            for (int b = 0; b < 4; b++) {
+                qraw[t][2 * b] = qp[8 * b];
+                qraw[t][2 * b + 1] = qp[8 * b + 1];
+            }
+        }
+    }
+    uint32_t entry0[kStages];
+#pragma unroll
+    for (uint32_t k = 0; k < kStages; k++) entry0[k] = k < n_local ? table_at(a.page_table, chunk_page(k)) : 0u;
+
+    // ---- query fragments: lane (row c16, group g) holds dims 32b + 8g .. +8
+    // of block b, pre-scaled by softmax_scale * log2(e)
+#pragma unroll
+    for (int t = 0; t < NT; t++)
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+            const float4 x = qraw[t][2 * b], y = qraw[t][2 * b + 1];
+            st[t].qf[b] = half8{(_Float16)(x.x * a.qscale), (_Float16)(x.y * a.qscale), (_Float16)(x.z * a.qscale),
+                                (_Float16)(x.w * a.qscale), (_Float16)(y.x * a.qscale), (_Float16)(y.y * a.qscale),
+                                (_Float16)(y.z * a.qscale), (_Float16)(y.w * a.qscale)};
+        }
+
+    // the fragments exist before the first ring load is issued
+#pragma unroll
+    for (int t = 0; t < NT; t++)
+#pragma unroll
+        for (int b = 0; b < 4; b++) asm volatile("" ::"v"(st[t].qf[b]) : "memory");
+
+    // ---- ring prologue: chunks 0 .. kStages - 2 in flight; page entries
+    // (scalar loads) run one chunk ahead of their use
+#pragma unroll
+    for (uint32_t k = 0; k < kStages - 1; k++)
+        if (k < n_local) issue(k, entry0[k], k);
+    uint32_t entry_next = entry0[kStages - 1];
+
+    if (n_local > 0) {
+        uint32_t pv_vq[8];
+        half8 pv_pf[NT][4];
+        uint32_t stage = 0;
+        for (uint32_t k = 0; k < n_local; k++) {
+            // refill the buffer chunk k - 1 used (its reads are complete)
+            if (k + kStages - 1 < n_local) {
+                wait_lgkmcnt0();
+                issue(k + kStages - 1, entry_next, stage == 0 ? kStages - 1 : stage - 1);
+                if (k + kStages < n_local) entry_next = table_at(a.page_table, chunk_page(k + kStages));
+            }
+            wait_chunk<kStages>(min((uint32_t)(kStages - 1), n_local - 1 - k));
+            const uint8_t *stg = ring + stage * kChunkBytes;
+            const uint32_t c = first + kSplitWaves * k;
+            uint32_t kq[16], kd[16], vd[16];
+            float s[NT][8];
+            read_kcodes(stg, lane, kq);
+            read_kscales(stg, grp, kd);
+            chunk_scores<NT>(st, kq, kd, s);
+            if (c >= clean_end) mask_scores<NT>(st, 32 * c, grp, s);
+            if (k > 0) chunk_pv<NT>(st, pv_vq, pv_pf);
+            if (32 * c + 32 > a.n_tokens) sanitize_vscales(ring + stage * kChunkBytes, lane, a.n_tokens - 32 * c);
+            read_vscales(stg, grp, vd);
+#pragma unroll
+            for (int t = 0; t < NT; t++) chunk_probs(st[t], s[t], vd, pv_pf[t]);
+            read_vcodes(stg, lane, pv_vq);
+            stage = stage == kStages - 1 ? 0 : stage + 1;
+        }
+        chunk_pv<NT>(st, pv_vq, pv_pf);
+    }
+
+    // ---- combine the waves (fixed wave order) and write the partials; the
+    // rings are reused once every wave is done with its own
+    wait_vmcnt<0>();
+    __syncthreads();
+    constexpr int R = 16 * NT;  // rows per block
+    constexpr int OS = 132;     // padded row stride
+    float *sm_m = reinterpret_cast<float *>(smem);
+    float *sm_l = sm_m + kSplitWaves * R;
+    float *sm_o = sm_l + kSplitWaves * R;
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+        float l = st[t].l_run;
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        const int row = 16 * t + c16;
+        if (grp == 0) {
+            sm_m[wave * R + row] = st[t].m_ref;
+            sm_l[wave * R + row] = l;
+        }
+#pragma unroll
+        for (int n = 0; n < 8; n++)
+            *reinterpret_cast<floatx4 *>(&sm_o[(wave * R + row) * OS + 16 * n + 4 * grp]) = st[t].acc[n];
+    }
+    __syncthreads();
+
+    const uint32_t units = a.W * a.Hq;
+    const uint32_t rows_here = min((uint32_t)R, rows_kv - block_row0);
+    for (uint32_t idx = threadIdx.x; idx < rows_here * 128; idx += blockDim.x) {
+        const uint32_t r = idx >> 7, t = idx & 127;
+        float M = kNegInf;
+#pragma unroll
+        for (int w = 0; w < kSplitWaves; w++) M = fmaxf(M, sm_m[w * R + r]);
+        float L = 0.f, A = 0.f;
+        if (M != kNegInf) {
+#pragma unroll
+            for (int w = 0; w < kSplitWaves; w++) {
+                const float mw = sm_m[w * R + r];
+                if (mw == kNegInf) continue;
+                const float f = fast_exp2(mw - M);
+                L += f * sm_l[w * R + r];
+                A += f * sm_o[(w * R + r) * OS + t];
+            }
+        }
+        const uint32_t rk = block_row0 + r;
+        const uint32_t wq = rk / a.G, hh = rk - wq * a.G;
+        const uint32_t unit = wq * a.Hq + kvh * a.G + hh;
+        const size_t pu = (size_t)split * units + unit;
+        a.part_o[pu * 128 + t] = A;
+        if (t == 0) {
+            a.part_ml[pu * 2] = M;
+            a.part_ml[pu * 2 + 1] = L;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Merge
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int k = 32; k >= 1; k >>= 1) x = fmaxf(x, __shfl_xor(x, k));
+    return x;
+}
+
+// Butterfly sum: a + b == b + a, so every lane ends with the same bits.
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int k = 32; k >= 1; k >>= 1) x += __shfl_xor(x, k);
+    return x;
+}
+
+// Block-wide log-sum-exp merge (Flash-Decoding's reduction step) of nrows
+// (row, query head) units over n_splits >= 1 split partials (m, l, acc[128]).
+// For row r (unit unit_of(r)): M = max m_s over splits with l_s > 0,
+// w_s = 2^(m_s - M) (0 for empty splits), L = sum w_s l_s, out[t] =
+// (sum_s w_s acc_s[t]) / L.  One wave per row computes M, w and L (lane j
+// sums splits j, j + 64, ... then a butterfly); dimension t sums splits in
+// order.
+// Latency: each thread issues its first (m, l) and the first 32 splits of
+// its first two dimensions before anything waits, so up to 32 splits and
+// 2 x blockDim dimensions take one memory round trip.
+// wl: LDS for nrows * n_splits float2; row_ml: LDS for nrows float2.
+constexpr int kMergeBatch = 32;
+
+template <class UnitOf>
+__device__ __forceinline__ void merge_rows(const float *part_ml, const float *part_o, float *out, uint32_t n_splits,
+                                           uint32_t units, uint32_t nrows, UnitOf unit_of, float2 *wl,
+                                           float2 *row_ml) {
+    const uint32_t nt = blockDim.x, tid = threadIdx.x;
+    const size_t mls = (size_t)units * 2, pos = (size_t)units * 128;
+    const uint32_t n_ml = nrows * n_splits, n_items = nrows * 128;
+    auto ml_at = [&](uint32_t i) {
+        const uint32_t r = i / n_splits, s = i - r * n_splits;
+        return *reinterpret_cast<const float2 *>(part_ml + s * mls + (size_t)unit_of(r) * 2);
+    };
+    auto po_of = [&](uint32_t i) { return part_o + (size_t)unit_of(i >> 7) * 128 + (i & 127); };
+    // clamped addresses keep every early load unconditional
+    const float2 ml0 = ml_at(min(tid, n_ml - 1));
+    const float *po0 = po_of(min(tid, n_items - 1)), *po1 = po_of(min(tid + nt, n_items - 1));
+    float o0[kMergeBatch], o1[kMergeBatch];
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; k++) {
+        const size_t off = (size_t)min((uint32_t)k, n_splits - 1) * pos;
+        o0[k] = po0[off];
+        o1[k] = po1[off];
+    }
+    if (tid < n_ml) wl[tid] = ml0;
+    for (uint32_t i = tid + nt; i < n_ml; i += nt) wl[i] = ml_at(i);
+    __syncthreads();
+    const uint32_t lane = tid & 63, nw = nt >> 6;
+    for (uint32_t r = __builtin_amdgcn_readfirstlane(tid >> 6); r < nrows; r += nw) {
+        float2 *row = wl + r * n_splits;
+        float M = kNegInf;
+        for (uint32_t s = lane; s < n_splits; s += 64) {
+            const float2 v = row[s];
+            if (v.y > 0.f) M = fmaxf(M, v.x);
+        }
+        M = wave_max(M);
+        float L = 0.f;
+        for (uint32_t s = lane; s < n_splits; s += 64) {
+            const float2 v = row[s];
+            const float w = v.y > 0.f ? fast_exp2(v.x - M) : 0.f;
+            row[s].x = w;
+            L += w * v.y;
+        }
+        L = wave_sum(L);
+        if (lane == 0) row_ml[r] = make_float2(M, L);
+    }
+    __syncthreads();
+    const uint32_t nb0 = min(n_splits, (uint32_t)kMergeBatch);
+    // dimension i: splits [0, 32) from `first`, the rest loaded here
+    auto finish = [&](uint32_t i, const float(&first)[kMergeBatch]) {
+        const uint32_t r = i >> 7;
+        const float2 *row = wl + r * n_splits;
+        const float *po = po_of(i);
+        float A = 0.f;
+#pragma unroll
+        for (int k = 0; k < kMergeBatch; k++)
+            if ((uint32_t)k < nb0) A += row[k].x * first[k];
+        for (uint32_t s0 = kMergeBatch; s0 < n_splits; s0 += kMergeBatch) {
+            float ob[kMergeBatch];
+#pragma unroll
+            for (int k = 0; k < kMergeBatch; k++) ob[k] = po[(size_t)min(s0 + k, n_splits - 1) * pos];
+#pragma unroll
+            for (int k = 0; k < kMergeBatch; k++)
+                if (s0 + k < n_splits) A += row[s0 + k].x * ob[k];
+        }
+        out[(size_t)unit_of(r) * 128 + (i & 127)] = A / row_ml[r].y;
+    };
+    if (tid < n_items) finish(tid, o0);
+    if (tid + nt < n_items) finish(tid + nt, o1);
+    for (uint32_t i = tid + 2 * nt; i < n_items; i += nt) {
+        const float *po = po_of(i);
+        float ob[kMergeBatch];
+#pragma unroll
+        for (int k = 0; k < kMergeBatch; k++) ob[k] = po[(size_t)min((uint32_t)k, n_splits - 1) * pos];
+        finish(i, ob);
+    }
+}
+
+// U (row, query head) units per workgroup of 128 U threads: U = 4 for calls
+// with thousands of units (prefill chunks) while the splits fit 512 per unit
+// in LDS, else one unit per workgroup for up to 4096 splits.
+constexpr int kMergeMaxSplits = 4096;
+constexpr int kMergeWideUnits = 4, kMergeWideSplits = 512;
+
+template <int U>
+__global__ __launch_bounds__(128 * U) void merge_kernel(const MergeArgs a) {
+    constexpr int kSplits = U == 1 ? kMergeMaxSplits : kMergeWideSplits;
+    __shared__ float2 wl[U * kSplits];
+    __shared__ float2 row_ml[U];
+    const uint32_t unit0 = blockIdx.x * U;
+    const uint32_t nrows = min((uint32_t)U, a.units - unit0);
+    merge_rows(a.part_ml, a.part_o, a.out, a.n_splits, a.units, nrows, [=](uint32_t r) { return unit0 + r; }, wl,
+               row_ml);
+}
+
+}  // namespace kvattn_dev
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+size_t kvattn_split_smem_bytes(int rt) {
+    return rt == 1 ? (size_t)kvattn_dev::SplitCfg<1>::lds_bytes : (size_t)kvattn_dev::SplitCfg<2>::lds_bytes;
+}
+
+uint32_t kvattn_merge_max_splits() { return kvattn_dev::kMergeMaxSplits; }
+
+hipError_t kvattn_split_setup() {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kvattn_dev::split_kernel<1>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kvattn_split_smem_bytes(1));
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kvattn_dev::split_kernel<2>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kvattn_split_smem_bytes(2));
+    return e;
+}
+
+// rt: row tiles of 16 per workgroup (1 or 2); n_row_blocks blocks of 16 * rt rows.
+// With events, the launch records them at the dispatch's own start and end
+// (timing without extra stream packets).
+hipError_t kvattn_launch_split(const SplitArgs &a, uint32_t n_items, uint32_t n_row_blocks, int rt, hipStream_t s,
+                               hipEvent_t ev_start, hipEvent_t ev_stop) {
+    (void)hipGetLastError();  // clear a stale error so the check below reports this launch
+    dim3 grid(n_items, a.Hkv, n_row_blocks);
+    dim3 block(64 * (rt == 1 ? kvattn_dev::SplitCfg<1>::waves : kvattn_dev::SplitCfg<2>::waves));
+    const uint32_t smem = (uint32_t)kvattn_split_smem_bytes(rt);
+    if (ev_start) {
+        if (rt == 1)
+            hipExtLaunchKernelGGL(kvattn_dev::split_kernel<1>, grid, block, smem, s, ev_start, ev_stop, 0, a);
+        else
+            hipExtLaunchKernelGGL(kvattn_dev::split_kernel<2>, grid, block, smem, s, ev_start, ev_stop, 0, a);
+    } else if (rt == 1) {
+        hipLaunchKernelGGL(kvattn_dev::split_kernel<1>, grid, block, smem, s, a);
+    } else {
+        hipLaunchKernelGGL(kvattn_dev::split_kernel<2>, grid, block, smem, s, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t kvattn_launch_merge(const MergeArgs &a, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
+    (void)hipGetLastError();
+    // few units (decode, verify): one per workgroup, the most parallel
+    // latency; thousands (prefill chunks): four per workgroup
+    if (a.units >= 1024 && a.n_splits <= kvattn_dev::kMergeWideSplits) {
+        constexpr int U = kvattn_dev::kMergeWideUnits;
+        dim3 grid((a.units + U - 1) / U), block(128 * U);
+        if (ev_start)
+            hipExtLaunchKernelGGL(kvattn_dev::merge_kernel<U>, grid, block, 0, s, ev_start, ev_stop, 0, a);
+        else
+            hipLaunchKernelGGL(kvattn_dev::merge_kernel<U>, grid, block, 0, s, a);
+    } else {
+        dim3 grid(a.units), block(128);
+        if (ev_start)
+            hipExtLaunchKernelGGL(kvattn_dev::merge_kernel<1>, grid, block, 0, s, ev_start, ev_stop, 0, a);
+        else
+            hipLaunchKernelGGL(kvattn_dev::merge_kernel<1>, grid, block, 0, s, a);
+    }
+    return hipGetLastError();
+}

@@ -1,0 +1,282 @@
+// wide_kernel.hip -- the kernel for calls with more than 32 rows per KV head
+// (prefill chunks, wide verify).
+#include "kernels_common.h"
+
+namespace kvattn_dev {
+
+// ---------------------------------------------------------------------------
+// Wide kernel (prefill chunks, and any call with more than 32 rows per KV
+// head).  A workgroup of 8 waves handles one split of one KV head for a block
+// of 256 rows; wave w owns rows 32w .. 32w + 31 (two 16-row tiles) over every
+// chunk of the split, so no combine across waves is needed.
+// Per 32-key chunk the workgroup first turns the staged codes into binary16
+// K' = c * d_K and V' = (n - 8) * d_V once (the f16 working view of the
+// pages' wide-prefill path), shared through LDS by all 256 rows; the matrix
+// cores then run on K' and V' with no per-block scale work in the row loop.
+// Each of K', V' is one rounding from the exact product (relative 2^-11).
+// Pipeline per chunk p (one barrier): wait for raw chunk p + 1, barrier,
+// issue raw chunk p + 3, dequantise p + 1 into the other view buffer,
+// compute p.  Raw chunks land in a 3-stage ring by direct-to-LDS loads, the
+// seven load instructions of a chunk spread over waves 0..6.
+// ---------------------------------------------------------------------------
+constexpr int kWideRows = 256;
+constexpr int kViewBytes = 16384;  // K' [tt][b][lane] x 16 B, then V' [n][lane] x 16 B
+
+// Scores for NT row tiles from the f16 view: S^T = K' Q^T, four blocks
+// accumulated in the MFMA.
+template <int NT>
+__device__ __forceinline__ void view_scores(const RowState (&st)[NT], const uint8_t *view, int lane,
+                                            float (&s)[NT][8]) {
+#pragma unroll
+    for (int tt = 0; tt < 2; tt++) {
+        floatx4 d[NT];
+#pragma unroll
+        for (int t = 0; t < NT; t++) d[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+            const half8 kf = *reinterpret_cast<const half8 *>(view + ((tt * 4 + b) * 64 + lane) * 16);
+#pragma unroll
+            for (int t = 0; t < NT; t++) d[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, st[t].qf[b], d[t], 0, 0, 0);
+        }
+#pragma unroll
+        for (int t = 0; t < NT; t++)
+#pragma unroll
+            for (int v = 0; v < 4; v++) s[t][4 * tt + v] = d[t][v];
+    }
+}
+
+// Softmax step of one chunk for one row tile (lazy reference as in
+// chunk_probs); P rounded to binary16 once.
+__device__ __forceinline__ void view_probs(RowState &st, const float s[8], half8 &pf) {
+    float m = s[0];
+#pragma unroll
+    for (int i = 1; i < 8; i++) m = fmaxf(m, s[i]);
+    if (__any(m > st.m_ref + kRescale)) {
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        const float m_new = fmaxf(st.m_ref, m);
+        const float alpha = (st.m_ref == kNegInf) ? 0.f : fast_exp2(st.m_ref - m_new);
+        st.l_run *= alpha;
+#pragma unroll
+        for (int n = 0; n < 8; n++) st.acc[n] *= alpha;
+        st.m_ref = m_new;
+    }
+    const float mu = (st.m_ref == kNegInf) ? 0.f : st.m_ref;
+    float p[8];
+    float lsum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        p[i] = fast_exp2(s[i] - mu);
+        lsum += p[i];
+    }
+    st.l_run += lsum;
+    pf = half8{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3],
+               (_Float16)p[4], (_Float16)p[5], (_Float16)p[6], (_Float16)p[7]};
+}
+
+template <int NT>
+__device__ __forceinline__ void view_pv(RowState (&st)[NT], const uint8_t *view, int lane, const half8 (&pf)[NT]) {
+#pragma unroll
+    for (int n = 0; n < 8; n++) {
+        const half8 vf = *reinterpret_cast<const half8 *>(view + 8192 + (n * 64 + lane) * 16);
+#pragma unroll
+        for (int t = 0; t < NT; t++) st[t].acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[t], st[t].acc[n], 0, 0, 0);
+    }
+}
+
+__device__ __forceinline__ half8 h8_mul(half8 x, uint4 sc) {
+    const half2v a = bits_h2(sc.x), b = bits_h2(sc.y), c = bits_h2(sc.z), d = bits_h2(sc.w);
+    return half8{x[0] * a.x, x[1] * a.y, x[2] * b.x, x[3] * b.y, x[4] * c.x, x[5] * c.y, x[6] * d.x, x[7] * d.y};
+}
+
+// Dequantise one staged raw chunk into the f16 view.  Threads 0..255: K
+// quarter q = t / 64 of lane l = t mod 64 (key tile q / 2, blocks 2 (q mod 2)
+// and +1); threads 256..511: V dwords 2h, 2h + 1 of lane l (value block h).
+// n_valid < 32 marks the chunk holding the end of the history: V' of keys at
+// or past it is zeroed (their scales are page padding).
+__device__ __forceinline__ void dequant_view(const uint8_t *raw, uint8_t *view, uint32_t n_valid) {
+    const int t = threadIdx.x, l = t & 63;
+    if (t < 256) {
+        const int q = t >> 6, tt = q >> 1, b0 = 2 * (q & 1);
+        const uint4 w = *reinterpret_cast<const uint4 *>(raw + q * 1024 + l * 16);
+        const uint32_t key = 16 * tt + (l & 15);
+        const uint32_t sc = *reinterpret_cast<const uint32_t *>(raw + kOffKS + key * 8 + b0 * 2);
+        const half8 k0 = q8_to_half8(w.x, w.y), k1 = q8_to_half8(w.z, w.w);
+        const _Float16 d0 = bits_h2(sc).x, d1 = bits_h2(sc).y;
+        half8 o0, o1;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            o0[i] = k0[i] * d0;
+            o1[i] = k1[i] * d1;
+        }
+        *reinterpret_cast<half8 *>(view + ((tt * 4 + b0) * 64 + l) * 16) = o0;
+        *reinterpret_cast<half8 *>(view + ((tt * 4 + b0 + 1) * 64 + l) * 16) = o1;
+    } else {
+        const int h = (t - 256) >> 6, g = l >> 4;
+        const uint2 w = *reinterpret_cast<const uint2 *>(raw + kOffV + (h >> 1) * 1024 + l * 16 + (h & 1) * 8);
+        const uint4 sc = *reinterpret_cast<const uint4 *>(raw + kOffVS + (h * 4 + g) * 16);
+        half8 v0 = h8_mul(q4_to_half8(w.x), sc), v1 = h8_mul(q4_to_half8(w.y), sc);
+        if (n_valid < 32) {
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const uint32_t key = 16 * (j >> 2) + 4 * g + (j & 3);  // key of operand slot j
+                if (key >= n_valid) {
+                    v0[j] = (_Float16)0.f;
+                    v1[j] = (_Float16)0.f;
+                }
+            }
+        }
+        *reinterpret_cast<half8 *>(view + 8192 + ((2 * h) * 64 + l) * 16) = v0;
+        *reinterpret_cast<half8 *>(view + 8192 + ((2 * h + 1) * 64 + l) * 16) = v1;
+    }
+}
+
+__global__ __launch_bounds__(512, 1) void wide_kernel(const SplitArgs a) {
+    constexpr int NT = 2;
+    __shared__ __attribute__((aligned(16))) uint8_t raw_ring[kStages][kChunkBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t views[2][kViewBytes];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int grp = lane >> 4;
+    const int c16 = lane & 15;
+    const uint32_t kvh = blockIdx.y;
+    const uint32_t block_row0 = blockIdx.z * kWideRows;
+    const uint32_t wave_row0 = block_row0 + 32 * wave;
+    const uint32_t rows_kv = a.W * a.G;
+    const uint32_t n_chunks_all = (a.n_tokens + 31) >> 5;
+    const uint32_t cpp = a.T >> 5;
+    const uint32_t split = blockIdx.x;
+    const uint32_t c_begin = split * a.split_chunks;
+    const uint32_t c_end = min(c_begin + a.split_chunks, n_chunks_all);
+    const uint32_t n = c_end - c_begin;  // chunks of this split (>= 1)
+    const uint32_t clean_end = (a.n_tokens - a.W + 1) >> 5;
+    const bool active = wave_row0 < rows_kv;  // wave has rows to compute
+
+    // this wave's share of a chunk's seven direct-to-LDS loads
+    auto issue = [&](uint32_t p) {
+        if (wave >= kDmaPerChunk) return;
+        const uint32_t chunk = c_begin + p;
+        const uint32_t page = chunk / cpp;
+        const uint32_t jj0 = (chunk - page * cpp) << 5;
+        const uint8_t *base = resolve_page(a, page);
+        const size_t kv = (size_t)kvh * a.T + jj0;
+        const uint32_t dst = lds_addr(raw_ring[p % kStages]);
+        if (wave < 4) {
+            dma16(base + kv * 128 + lane * 16 + 1024 * wave, dst + 1024 * wave);
+        } else if (wave < 6) {
+            dma16(base + a.sec_vc + kv * 64 + lane * 16 + 1024 * (wave - 4), dst + kOffV + 1024 * (wave - 4));
+        } else if (lane < 32) {
+            const uint8_t *sp = lane < 16 ? base + a.sec_kd + kv * 8 + lane * 16
+                                          : base + a.sec_vd + (size_t)kvh * a.T * 8 + (size_t)(jj0 >> 5) * 256 + (lane - 16) * 16;
+            dma16(sp, dst + kOffKS);
+        }
+    };
+    auto n_valid_of = [&](uint32_t p) {
+        const uint32_t c = c_begin + p;
+        return 32 * c + 32 > a.n_tokens ? a.n_tokens - 32 * c : 32u;
+    };
+
+    // ---- queries (two 16-row tiles per wave), converted before any ring load
+    RowState st[NT];
+    float4 qraw[NT][8];
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+        st[t].row_pos = -1;
+        st[t].m_ref = kNegInf;
+        st[t].l_run = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; k++) st[t].acc[k] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 8; i++) qraw[t][i] = float4{0.f, 0.f, 0.f, 0.f};
+        const uint32_t r = wave_row0 + 16 * t + c16;
+        if (r < rows_kv) {
+            const uint32_t w = r / a.G, hh = r - w * a.G;
+            const uint32_t h = kvh * a.G + hh;
+            st[t].row_pos = (int)(a.n_tokens - a.W + w);
+            const float4 *qp = reinterpret_cast<const float4 *>(a.q + ((size_t)w * a.Hq + h) * 128 + 8 * grp);
+#pragma unroll
+            for (int b = 0; b < 4; b++) {
+                qraw[t][2 * b] = qp[8 * b];
+                qraw[t][2 * b + 1] = qp[8 * b + 1];
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; t++)
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+            const float4 x = qraw[t][2 * b], y = qraw[t][2 * b + 1];
+            st[t].qf[b] = half8{(_Float16)(x.x * a.qscale), (_Float16)(x.y * a.qscale), (_Float16)(x.z * a.qscale),
+                                (_Float16)(x.w * a.qscale), (_Float16)(y.x * a.qscale), (_Float16)(y.y * a.qscale),
+                                (_Float16)(y.z * a.qscale), (_Float16)(y.w * a.qscale)};
+            asm volatile("" ::"v"(st[t].qf[b]) : "memory");
+        }
+
+    // ---- prologue: raw chunks 0..2 in flight, chunk 0 into view 0
+#pragma unroll
+    for (uint32_t p = 0; p < kStages; p++)
+        if (p < n) issue(p);
+    wait_chunk_wide(min(n - 1, 2u));
+    __syncthreads();
+    dequant_view(raw_ring[0], views[0], n_valid_of(0));
+
+    for (uint32_t p = 0; p < n; p++) {
+        // raw chunk p + 1 landed (every wave waited for its own share)
+        if (p + 1 < n) wait_chunk_wide(min(n - 2 - p, 1u));
+        __syncthreads();
+        if (p + kStages < n) issue(p + kStages);
+        if (p + 1 < n) dequant_view(raw_ring[(p + 1) % kStages], views[(p + 1) & 1], n_valid_of(p + 1));
+        if (active) {
+            const uint8_t *view = views[p & 1];
+            const uint32_t c = c_begin + p;
+            float s[NT][8];
+            half8 pf[NT];
+            view_scores<NT>(st, view, lane, s);
+            if (c >= clean_end) mask_scores<NT>(st, 32 * c, grp, s);
+#pragma unroll
+            for (int t = 0; t < NT; t++) view_probs(st[t], s[t], pf[t]);
+            view_pv<NT>(st, view, lane, pf);
+        }
+    }
+
+    // ---- partials of this wave's rows
+    const uint32_t units = a.W * a.Hq;
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+        float l = st[t].l_run;
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        const uint32_t r = wave_row0 + 16 * t + c16;
+        if (r < rows_kv) {
+            const uint32_t w = r / a.G, hh = r - w * a.G;
+            const uint32_t unit = w * a.Hq + kvh * a.G + hh;
+            const size_t pu = (size_t)split * units + unit;
+#pragma unroll
+            for (int k = 0; k < 8; k++)
+                *reinterpret_cast<floatx4 *>(a.part_o + pu * 128 + 16 * k + 4 * grp) = st[t].acc[k];
+            if (grp == 0) {
+                a.part_ml[pu * 2] = st[t].m_ref;
+                a.part_ml[pu * 2 + 1] = l;
+            }
+        }
+    }
+}
+
+}  // namespace kvattn_dev
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+hipError_t kvattn_launch_wide(const SplitArgs &a, uint32_t n_splits, uint32_t n_row_blocks, hipStream_t s,
+                              hipEvent_t ev_start, hipEvent_t ev_stop) {
+    (void)hipGetLastError();
+    dim3 grid(n_splits, a.Hkv, n_row_blocks), block(512);
+    if (ev_start)
+        hipExtLaunchKernelGGL(kvattn_dev::wide_kernel, grid, block, 0, s, ev_start, ev_stop, 0, a);
+    else
+        hipLaunchKernelGGL(kvattn_dev::wide_kernel, grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+uint32_t kvattn_wide_rows() { return kvattn_dev::kWideRows; }
