@@ -50,11 +50,14 @@ typedef enum kvattn_status {
     KVATTN_E_HIP = -7          /* a HIP runtime call failed; kvattn_last_error names it */
 } kvattn_status;
 
-/* Block formats: 32 values per block, one IEEE binary16 scale d.
- * Q8_0: 32 int8 codes c, value = d * c.  Q4_0: 32 4-bit codes n, value =
- * d * (n - 8).  (The cache types the pages qualify: "troed's fork ...",
- * section "Adaptive KV Streaming for llama.cpp V2": Q8_0 K / Q4_0 V.) */
-enum { KVATTN_TYPE_Q4_0 = 2, KVATTN_TYPE_Q8_0 = 8 };
+/* Cache element types.  Q8_0 and Q4_0: blocks of 32 values with one IEEE
+ * binary16 scale d; Q8_0 holds 32 int8 codes c (value d * c), Q4_0 32 4-bit
+ * codes n (value d * (n - 8)).  F16: plain IEEE binary16 values.  The pages
+ * qualify Q8_0 K / Q4_0 V ("troed's fork ...", section "Adaptive KV Streaming
+ * for llama.cpp V2") and require the same-type pairs beside it ("Required
+ * FlashAttention kernels"): the supported (k_type, v_type) pairs are
+ * (Q8_0, Q4_0), (Q8_0, Q8_0), (Q4_0, Q4_0) and (F16, F16). */
+enum { KVATTN_TYPE_F16 = 1, KVATTN_TYPE_Q4_0 = 2, KVATTN_TYPE_Q8_0 = 8 };
 
 /* Page-table entries (one uint32 per logical page):
  *   id < 0x80000000       resident pool page `id`
@@ -72,21 +75,29 @@ enum { KVATTN_TYPE_Q4_0 = 2, KVATTN_TYPE_Q8_0 = 8 };
  * fork ...", section "KV data movement and attention": 256 positions per
  * page, K and V page sizes follow the quant types).  The code sections are
  * tiled so that each lane of a 64-wide wavefront reads its matrix-core
- * operand with one aligned 16-byte load.
- *   1. K codes, int8, H*T*128 bytes.  Head h starts at h*T*128; 16-token
- *      tiles of 2048 bytes.  In a tile, token j (0..15) and dim t have byte
- *         (t/64)*1024 + (((t%32)/8)*16 + j)*16 + ((t/32)%2)*8 + t%8.
- *   2. K scales, binary16 [H][T][4] (one per 32-dim block).
- *   3. V codes, 4 bits, H*T*64 bytes.  Head h starts at h*T*64; 32-token
- *      tiles of 2048 bytes.  In a tile, token j (0..31) and dim t have byte
- *         (t/64)*1024 + (((j%16)/4)*16 + t%16)*16 + ((t/16)%4)*4 + j%4,
- *      low nibble for j < 16, high nibble for j >= 16.
- *   4. V scales, binary16, H*T*8 bytes.  Head h starts at h*T*8; 32-token
- *      tiles of 256 bytes.  In a tile, token j (0..31) and block b have byte
- *         (b*4 + (j%16)/4)*16 + ((j/16)*4 + j%4)*2.
- * Page size = H*T*208 bytes (425,984 at H = 8, T = 256).  Pool pages, ring
- * slots and host-history pages all use this layout, so a host-to-device copy
- * of a page is a plain memcpy.
+ * operand with aligned 16-byte loads.  Below, j is a token's position in the
+ * page, t a dimension (0..127), jj = j % 32, and a V key slot is
+ * g = (jj % 16) / 4, s = (jj / 16) * 4 + jj % 4.
+ *   1. K codes, H*T*kc bytes (kc = 128 for Q8_0, 64 for Q4_0, 256 for F16).
+ *      Head h starts at h*T*kc; 16-token tiles of 16*kc bytes.  In a tile:
+ *        Q8_0: byte (t/64)*1024 + (((t%32)/8)*16 + j%16)*16 + ((t/32)%2)*8 + t%8.
+ *        Q4_0: byte (((t%32)/8)*16 + j%16)*16 + (t/32)*4 + (t%8)%4, the low
+ *              nibble for t%8 < 4, else the high nibble.
+ *        F16:  bytes (t/32)*1024 + (((t%32)/8)*16 + j%16)*16 + (t%8)*2, +1.
+ *   2. K scales (Q8_0, Q4_0 only), binary16 [H][T][4] (one per 32-dim block).
+ *   3. V codes, H*T*vc bytes (vc = 128 for Q8_0, 64 for Q4_0, 256 for F16).
+ *      Head h starts at h*T*vc; 32-token tiles of 32*vc bytes.  In a tile:
+ *        Q4_0: byte (t/64)*1024 + (g*16 + t%16)*16 + ((t/16)%4)*4 + jj%4,
+ *              the low nibble for jj < 16, else the high nibble.
+ *        Q8_0: byte (t/32)*1024 + (g*16 + t%16)*16 + ((t/16)%2)*8 + s.
+ *        F16:  bytes (t/16)*1024 + (g*16 + t%16)*16 + s*2, +1.
+ *   4. V scales (Q8_0, Q4_0 only), binary16, H*T*8 bytes.  Head h starts at
+ *      h*T*8; 32-token tiles of 256 bytes.  In a tile, token j and block b
+ *      have byte (b*4 + (jj%16)/4)*16 + ((jj/16)*4 + jj%4)*2.
+ * binary16 values are little-endian.  Page size = H*T*(kc + 8 + vc + 8) for
+ * quantised pairs (425,984 at Q8_0/Q4_0, H = 8, T = 256), H*T*512 for F16.
+ * Pool pages, ring slots and host-history pages all use this layout, so a
+ * host-to-device copy of a page is a plain memcpy.
  */
 
 /* Parameters.  Append-only: new fields go at the end, and struct_size (the
@@ -98,8 +109,8 @@ typedef struct kvattn_params {
     uint32_t n_kv_heads;          /* KV heads; query head h reads KV head h / (n_q_heads / n_kv_heads) */
     uint32_t head_dim;            /* must be 128 */
     uint32_t page_tokens;         /* token positions per page; a multiple of 32 (256 in the workloads) */
-    uint32_t k_type;              /* KVATTN_TYPE_Q8_0 */
-    uint32_t v_type;              /* KVATTN_TYPE_Q4_0 */
+    uint32_t k_type;              /* KVATTN_TYPE_*: one of the supported pairs (see above) */
+    uint32_t v_type;
     uint32_t n_pool_pages;        /* pages in the resident pool buffer */
     uint32_t n_ring_slots;        /* pages in the ring buffer (0 = no ring) */
     uint32_t max_pages_per_layer; /* upper bound of ceil(n_tokens / page_tokens) */

@@ -145,46 +145,88 @@ def quantize_q4_0(x: torch.Tensor):
 # --------------------------------------------------------------------------
 # Page packing
 # --------------------------------------------------------------------------
-def page_bytes(n_kv_heads: int, page_tokens: int = PAGE_TOKENS) -> int:
-    return n_kv_heads * page_tokens * (HEAD_DIM + 8 + HEAD_DIM // 2 + 8)
+F16, Q4_0, Q8_0 = 1, 2, 8   # element types
 
 
-def section_offsets(n_kv_heads: int, page_tokens: int = PAGE_TOKENS):
+def code_bytes(t: int) -> int:
+    return {Q8_0: HEAD_DIM, Q4_0: HEAD_DIM // 2, F16: 2 * HEAD_DIM}[t]
+
+
+def scale_bytes(t: int) -> int:
+    return 0 if t == F16 else 8
+
+
+def page_bytes(n_kv_heads: int, page_tokens: int = PAGE_TOKENS, k_type: int = Q8_0, v_type: int = Q4_0) -> int:
+    return n_kv_heads * page_tokens * (code_bytes(k_type) + scale_bytes(k_type) + code_bytes(v_type) +
+                                       scale_bytes(v_type))
+
+
+def section_offsets(n_kv_heads: int, page_tokens: int = PAGE_TOKENS, k_type: int = Q8_0, v_type: int = Q4_0):
     H, T = n_kv_heads, page_tokens
     k_codes = 0
-    k_scales = H * T * HEAD_DIM
-    v_codes = k_scales + H * T * 8
-    v_scales = v_codes + H * T * (HEAD_DIM // 2)
+    k_scales = H * T * code_bytes(k_type)
+    v_codes = k_scales + H * T * scale_bytes(k_type)
+    v_scales = v_codes + H * T * code_bytes(v_type)
     return k_codes, k_scales, v_codes, v_scales
 
 
 _gather_cache = {}
 
 
-def _gather_maps(page_tokens: int, device):
-    """For each byte of one head's K-code / V-code section, the flat index
-    (token * 128 + dim) of the element(s) stored there."""
-    key = (page_tokens, str(device))
+def _code_offsets(role: str, t_: int, page_tokens: int, device):
+    """Byte offset inside one head's code section of every element (token j,
+    dim t), flat index j * 128 + t, and for 4-bit types whether it is the high
+    nibble (placement only: the byte formulas of the page layout)."""
+    key = (role, t_, page_tokens, str(device))
     if key in _gather_cache:
         return _gather_cache[key]
     T = page_tokens
-    off = np.arange(T * HEAD_DIM, dtype=np.int64)
-    tile, o = off // 2048, off % 2048
-    lane = (o % 1024) // 16
-    dim = 64 * (o // 1024) + 32 * ((o % 16) // 8) + 8 * (lane // 16) + o % 8
-    tok = 16 * tile + lane % 16
-    k_src = tok * HEAD_DIM + dim
-
-    off = np.arange(T * HEAD_DIM // 2, dtype=np.int64)
-    tile, o = off // 2048, off % 2048
-    lane = (o % 1024) // 16
-    dim = 64 * (o // 1024) + 16 * ((o % 16) // 4) + lane % 16
-    tok_lo = 32 * tile + 4 * (lane // 16) + o % 4
-    v_lo = tok_lo * HEAD_DIM + dim
-    v_hi = (tok_lo + 16) * HEAD_DIM + dim
-    maps = tuple(torch.from_numpy(a).to(device) for a in (k_src, v_lo, v_hi))
+    j = np.repeat(np.arange(T, dtype=np.int64), HEAD_DIM)
+    t = np.tile(np.arange(HEAD_DIM, dtype=np.int64), T)
+    hi = None
+    if role == "K":
+        lane = ((t % 32) // 8) * 16 + j % 16
+        if t_ == Q8_0:
+            off = (j // 16) * 2048 + (t // 64) * 1024 + lane * 16 + ((t // 32) % 2) * 8 + t % 8
+        elif t_ == Q4_0:
+            off = (j // 16) * 1024 + lane * 16 + (t // 32) * 4 + (t % 8) % 4
+            hi = (t % 8) >= 4
+        else:
+            off = (j // 16) * 4096 + (t // 32) * 1024 + lane * 16 + (t % 8) * 2
+    else:
+        jj = j % 32
+        g, slot = (jj % 16) // 4, (jj // 16) * 4 + jj % 4
+        lane = g * 16 + t % 16
+        if t_ == Q4_0:
+            off = (j // 32) * 2048 + (t // 64) * 1024 + lane * 16 + ((t // 16) % 4) * 4 + jj % 4
+            hi = jj >= 16
+        elif t_ == Q8_0:
+            off = (j // 32) * 4096 + (t // 32) * 1024 + lane * 16 + ((t // 16) % 2) * 8 + slot
+        else:
+            off = (j // 32) * 8192 + (t // 16) * 1024 + lane * 16 + slot * 2
+    maps = (torch.from_numpy(off).to(device), None if hi is None else torch.from_numpy(hi).to(device))
     _gather_cache[key] = maps
     return maps
+
+
+def _pack_codes(codes, role, t_, T):
+    """codes [n_pages][H][T*128] (int8 codes, nibbles 0..15, or binary16 bits
+    as int16) -> section bytes [n_pages][H][T * code_bytes]."""
+    n_pages, H, _ = codes.shape
+    off, hi = _code_offsets(role, t_, T, codes.device)
+    nb = T * code_bytes(t_)
+    out = torch.zeros((n_pages, H, nb), dtype=torch.int32, device=codes.device)
+    c = codes.to(torch.int32)
+    if t_ == Q8_0:
+        out[:, :, off] = c & 0xFF
+    elif t_ == Q4_0:
+        lo_sel, hi_sel = ~hi, hi
+        out[:, :, off[lo_sel]] |= c[:, :, lo_sel] & 0x0F
+        out[:, :, off[hi_sel]] |= (c[:, :, hi_sel] & 0x0F) << 4
+    else:
+        out[:, :, off] = c & 0xFF
+        out[:, :, off + 1] = (c >> 8) & 0xFF
+    return out.to(torch.uint8)
 
 
 def _vscale_map(page_tokens: int, device):
@@ -200,14 +242,16 @@ def _vscale_map(page_tokens: int, device):
     return _gather_cache[key]
 
 
-def pack_pages(kc, kd, vc, vd, page_tokens: int = PAGE_TOKENS, pad: str = "zero", pad_seed: int = 0):
+def pack_pages(kc, kd, vc, vd, page_tokens: int = PAGE_TOKENS, pad: str = "zero", pad_seed: int = 0,
+               k_type: int = Q8_0, v_type: int = Q4_0):
     """Pack logical arrays into pages.
 
-    kc int8 [N][H][128], kd float16 [N][H][4], vc uint8 [N][H][128] (0..15),
-    vd float16 [N][H][4]  ->  uint8 [ceil(N/T)][page_bytes] on kc's device.
-    Token slots beyond N in the last page are filled with zeros
-    (pad="zero") or with seeded random bytes, NaN-able scales included
-    (pad="garbage"), which a correct reader never touches.
+    kc [N][H][128]: int8 codes (Q8_0), uint8 nibbles 0..15 (Q4_0) or float16
+    values (F16); kd float16 [N][H][4] (None for F16); vc, vd likewise for V.
+    Returns uint8 [ceil(N/T)][page_bytes] on kc's device.  Token slots beyond
+    N in the last page are filled with zeros (pad="zero") or with seeded
+    random bytes, NaN-able scales included (pad="garbage"), which a correct
+    reader never touches.
     """
     N, H, D = kc.shape
     assert D == HEAD_DIM and page_tokens % 32 == 0
@@ -216,7 +260,7 @@ def pack_pages(kc, kd, vc, vd, page_tokens: int = PAGE_TOKENS, pad: str = "zero"
     n_pages = -(-N // T)
     padN = n_pages * T
 
-    def padded(a, fill_dtype):
+    def padded(a, kind):
         if padN == N:
             return a
         extra = list(a.shape)
@@ -227,28 +271,30 @@ def pack_pages(kc, kd, vc, vd, page_tokens: int = PAGE_TOKENS, pad: str = "zero"
             nbytes = int(np.prod(extra)) * a.element_size()
             raw = torch.randint(0, 256, (nbytes,), generator=g, dtype=torch.uint8)
             fill = raw.view(a.dtype).reshape(extra).to(dev)
-            if a.dtype == torch.uint8:
-                fill = fill & 0x0F if fill_dtype == "nib" else fill
+            if kind == "nib":
+                fill = fill & 0x0F
         else:
             fill = torch.zeros(extra, dtype=a.dtype, device=dev)
         return torch.cat([a, fill], 0)
 
-    kc_p = padded(kc, "byte").view(torch.uint8).reshape(n_pages, T, H, D).permute(0, 2, 1, 3)
-    vc_p = padded(vc, "nib").reshape(n_pages, T, H, D).permute(0, 2, 1, 3)
-    kd_p = padded(kd, "half").reshape(n_pages, T, H, 4).permute(0, 2, 1, 3)
-    vd_p = padded(vd, "half").reshape(n_pages, T, H, 4).permute(0, 2, 1, 3)
+    def codes_of(c, t_):
+        if t_ == F16:
+            c = c.view(torch.int16)
+        c = padded(c, "nib" if t_ == Q4_0 else "byte")
+        return c.reshape(n_pages, T, H, D).permute(0, 2, 1, 3).reshape(n_pages, H, T * D)
 
-    k_src, v_lo, v_hi = _gather_maps(T, dev)
-    kflat = kc_p.reshape(n_pages, H, T * D)
-    vflat = vc_p.reshape(n_pages, H, T * D)
-    k_bytes = kflat[:, :, k_src]
-    v_bytes = (vflat[:, :, v_lo] & 0x0F) | ((vflat[:, :, v_hi] & 0x0F) << 4)
-    kd_bytes = kd_p.contiguous().view(torch.uint8).reshape(n_pages, H * T * 8)
-    vd_src = _vscale_map(T, dev)
-    vd_flat = vd_p.contiguous().reshape(n_pages, H, T * 4)   # (token, block) flat
-    vd_bytes = vd_flat[:, :, vd_src].contiguous().view(torch.uint8).reshape(n_pages, H * T * 8)
-    pages = torch.cat([k_bytes.reshape(n_pages, -1), kd_bytes, v_bytes.reshape(n_pages, -1), vd_bytes], 1)
-    assert pages.shape[1] == page_bytes(H, T)
+    parts = [_pack_codes(codes_of(kc, k_type), "K", k_type, T).reshape(n_pages, -1)]
+    if k_type != F16:
+        kd_p = padded(kd, "half").reshape(n_pages, T, H, 4).permute(0, 2, 1, 3)
+        parts.append(kd_p.contiguous().view(torch.uint8).reshape(n_pages, H * T * 8))
+    parts.append(_pack_codes(codes_of(vc, v_type), "V", v_type, T).reshape(n_pages, -1))
+    if v_type != F16:
+        vd_p = padded(vd, "half").reshape(n_pages, T, H, 4).permute(0, 2, 1, 3)
+        vd_src = _vscale_map(T, dev)
+        vd_flat = vd_p.contiguous().reshape(n_pages, H, T * 4)   # (token, block) flat
+        parts.append(vd_flat[:, :, vd_src].contiguous().view(torch.uint8).reshape(n_pages, H * T * 8))
+    pages = torch.cat(parts, 1)
+    assert pages.shape[1] == page_bytes(H, T, k_type, v_type)
     return pages.contiguous()
 
 
@@ -257,28 +303,40 @@ def pack_pages(kc, kd, vc, vd, page_tokens: int = PAGE_TOKENS, pad: str = "zero"
 # --------------------------------------------------------------------------
 @dataclass
 class LayerKV:
-    kc: torch.Tensor  # int8 [N][H][128]
-    kd: torch.Tensor  # float16 [N][H][4]
-    vc: torch.Tensor  # uint8 [N][H][128]
-    vd: torch.Tensor  # float16 [N][H][4]
+    kc: torch.Tensor  # [N][H][128]: int8 codes (Q8_0), uint8 nibbles (Q4_0) or float16 values (F16)
+    kd: torch.Tensor  # float16 [N][H][4], None for F16
+    vc: torch.Tensor  # as kc, for V
+    vd: torch.Tensor
     pages: torch.Tensor = field(default=None)  # uint8 [n_pages][page_bytes]
+    k_type: int = Q8_0
+    v_type: int = Q4_0
+
+
+def quantize(x: torch.Tensor, t_: int):
+    """fp32 [..., 128] -> (codes, scales) of element type t_ (F16: the values
+    rounded to binary16, no scales)."""
+    if t_ == Q8_0:
+        return quantize_q8_0(x)
+    if t_ == Q4_0:
+        return quantize_q4_0(x)
+    return x.to(torch.float16), None
 
 
 def draw_layer(n_tokens, n_kv_heads, layer, wid, seed=BASE_SEED, device="cpu", pack=True, pad="zero",
-               page_tokens=PAGE_TOKENS):
+               page_tokens=PAGE_TOKENS, k_type=Q8_0, v_type=Q4_0):
     """N(0,1) keys and values for one layer, quantised (and packed)."""
     gk = generator(seed, wid, layer, T_K, device)
     gv = generator(seed, wid, layer, T_V, device)
     K = torch.randn((n_tokens, n_kv_heads, HEAD_DIM), generator=gk, device=device, dtype=torch.float32)
-    kc, kd = quantize_q8_0(K)
+    kc, kd = quantize(K, k_type)
     del K
     V = torch.randn((n_tokens, n_kv_heads, HEAD_DIM), generator=gv, device=device, dtype=torch.float32)
-    vc, vd = quantize_q4_0(V)
+    vc, vd = quantize(V, v_type)
     del V
-    out = LayerKV(kc, kd, vc, vd)
+    out = LayerKV(kc, kd, vc, vd, k_type=k_type, v_type=v_type)
     if pack:
         out.pages = pack_pages(kc, kd, vc, vd, page_tokens, pad=pad,
-                               pad_seed=derive_seed(seed, wid, layer, T_GARBAGE))
+                               pad_seed=derive_seed(seed, wid, layer, T_GARBAGE), k_type=k_type, v_type=v_type)
     return out
 
 

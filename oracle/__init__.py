@@ -32,6 +32,7 @@ _lib = None
 
 HEAD_DIM = 128
 BLOCK = 32
+F16, Q4_0, Q8_0 = 1, 2, 8   # element types (K, V pairs: (Q8_0, Q4_0), (Q8_0, Q8_0), (Q4_0, Q4_0), (F16, F16))
 HOST_ENTRY = 0xFFFFFFFF
 RING_FLAG = 0x80000000
 
@@ -58,19 +59,23 @@ def _load():
         D = ctypes.c_double
         lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
         lib.oracle_f16_to_f64.restype = D
-        lib.oracle_page_bytes.argtypes = [I, I]
+        lib.oracle_page_bytes.argtypes = [I, I, I, I]
         lib.oracle_page_bytes.restype = Z
+        lib.oracle_pair_supported.argtypes = [I, I]
+        lib.oracle_pair_supported.restype = I
         for name in ("oracle_k_code", "oracle_v_code"):
-            getattr(lib, name).argtypes = [P, I, I, I, I, I]
+            getattr(lib, name).argtypes = [P, I, I, I, I, I, I, I]
             getattr(lib, name).restype = I
         for name in ("oracle_k_scale", "oracle_v_scale", "oracle_k_value", "oracle_v_value"):
-            getattr(lib, name).argtypes = [P, I, I, I, I, I]
+            getattr(lib, name).argtypes = [P, I, I, I, I, I, I, I]
             getattr(lib, name).restype = D
-        lib.oracle_attend_paged.argtypes = [P, Z, P, Z, P, P, I, I, I, I, P, I, D, P, I, P, P, I]
+        lib.oracle_attend_paged.argtypes = [P, Z, P, Z, P, P, I, I, I, I, I, I, P, I, D, P, I, P, P, I]
         lib.oracle_attend_paged.restype = I
+        lib.oracle_attend_values.argtypes = [P, P, I, I, I, P, I, D, P, I, P, P, I]
+        lib.oracle_attend_values.restype = I
         lib.oracle_attend_logical.argtypes = [P, P, P, P, I, I, I, P, I, D, P, I, P, P, I]
         lib.oracle_attend_logical.restype = I
-        lib.oracle_split_partials.argtypes = [P, I, I, I, I, P, I, D, P, I, P, P, P]
+        lib.oracle_split_partials.argtypes = [P, I, I, I, I, I, I, P, I, D, P, I, P, P, P]
         lib.oracle_split_partials.restype = I
         lib.oracle_merge.argtypes = [P, P, P, I, I, P]
         lib.oracle_merge.restype = I
@@ -80,7 +85,7 @@ def _load():
         lib.oracle_quantize_q8_0.restype = None
         lib.oracle_quantize_q4_0.argtypes = [P, I, P, P]
         lib.oracle_quantize_q4_0.restype = None
-        lib.oracle_unpack_page.argtypes = [P, I, I, P, P, P, P]
+        lib.oracle_unpack_page.argtypes = [P, I, I, I, I, P, P, P, P]
         lib.oracle_unpack_page.restype = None
         _lib = lib
     return _lib
@@ -99,8 +104,12 @@ def f16_to_f64(bits: int) -> float:
     return _load().oracle_f16_to_f64(int(bits) & 0xFFFF)
 
 
-def page_bytes(n_kv_heads: int, page_tokens: int) -> int:
-    return int(_load().oracle_page_bytes(n_kv_heads, page_tokens))
+def page_bytes(n_kv_heads: int, page_tokens: int, k_type: int = Q8_0, v_type: int = Q4_0) -> int:
+    return int(_load().oracle_page_bytes(k_type, v_type, n_kv_heads, page_tokens))
+
+
+def pair_supported(k_type: int, v_type: int) -> bool:
+    return bool(_load().oracle_pair_supported(k_type, v_type))
 
 
 def _page_arg(page):
@@ -108,27 +117,27 @@ def _page_arg(page):
     return page, ctypes.c_void_p(page.ctypes.data)
 
 
-def k_code(page, H, T, head, j, t):
+def k_code(page, H, T, head, j, t, k_type=Q8_0, v_type=Q4_0):
     page, p = _page_arg(page)
-    return _load().oracle_k_code(p, H, T, head, j, t)
+    return _load().oracle_k_code(p, k_type, v_type, H, T, head, j, t)
 
 
-def v_code(page, H, T, head, j, t):
+def v_code(page, H, T, head, j, t, k_type=Q8_0, v_type=Q4_0):
     page, p = _page_arg(page)
-    return _load().oracle_v_code(p, H, T, head, j, t)
+    return _load().oracle_v_code(p, k_type, v_type, H, T, head, j, t)
 
 
-def k_scale(page, H, T, head, j, b):
+def k_scale(page, H, T, head, j, b, k_type=Q8_0, v_type=Q4_0):
     page, p = _page_arg(page)
-    return _load().oracle_k_scale(p, H, T, head, j, b)
+    return _load().oracle_k_scale(p, k_type, v_type, H, T, head, j, b)
 
 
-def v_scale(page, H, T, head, j, b):
+def v_scale(page, H, T, head, j, b, k_type=Q8_0, v_type=Q4_0):
     page, p = _page_arg(page)
-    return _load().oracle_v_scale(p, H, T, head, j, b)
+    return _load().oracle_v_scale(p, k_type, v_type, H, T, head, j, b)
 
 
-def decode_page(page, H, T):
+def decode_page(page, H, T, k_type=Q8_0, v_type=Q4_0):
     """All dequantised K-hat and V-hat of one page: two float64 [T][H][128]."""
     page, p = _page_arg(page)
     lib = _load()
@@ -137,13 +146,13 @@ def decode_page(page, H, T):
     for j in range(T):
         for h in range(H):
             for t in range(HEAD_DIM):
-                K[j, h, t] = lib.oracle_k_value(p, H, T, h, j, t)
-                V[j, h, t] = lib.oracle_v_value(p, H, T, h, j, t)
+                K[j, h, t] = lib.oracle_k_value(p, k_type, v_type, H, T, h, j, t)
+                V[j, h, t] = lib.oracle_v_value(p, k_type, v_type, H, T, h, j, t)
     return K, V
 
 
 def attend_paged(page_table, n_tokens, page_tokens, n_q_heads, n_kv_heads, q, scale,
-                 pool=None, ring=None, history=None, rows=None, n_threads=None):
+                 pool=None, ring=None, history=None, rows=None, n_threads=None, k_type=Q8_0, v_type=Q4_0):
     """Exact attention read through a page table.
 
     page_table: uint32 [ceil(N/T)] entries (pool id, RING_FLAG|slot, HOST_ENTRY).
@@ -164,7 +173,8 @@ def attend_paged(page_table, n_tokens, page_tokens, n_q_heads, n_kv_heads, q, sc
     lse = np.empty((n_rows, n_q_heads))
     rc = _load().oracle_attend_paged(
         _ptr(pool), 0 if pool is None else pool.shape[0], _ptr(ring), 0 if ring is None else ring.shape[0],
-        _ptr(history), _ptr(pt), n_tokens, page_tokens, n_q_heads, n_kv_heads, _ptr(q), W, float(scale),
+        _ptr(history), _ptr(pt), n_tokens, page_tokens, k_type, v_type, n_q_heads, n_kv_heads, _ptr(q), W,
+        float(scale),
         _ptr(rows_a), n_rows, _ptr(out), _ptr(lse), _threads(n_threads))
     if rc != 0:
         raise ValueError(f"oracle_attend_paged failed ({rc})")
@@ -196,7 +206,8 @@ def attend_logical(kc, kd, vc, vd, n_q_heads, q, scale, rows=None, n_threads=Non
     return out, lse
 
 
-def split_partials(pages, page_tokens, n_tokens, n_q_heads, n_kv_heads, q, scale, bounds):
+def split_partials(pages, page_tokens, n_tokens, n_q_heads, n_kv_heads, q, scale, bounds, k_type=Q8_0,
+                   v_type=Q4_0):
     """Per-split un-normalised partials (m, l, acc) over logical pages.
 
     pages: uint8 [n_pages][page_bytes] in logical order.  bounds: split key
@@ -212,7 +223,8 @@ def split_partials(pages, page_tokens, n_tokens, n_q_heads, n_kv_heads, q, scale
     m = np.empty((S, W, n_q_heads))
     l = np.empty((S, W, n_q_heads))
     acc = np.empty((S, W, n_q_heads, HEAD_DIM))
-    rc = _load().oracle_split_partials(ctypes.cast(ptrs, ctypes.c_void_p), page_tokens, n_tokens, n_q_heads,
+    rc = _load().oracle_split_partials(ctypes.cast(ptrs, ctypes.c_void_p), page_tokens, k_type, v_type, n_tokens,
+                                       n_q_heads,
                                        n_kv_heads, _ptr(q), W, float(scale), _ptr(b), S, _ptr(m), _ptr(l),
                                        _ptr(acc))
     if rc != 0:
@@ -265,13 +277,32 @@ def quantize_q4_0(x):
     return codes, scales
 
 
-def unpack_page(page, H, T):
-    """Codes and scales of one page in logical order: kc int8 [T][H][128],
-    kd uint16 [T][H][4], vc uint8 [T][H][128] (0..15), vd uint16 [T][H][4]."""
+def unpack_page(page, H, T, k_type=Q8_0, v_type=Q4_0):
+    """Codes and scales of one page in logical order: kcode int32 [T][H][128]
+    (Q8_0 the signed code, Q4_0 the nibble, F16 the binary16 bits), kd uint16
+    [T][H][4], vcode int32 [T][H][128], vd uint16 [T][H][4] (zero for F16)."""
     page, p = _page_arg(page)
-    kc = np.empty((T, H, HEAD_DIM), dtype=np.int8)
-    vc = np.empty((T, H, HEAD_DIM), dtype=np.uint8)
+    kc = np.empty((T, H, HEAD_DIM), dtype=np.int32)
+    vc = np.empty((T, H, HEAD_DIM), dtype=np.int32)
     kd = np.empty((T, H, HEAD_DIM // BLOCK), dtype=np.uint16)
     vd = np.empty((T, H, HEAD_DIM // BLOCK), dtype=np.uint16)
-    _load().oracle_unpack_page(p, H, T, _ptr(kc), _ptr(kd), _ptr(vc), _ptr(vd))
+    _load().oracle_unpack_page(p, k_type, v_type, H, T, _ptr(kc), _ptr(kd), _ptr(vc), _ptr(vd))
     return kc, kd, vc, vd
+
+
+def attend_values(K, V, n_q_heads, q, scale, rows=None, n_threads=None):
+    """Exact attention over plain fp64 keys / values [N][Hkv][128]."""
+    K = np.ascontiguousarray(K, dtype=np.float64)
+    V = np.ascontiguousarray(V, dtype=np.float64)
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    N, H = K.shape[0], K.shape[1]
+    W = q.shape[0]
+    rows_a = None if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
+    n_rows = W if rows_a is None else len(rows_a)
+    out = np.empty((n_rows, n_q_heads, HEAD_DIM))
+    lse = np.empty((n_rows, n_q_heads))
+    rc = _load().oracle_attend_values(_ptr(K), _ptr(V), N, n_q_heads, H, _ptr(q), W, float(scale), _ptr(rows_a),
+                                      n_rows, _ptr(out), _ptr(lse), _threads(n_threads))
+    if rc != 0:
+        raise ValueError(f"oracle_attend_values failed ({rc})")
+    return out, lse

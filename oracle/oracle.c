@@ -28,24 +28,32 @@
  *     rows).
  *   - Grouped-query attention: query head h reads KV head floor(h / G),
  *     G = n_q_heads / n_kv_heads.
+ *   - Element types: Q8_0 (8), Q4_0 (2), F16 (1, plain IEEE binary16, no
+ *     scales).  Supported pairs (K, V): (Q8_0, Q4_0), (Q8_0, Q8_0),
+ *     (Q4_0, Q4_0), (F16, F16).
  *   - Page layout (head_dim 128, T tokens per page, H KV heads), four
- *     sections in this order:
- *       K codes   int8    H * T * 128 bytes
+ *     sections in this order (scales only for the block types):
+ *       K codes   H * T * kc bytes (kc = 128 Q8_0, 64 Q4_0, 256 F16)
  *       K scales  binary16 H * T * 4
- *       V nibbles uint8   H * T * 64 bytes
+ *       V codes   H * T * vc bytes (vc = 128 Q8_0, 64 Q4_0, 256 F16)
  *       V scales  binary16 H * T * 4
  *     K scales are stored [head][token][block].  V scales of head h start at
  *     h*T*8 bytes into their section, in 32-token tiles of 256 bytes; inside
  *     a tile, token j (jj = j%32) and block b sit at
  *         (b*4 + (jj%16)/4)*16 + ((jj/16)*4 + jj%4)*2.
- *     K codes of head h start at
- *     h*T*128; a 16-token tile occupies 2048 bytes; inside it, the byte of
- *     (token j, dim t) is at
- *         (t/64)*1024 + (((t%32)/8)*16 + j%16)*16 + ((t/32)%2)*8 + t%8.
- *     V nibbles of head h start at h*T*64; a 32-token tile occupies 2048
- *     bytes; inside it, for token j (jj = j%32) and dim t the byte is at
- *         (t/64)*1024 + (((jj%16)/4)*16 + t%16)*16 + ((t/16)%4)*4 + jj%4
- *     and the code is the low nibble when jj < 16, else the high nibble.
+ *     K codes of head h start at h*T*kc in 16-token tiles of 16*kc bytes;
+ *     inside a tile, for token j and dim t:
+ *       Q8_0  byte (t/64)*1024 + (((t%32)/8)*16 + j%16)*16 + ((t/32)%2)*8 + t%8
+ *       Q4_0  byte (((t%32)/8)*16 + j%16)*16 + (t/32)*4 + (t%8)%4, the low
+ *             nibble when t%8 < 4, else the high nibble
+ *       F16   bytes at (t/32)*1024 + (((t%32)/8)*16 + j%16)*16 + (t%8)*2
+ *     V codes of head h start at h*T*vc in 32-token tiles of 32*vc bytes;
+ *     with jj = j%32, g = (jj%16)/4 and s = (jj/16)*4 + jj%4:
+ *       Q4_0  byte (t/64)*1024 + (g*16 + t%16)*16 + ((t/16)%4)*4 + jj%4, the
+ *             low nibble when jj < 16, else the high nibble
+ *       Q8_0  byte (t/32)*1024 + (g*16 + t%16)*16 + ((t/16)%2)*8 + s
+ *       F16   bytes at (t/16)*1024 + (g*16 + t%16)*16 + s*2
+ *     binary16 values are little-endian.
  *   - Page-table entry: an id below 0x80000000 names a pool page;
  *     0x80000000|s names ring slot s; 0xFFFFFFFF means "in the host
  *     history", i.e. logical page P is page P of the layer's host copy.
@@ -80,60 +88,101 @@ double oracle_f16_to_f64(uint16_t bits) {
 /* ---------------------------------------------------------------------- */
 /* Page layout reading                                                     */
 /* ---------------------------------------------------------------------- */
-static size_t sec_k_codes(int H, int T) { (void)H; (void)T; return 0; }
-static size_t sec_k_scales(int H, int T) { return (size_t)H * T * HEAD_DIM; }
-static size_t sec_v_codes(int H, int T) { return sec_k_scales(H, T) + (size_t)H * T * N_BLOCKS * 2; }
-static size_t sec_v_scales(int H, int T) { return sec_v_codes(H, T) + (size_t)H * T * (HEAD_DIM / 2); }
+#define T_F16 1
+#define T_Q4_0 2
+#define T_Q8_0 8
 
-size_t oracle_page_bytes(int n_kv_heads, int page_tokens) {
-    return sec_v_scales(n_kv_heads, page_tokens) + (size_t)n_kv_heads * page_tokens * N_BLOCKS * 2;
+static int code_bytes(int type) { return type == T_Q8_0 ? HEAD_DIM : type == T_Q4_0 ? HEAD_DIM / 2 : 2 * HEAD_DIM; }
+static int scale_bytes(int type) { return type == T_F16 ? 0 : N_BLOCKS * 2; }
+
+static size_t sec_k_codes(int kt, int vt, int H, int T) { (void)kt; (void)vt; (void)H; (void)T; return 0; }
+static size_t sec_k_scales(int kt, int vt, int H, int T) { (void)vt; return (size_t)H * T * code_bytes(kt); }
+static size_t sec_v_codes(int kt, int vt, int H, int T) {
+    return sec_k_scales(kt, vt, H, T) + (size_t)H * T * scale_bytes(kt);
+}
+static size_t sec_v_scales(int kt, int vt, int H, int T) {
+    return sec_v_codes(kt, vt, H, T) + (size_t)H * T * code_bytes(vt);
+}
+
+int oracle_pair_supported(int kt, int vt) {
+    return (kt == T_Q8_0 && vt == T_Q4_0) || (kt == T_Q8_0 && vt == T_Q8_0) || (kt == T_Q4_0 && vt == T_Q4_0) ||
+           (kt == T_F16 && vt == T_F16);
+}
+
+size_t oracle_page_bytes(int kt, int vt, int n_kv_heads, int page_tokens) {
+    return sec_v_scales(kt, vt, n_kv_heads, page_tokens) + (size_t)n_kv_heads * page_tokens * scale_bytes(vt);
 }
 
 static uint16_t read_u16(const uint8_t *p) { return (uint16_t)(p[0] | (p[1] << 8)); }
 
-int oracle_k_code(const uint8_t *page, int H, int T, int head, int j, int t) {
-    size_t base = sec_k_codes(H, T) + (size_t)head * T * HEAD_DIM + (size_t)(j / 16) * 2048;
-    size_t off = (size_t)(t / 64) * 1024 + (size_t)(((t % 32) / 8) * 16 + j % 16) * 16 +
-                 (size_t)((t / 32) % 2) * 8 + (size_t)(t % 8);
-    return (int)(int8_t)page[base + off];
+/* The code of (head, token j, dim t): Q8_0 the signed int8, Q4_0 the nibble
+ * n (0..15), F16 the binary16 bits. */
+int oracle_k_code(const uint8_t *page, int kt, int vt, int H, int T, int head, int j, int t) {
+    const int kc = code_bytes(kt);
+    const size_t base = sec_k_codes(kt, vt, H, T) + (size_t)head * T * kc + (size_t)(j / 16) * 16 * kc;
+    const size_t lane = (size_t)(((t % 32) / 8) * 16 + j % 16);
+    if (kt == T_Q8_0) {
+        size_t off = (size_t)(t / 64) * 1024 + lane * 16 + (size_t)((t / 32) % 2) * 8 + (size_t)(t % 8);
+        return (int)(int8_t)page[base + off];
+    }
+    if (kt == T_Q4_0) {
+        uint8_t byte = page[base + lane * 16 + (size_t)(t / 32) * 4 + (size_t)((t % 8) % 4)];
+        return (t % 8) < 4 ? (byte & 0x0F) : (byte >> 4);
+    }
+    return (int)read_u16(page + base + (size_t)(t / 32) * 1024 + lane * 16 + (size_t)(t % 8) * 2);
 }
 
-int oracle_v_code(const uint8_t *page, int H, int T, int head, int j, int t) {
-    int jj = j % 32;
-    size_t base = sec_v_codes(H, T) + (size_t)head * T * (HEAD_DIM / 2) + (size_t)(j / 32) * 2048;
-    size_t off = (size_t)(t / 64) * 1024 + (size_t)(((jj % 16) / 4) * 16 + t % 16) * 16 +
-                 (size_t)((t / 16) % 4) * 4 + (size_t)(jj % 4);
-    uint8_t byte = page[base + off];
-    return jj < 16 ? (byte & 0x0F) : (byte >> 4);
+int oracle_v_code(const uint8_t *page, int kt, int vt, int H, int T, int head, int j, int t) {
+    const int vc = code_bytes(vt);
+    const int jj = j % 32, g = (jj % 16) / 4, slot = (jj / 16) * 4 + jj % 4;
+    const size_t base = sec_v_codes(kt, vt, H, T) + (size_t)head * T * vc + (size_t)(j / 32) * 32 * vc;
+    const size_t lane = (size_t)(g * 16 + t % 16);
+    if (vt == T_Q4_0) {
+        uint8_t byte = page[base + (size_t)(t / 64) * 1024 + lane * 16 + (size_t)((t / 16) % 4) * 4 + (size_t)(jj % 4)];
+        return jj < 16 ? (byte & 0x0F) : (byte >> 4);
+    }
+    if (vt == T_Q8_0) {
+        return (int)(int8_t)page[base + (size_t)(t / 32) * 1024 + lane * 16 + (size_t)((t / 16) % 2) * 8 + (size_t)slot];
+    }
+    return (int)read_u16(page + base + (size_t)(t / 16) * 1024 + lane * 16 + (size_t)slot * 2);
 }
 
-static uint16_t k_scale_bits(const uint8_t *page, int H, int T, int head, int j, int block) {
-    size_t off = sec_k_scales(H, T) + (((size_t)head * T + j) * N_BLOCKS + block) * 2;
+static uint16_t k_scale_bits(const uint8_t *page, int kt, int vt, int H, int T, int head, int j, int block) {
+    size_t off = sec_k_scales(kt, vt, H, T) + (((size_t)head * T + j) * N_BLOCKS + block) * 2;
     return read_u16(page + off);
 }
 
-static uint16_t v_scale_bits(const uint8_t *page, int H, int T, int head, int j, int block) {
+static uint16_t v_scale_bits(const uint8_t *page, int kt, int vt, int H, int T, int head, int j, int block) {
     int jj = j % 32;
-    size_t off = sec_v_scales(H, T) + (size_t)head * T * N_BLOCKS * 2 + (size_t)(j / 32) * 256 +
+    size_t off = sec_v_scales(kt, vt, H, T) + (size_t)head * T * N_BLOCKS * 2 + (size_t)(j / 32) * 256 +
                  (size_t)(block * 4 + (jj % 16) / 4) * 16 + (size_t)((jj / 16) * 4 + jj % 4) * 2;
     return read_u16(page + off);
 }
 
-double oracle_k_scale(const uint8_t *page, int H, int T, int head, int j, int block) {
-    return oracle_f16_to_f64(k_scale_bits(page, H, T, head, j, block));
+double oracle_k_scale(const uint8_t *page, int kt, int vt, int H, int T, int head, int j, int block) {
+    return kt == T_F16 ? 1.0 : oracle_f16_to_f64(k_scale_bits(page, kt, vt, H, T, head, j, block));
 }
 
-double oracle_v_scale(const uint8_t *page, int H, int T, int head, int j, int block) {
-    return oracle_f16_to_f64(v_scale_bits(page, H, T, head, j, block));
+double oracle_v_scale(const uint8_t *page, int kt, int vt, int H, int T, int head, int j, int block) {
+    return vt == T_F16 ? 1.0 : oracle_f16_to_f64(v_scale_bits(page, kt, vt, H, T, head, j, block));
+}
+
+/* Element value of a code of the given type (exact in fp64). */
+static double value_of(int type, double scale, int code) {
+    if (type == T_Q8_0) return scale * (double)code;
+    if (type == T_Q4_0) return scale * (double)(code - 8);
+    return oracle_f16_to_f64((uint16_t)code);
 }
 
 /* Dequantised key / value element (exact in fp64). */
-double oracle_k_value(const uint8_t *page, int H, int T, int head, int j, int t) {
-    return oracle_k_scale(page, H, T, head, j, t / BLOCK) * (double)oracle_k_code(page, H, T, head, j, t);
+double oracle_k_value(const uint8_t *page, int kt, int vt, int H, int T, int head, int j, int t) {
+    return value_of(kt, oracle_k_scale(page, kt, vt, H, T, head, j, t / BLOCK),
+                    oracle_k_code(page, kt, vt, H, T, head, j, t));
 }
 
-double oracle_v_value(const uint8_t *page, int H, int T, int head, int j, int t) {
-    return oracle_v_scale(page, H, T, head, j, t / BLOCK) * (double)(oracle_v_code(page, H, T, head, j, t) - 8);
+double oracle_v_value(const uint8_t *page, int kt, int vt, int H, int T, int head, int j, int t) {
+    return value_of(vt, oracle_v_scale(page, kt, vt, H, T, head, j, t / BLOCK),
+                    oracle_v_code(page, kt, vt, H, T, head, j, t));
 }
 
 /* ---------------------------------------------------------------------- */
@@ -164,15 +213,20 @@ static const uint8_t *resolve(const oracle_store *st, uint32_t entry, size_t log
 /* ---------------------------------------------------------------------- */
 typedef struct {
     /* paged */
-    const uint8_t *const *pages; int H; int T;
-    /* logical (unpaged): [N][H][128] codes, [N][H][4] scales */
+    const uint8_t *const *pages; int H; int T; int kt; int vt;
+    /* logical (unpaged, Q8_0 K / Q4_0 V): [N][H][128] codes, [N][H][4] scales */
     const int8_t *kc; const uint16_t *kd; const uint8_t *vc; const uint16_t *vd;
+    /* plain values: [N][H][128] fp64 (any type, dequantised by the caller) */
+    const double *kv; const double *vv;
 } key_source;
 
 static void k_row(const key_source *src, int g, int j, double *out) {
     if (src->pages) {
         const uint8_t *pg = src->pages[j / src->T];
-        for (int t = 0; t < HEAD_DIM; t++) out[t] = oracle_k_value(pg, src->H, src->T, g, j % src->T, t);
+        for (int t = 0; t < HEAD_DIM; t++)
+            out[t] = oracle_k_value(pg, src->kt, src->vt, src->H, src->T, g, j % src->T, t);
+    } else if (src->kv) {
+        memcpy(out, src->kv + ((size_t)j * src->H + g) * HEAD_DIM, sizeof(double) * HEAD_DIM);
     } else {
         size_t row = ((size_t)j * src->H + g);
         for (int t = 0; t < HEAD_DIM; t++)
@@ -183,7 +237,10 @@ static void k_row(const key_source *src, int g, int j, double *out) {
 static void v_row(const key_source *src, int g, int j, double *out) {
     if (src->pages) {
         const uint8_t *pg = src->pages[j / src->T];
-        for (int t = 0; t < HEAD_DIM; t++) out[t] = oracle_v_value(pg, src->H, src->T, g, j % src->T, t);
+        for (int t = 0; t < HEAD_DIM; t++)
+            out[t] = oracle_v_value(pg, src->kt, src->vt, src->H, src->T, g, j % src->T, t);
+    } else if (src->vv) {
+        memcpy(out, src->vv + ((size_t)j * src->H + g) * HEAD_DIM, sizeof(double) * HEAD_DIM);
     } else {
         size_t row = ((size_t)j * src->H + g);
         for (int t = 0; t < HEAD_DIM; t++)
@@ -253,17 +310,17 @@ static int attend_rows(const key_source *src, int n_tokens, int Hq, int Hkv, con
 /* Attention through a page table.  page_table[P] for P < ceil(N / T). */
 int oracle_attend_paged(const uint8_t *pool, size_t n_pool, const uint8_t *ring, size_t n_ring,
                         const uint8_t *history, const uint32_t *page_table, int n_tokens, int page_tokens,
-                        int Hq, int Hkv, const float *q, int W, double scale, const int *rows, int n_rows,
-                        double *out, double *lse, int n_threads) {
-    if (n_tokens <= 0 || page_tokens <= 0 || page_tokens % 32 != 0) return -1;
-    oracle_store st = {pool, n_pool, ring, n_ring, history, oracle_page_bytes(Hkv, page_tokens)};
+                        int kt, int vt, int Hq, int Hkv, const float *q, int W, double scale, const int *rows,
+                        int n_rows, double *out, double *lse, int n_threads) {
+    if (n_tokens <= 0 || page_tokens <= 0 || page_tokens % 32 != 0 || !oracle_pair_supported(kt, vt)) return -1;
+    oracle_store st = {pool, n_pool, ring, n_ring, history, oracle_page_bytes(kt, vt, Hkv, page_tokens)};
     int n_pages = (n_tokens + page_tokens - 1) / page_tokens;
     const uint8_t **pages = (const uint8_t **)malloc(sizeof(uint8_t *) * (size_t)n_pages);
     for (int p = 0; p < n_pages; p++) {
         pages[p] = resolve(&st, page_table[p], (size_t)p);
         if (!pages[p]) { free(pages); return -2; }
     }
-    key_source src = {pages, Hkv, page_tokens, NULL, NULL, NULL, NULL};
+    key_source src = {pages, Hkv, page_tokens, kt, vt, NULL, NULL, NULL, NULL, NULL, NULL};
     int rc = attend_rows(&src, n_tokens, Hq, Hkv, q, W, scale, rows, n_rows, out, lse, n_threads);
     free(pages);
     return rc;
@@ -273,7 +330,15 @@ int oracle_attend_paged(const uint8_t *pool, size_t n_pool, const uint8_t *ring,
 int oracle_attend_logical(const int8_t *kc, const uint16_t *kd, const uint8_t *vc, const uint16_t *vd,
                           int n_tokens, int Hq, int Hkv, const float *q, int W, double scale, const int *rows,
                           int n_rows, double *out, double *lse, int n_threads) {
-    key_source src = {NULL, Hkv, 0, kc, kd, vc, vd};
+    key_source src = {NULL, Hkv, 0, T_Q8_0, T_Q4_0, kc, kd, vc, vd, NULL, NULL};
+    return attend_rows(&src, n_tokens, Hq, Hkv, q, W, scale, rows, n_rows, out, lse, n_threads);
+}
+
+/* Attention over plain fp64 keys and values [N][Hkv][128] (any element type,
+ * dequantised by the caller). */
+int oracle_attend_values(const double *kv, const double *vv, int n_tokens, int Hq, int Hkv, const float *q, int W,
+                         double scale, const int *rows, int n_rows, double *out, double *lse, int n_threads) {
+    key_source src = {NULL, Hkv, 0, 0, 0, NULL, NULL, NULL, NULL, kv, vv};
     return attend_rows(&src, n_tokens, Hq, Hkv, q, W, scale, rows, n_rows, out, lse, n_threads);
 }
 
@@ -281,12 +346,12 @@ int oracle_attend_logical(const int8_t *kc, const uint16_t *kd, const uint8_t *v
  * (bounds[0] = 0 < ... < bounds[n_splits] >= n_tokens), each split reduced
  * on its own to (m, l, acc).  Layout: m, l [n_splits][W][Hq]; acc
  * [n_splits][W][Hq][128].  Keys beyond a row's position are excluded. */
-int oracle_split_partials(const uint8_t *const *pages, int page_tokens, int n_tokens, int Hq, int Hkv,
-                          const float *q, int W, double scale, const int *bounds, int n_splits,
+int oracle_split_partials(const uint8_t *const *pages, int page_tokens, int kt, int vt, int n_tokens, int Hq,
+                          int Hkv, const float *q, int W, double scale, const int *bounds, int n_splits,
                           double *m, double *l, double *acc) {
-    if (Hkv <= 0 || Hq % Hkv != 0 || W <= 0 || W > n_tokens) return -1;
+    if (Hkv <= 0 || Hq % Hkv != 0 || W <= 0 || W > n_tokens || !oracle_pair_supported(kt, vt)) return -1;
     int G = Hq / Hkv;
-    key_source src = {pages, Hkv, page_tokens, NULL, NULL, NULL, NULL};
+    key_source src = {pages, Hkv, page_tokens, kt, vt, NULL, NULL, NULL, NULL, NULL, NULL};
     for (int s = 0; s < n_splits; s++)
         for (int r = 0; r < W; r++)
             for (int h = 0; h < Hq; h++) {
@@ -422,20 +487,21 @@ void oracle_quantize_q4_0(const float *x, int n_blocks, uint8_t *codes, uint16_t
     }
 }
 
-/* Every code and scale of one page, in logical order:
- * kc int8 [T][H][128], kd binary16 [T][H][4], vc 0..15 [T][H][128],
- * vd binary16 [T][H][4]. */
-void oracle_unpack_page(const uint8_t *page, int H, int T, int8_t *kc, uint16_t *kd, uint8_t *vc, uint16_t *vd) {
+/* Every code and scale of one page, in logical order: kcode, vcode int32
+ * [T][H][128] (Q8_0 the signed code, Q4_0 the nibble, F16 the binary16
+ * bits); kd, vd binary16 [T][H][4] (zero for F16). */
+void oracle_unpack_page(const uint8_t *page, int kt, int vt, int H, int T, int32_t *kcode, uint16_t *kd,
+                        int32_t *vcode, uint16_t *vd) {
     for (int j = 0; j < T; j++)
         for (int h = 0; h < H; h++) {
             const size_t row = (size_t)j * H + h;
             for (int t = 0; t < HEAD_DIM; t++) {
-                kc[row * HEAD_DIM + t] = (int8_t)oracle_k_code(page, H, T, h, j, t);
-                vc[row * HEAD_DIM + t] = (uint8_t)oracle_v_code(page, H, T, h, j, t);
+                kcode[row * HEAD_DIM + t] = oracle_k_code(page, kt, vt, H, T, h, j, t);
+                vcode[row * HEAD_DIM + t] = oracle_v_code(page, kt, vt, H, T, h, j, t);
             }
             for (int b = 0; b < N_BLOCKS; b++) {
-                kd[row * N_BLOCKS + b] = k_scale_bits(page, H, T, h, j, b);
-                vd[row * N_BLOCKS + b] = v_scale_bits(page, H, T, h, j, b);
+                kd[row * N_BLOCKS + b] = kt == T_F16 ? 0 : k_scale_bits(page, kt, vt, H, T, h, j, b);
+                vd[row * N_BLOCKS + b] = vt == T_F16 ? 0 : v_scale_bits(page, kt, vt, H, T, h, j, b);
             }
         }
 }

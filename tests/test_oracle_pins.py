@@ -22,8 +22,23 @@ D = 128
 
 
 # ---------------------------------------------------------------- helpers
-def cache(n_tokens, n_kv_heads, layer=0, wid=90, page_tokens=256, pad="zero"):
-    return inputs.draw_layer(n_tokens, n_kv_heads, layer, wid, page_tokens=page_tokens, pad=pad)
+Q8_0, Q4_0, F16 = inputs.Q8_0, inputs.Q4_0, inputs.F16
+PAIRS = [(Q8_0, Q4_0), (Q8_0, Q8_0), (Q4_0, Q4_0), (F16, F16)]
+PAIR_IDS = ["q8k-q4v", "q8k-q8v", "q4k-q4v", "f16k-f16v"]
+
+
+def cache(n_tokens, n_kv_heads, layer=0, wid=90, page_tokens=256, pad="zero", k_type=Q8_0, v_type=Q4_0):
+    return inputs.draw_layer(n_tokens, n_kv_heads, layer, wid, page_tokens=page_tokens, pad=pad, k_type=k_type,
+                             v_type=v_type)
+
+
+def dequant(codes, scales, t_):
+    """Element values from the quantiser's unpaged arrays, by the block-format
+    definitions: Q8_0 d * c, Q4_0 d * (n - 8), F16 the value itself."""
+    if t_ == F16:
+        return codes.double()
+    d = scales.double().repeat_interleave(32, dim=-1)
+    return d * (codes.double() - (8.0 if t_ == Q4_0 else 0.0))
 
 
 def np_arrays(kv):
@@ -36,8 +51,8 @@ def sdpa_reference(kv, q, scale):
     N, H, _ = kv.kc.shape
     W, Hq, _ = q.shape
     G = Hq // H
-    K = kv.kd.double().repeat_interleave(32, dim=-1) * kv.kc.double()          # [N][H][D]
-    V = kv.vd.double().repeat_interleave(32, dim=-1) * (kv.vc.double() - 8.0)
+    K = dequant(kv.kc, kv.kd, kv.k_type)                                         # [N][H][D]
+    V = dequant(kv.vc, kv.vd, kv.v_type)
     Kh = K.permute(1, 0, 2).repeat_interleave(G, dim=0)                          # [Hq][N][D]
     Vh = V.permute(1, 0, 2).repeat_interleave(G, dim=0)
     Qh = q.double().permute(1, 0, 2)                                             # [Hq][W][D]
@@ -54,7 +69,8 @@ def identity_paged(oracle, kv, q, scale, page_tokens=256):
     n_pages = kv.pages.shape[0]
     pt = np.arange(n_pages, dtype=np.uint32)
     N, H = kv.kc.shape[:2]
-    return oracle.attend_paged(pt, N, page_tokens, q.shape[1], H, q.numpy(), scale, pool=kv.pages.numpy())
+    return oracle.attend_paged(pt, N, page_tokens, q.shape[1], H, q.numpy(), scale, pool=kv.pages.numpy(),
+                               k_type=kv.k_type, v_type=kv.v_type)
 
 
 def scattered_paged(oracle, kv, q, scale, seed, page_tokens=256):
@@ -82,7 +98,7 @@ def scattered_paged(oracle, kv, q, scale, seed, page_tokens=256):
             pt[p] = inputs.HOST_ENTRY
     N, H = kv.kc.shape[:2]
     return oracle.attend_paged(pt, N, page_tokens, q.shape[1], H, q.numpy(), scale, pool=pool, ring=ring,
-                               history=history)
+                               history=history, k_type=kv.k_type, v_type=kv.v_type)
 
 
 def const_cache(n_tokens, n_kv_heads, kc, kd, vc, vd, page_tokens=256):
@@ -199,6 +215,97 @@ def test_attention_matches_library_sdpa(oracle_mod, N, Hq, Hkv, W, T):
     out, lse = scattered_paged(oracle_mod, kv, q, scale, seed=N, page_tokens=T)
     assert np.max(np.abs(out - ref)) <= 1e-12
     assert np.max(np.abs(lse - ref_lse)) <= 1e-12
+
+
+PAIR_CASES = [
+    # (N, Hq, Hkv, W, page_tokens)
+    (300, 6, 2, 3, 256),      # ragged last page, GQA 3:1
+    (200, 8, 2, 6, 64),       # small pages, 6 verify rows
+    (37, 4, 1, 2, 32),        # fewer keys than one page
+]
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
+@pytest.mark.parametrize("N,Hq,Hkv,W,T", PAIR_CASES)
+def test_pair_attention_matches_library_sdpa(oracle_mod, pair, N, Hq, Hkv, W, T):
+    """Every supported (K, V) element-type pair, pages scattered over pool,
+    ring and host, against torch's fp64 SDPA on the quantiser's unpaged
+    arrays dequantised by the block-format definitions."""
+    kv = cache(N, Hkv, page_tokens=T, k_type=pair[0], v_type=pair[1], pad="garbage")
+    q = inputs.draw_queries(W, Hq, 0, 91)
+    scale = 1 / math.sqrt(D)
+    ref, ref_lse = sdpa_reference(kv, q, scale)
+    out, lse = scattered_paged(oracle_mod, kv, q, scale, seed=N + pair[0], page_tokens=T)
+    assert np.max(np.abs(out - ref)) <= 1e-12
+    assert np.max(np.abs(lse - ref_lse)) <= 1e-12
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
+def test_pair_page_bytes_closed_form(oracle_mod, pair):
+    """Per (head, token): code bytes (128 Q8_0, 64 Q4_0, 256 F16) plus 8 scale
+    bytes for each block type."""
+    per = {Q8_0: 128 + 8, Q4_0: 64 + 8, F16: 256}
+    for H, T in [(8, 256), (2, 64), (1, 32)]:
+        want = H * T * (per[pair[0]] + per[pair[1]])
+        assert oracle_mod.page_bytes(H, T, *pair) == want == inputs.page_bytes(H, T, *pair)
+        assert oracle_mod.pair_supported(*pair)
+    assert not oracle_mod.pair_supported(Q4_0, Q8_0) and not oracle_mod.pair_supported(F16, Q4_0)
+
+
+def test_pair_codes_exhaustive():
+    """Every 4-bit K code, every int8 V code and every binary16 pattern as a
+    K and a V element is read back from packed pages with its own bits."""
+    import oracle as om
+    T, H = 256, 2
+    j = torch.arange(T).view(-1, 1, 1)
+    h = torch.arange(H).view(1, -1, 1)
+    t = torch.arange(D).view(1, 1, -1)
+    sc = torch.tensor(SCALES, dtype=torch.float16)
+    kd = sc[(j * 4 + torch.arange(4).view(1, 1, -1) + h) % len(SCALES)].expand(T, H, 4).contiguous()
+    vd = sc[(j * 4 + torch.arange(4).view(1, 1, -1) + 2 + h) % len(SCALES)].expand(T, H, 4).contiguous()
+    # Q4_0 K / Q4_0 V
+    kc4 = ((j * 5 + t * 3 + h) % 16).expand(T, H, D).to(torch.uint8).contiguous()
+    vc4 = ((j * 7 + t + 2 * h) % 16).expand(T, H, D).to(torch.uint8).contiguous()
+    page = inputs.pack_pages(kc4, kd, vc4, vd, T, k_type=Q4_0, v_type=Q4_0)[0].numpy()
+    a, b, c, e = om.unpack_page(page, H, T, Q4_0, Q4_0)
+    assert np.array_equal(a, kc4.numpy()) and np.array_equal(c, vc4.numpy())
+    assert np.array_equal(b, kd.numpy().view(np.uint16)) and np.array_equal(e, vd.numpy().view(np.uint16))
+    assert set(np.unique(a)) == set(range(16))
+    # Q8_0 K / Q8_0 V
+    kc8 = (((j * 128 + t + 97 * h) % 256) - 128).expand(T, H, D).to(torch.int8).contiguous()
+    vc8 = (((j * 131 + t * 3 + 5 * h) % 256) - 128).expand(T, H, D).to(torch.int8).contiguous()
+    page = inputs.pack_pages(kc8, kd, vc8, vd, T, k_type=Q8_0, v_type=Q8_0)[0].numpy()
+    a, b, c, e = om.unpack_page(page, H, T, Q8_0, Q8_0)
+    assert np.array_equal(a, kc8.numpy()) and np.array_equal(c, vc8.numpy())
+    assert np.array_equal(e, vd.numpy().view(np.uint16))
+    assert set(np.unique(c)) == set(range(-128, 128))
+    K, V = om.decode_page(page, H, T, Q8_0, Q8_0)
+    assert np.array_equal(V, np.repeat(vd.double().numpy(), 32, -1) * vc8.double().numpy())
+    # F16 / F16: all 65,536 patterns (T * H * D = 65,536), V in another order
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(T, H, D)
+    kf = torch.from_numpy(bits.copy()).view(torch.float16)
+    vf = torch.from_numpy(bits[::-1].copy()).view(torch.float16)
+    page = inputs.pack_pages(kf, None, vf, None, T, k_type=F16, v_type=F16)[0].numpy()
+    assert page.size == H * T * 512
+    a, _, c, _ = om.unpack_page(page, H, T, F16, F16)
+    assert np.array_equal(a.astype(np.uint16), bits) and np.array_equal(c.astype(np.uint16), bits[::-1])
+    K, V = om.decode_page(page, H, T, F16, F16)
+    ref = bits.view(np.float16).astype(np.float64)
+    fin = np.isfinite(ref)
+    assert np.array_equal(K[fin], ref[fin]) and np.array_equal(np.isnan(K), np.isnan(ref))
+
+
+@pytest.mark.parametrize("pair", PAIRS[1:], ids=PAIR_IDS[1:])
+def test_pair_split_merge_identity(oracle_mod, pair):
+    N, Hq, H, W = 700, 4, 2, 3
+    kv = cache(N, H, k_type=pair[0], v_type=pair[1])
+    q = inputs.draw_queries(W, Hq, 0, 92)
+    s = 1 / math.sqrt(D)
+    full, _ = identity_paged(oracle_mod, kv, q, s)
+    bounds = [0, 100, 256, 257, 600, N + 10]
+    m, l, acc = oracle_mod.split_partials(kv.pages.numpy(), 256, N, Hq, H, q.numpy(), s, bounds,
+                                          k_type=pair[0], v_type=pair[1])
+    assert np.max(np.abs(oracle_mod.merge(m, l, acc) - full)) <= 1e-12
 
 
 def test_logical_equals_paged_bitwise(oracle_mod):
@@ -371,25 +478,34 @@ def test_split_merge_identity(oracle_mod, seed):
 
 
 MUTATIONS = [
-    ("nibble halves swapped", "return jj < 16 ? (byte & 0x0F) : (byte >> 4);",
+    # (name, pair, text in oracle.c, planted replacement)
+    ("nibble halves swapped", (Q8_0, Q4_0), "return jj < 16 ? (byte & 0x0F) : (byte >> 4);",
      "return jj >= 16 ? (byte & 0x0F) : (byte >> 4);"),
-    ("Q4_0 offset wrong", "(double)(oracle_v_code(page, H, T, head, j, t) - 8)",
-     "(double)(oracle_v_code(page, H, T, head, j, t) - 7)"),
-    ("K layout half-block offset dropped", "(size_t)((t / 32) % 2) * 8 + (size_t)(t % 8);",
+    ("Q4_0 offset wrong", (Q8_0, Q4_0), "return scale * (double)(code - 8);", "return scale * (double)(code - 7);"),
+    ("K layout half-block offset dropped", (Q8_0, Q4_0), "(size_t)((t / 32) % 2) * 8 + (size_t)(t % 8);",
      "(size_t)((t / 32) % 2) * 0 + (size_t)(t % 8);"),
-    ("GQA map transposed", "attend_range(src, h / G,", "attend_range(src, h % Hkv,"),
-    ("causal mask off by one", "scale, 0, pos + 1, &m, &l, acc);", "scale, 0, pos, &m, &l, acc);"),
-    ("K scale block index wrong", "sec_k_scales(H, T) + (((size_t)head * T + j) * N_BLOCKS + block) * 2;",
-     "sec_k_scales(H, T) + (((size_t)head * T + j) * N_BLOCKS + (block ^ 1)) * 2;"),
-    ("V scale tile slot wrong", "(size_t)((jj / 16) * 4 + jj % 4) * 2;",
+    ("GQA map transposed", (Q8_0, Q4_0), "attend_range(src, h / G,", "attend_range(src, h % Hkv,"),
+    ("causal mask off by one", (Q8_0, Q4_0), "scale, 0, pos + 1, &m, &l, acc);", "scale, 0, pos, &m, &l, acc);"),
+    ("K scale block index wrong", (Q8_0, Q4_0),
+     "sec_k_scales(kt, vt, H, T) + (((size_t)head * T + j) * N_BLOCKS + block) * 2;",
+     "sec_k_scales(kt, vt, H, T) + (((size_t)head * T + j) * N_BLOCKS + (block ^ 1)) * 2;"),
+    ("V scale tile slot wrong", (Q8_0, Q4_0), "(size_t)((jj / 16) * 4 + jj % 4) * 2;",
      "(size_t)((jj / 16) * 4 + (jj + 1) % 4) * 2;"),
-    ("V tile stride wrong", "(size_t)head * T * (HEAD_DIM / 2) + (size_t)(j / 32) * 2048;",
-     "(size_t)head * T * (HEAD_DIM / 2) + (size_t)(j / 32) * 1024;"),
+    ("V tile stride wrong", (Q8_0, Q4_0), "(size_t)(j / 32) * 32 * vc;", "(size_t)(j / 32) * 16 * vc;"),
+    ("Q4_0 K nibble halves swapped", (Q4_0, Q4_0), "return (t % 8) < 4 ? (byte & 0x0F) : (byte >> 4);",
+     "return (t % 8) >= 4 ? (byte & 0x0F) : (byte >> 4);"),
+    ("Q8_0 V half-tile offset dropped", (Q8_0, Q8_0), "lane * 16 + (size_t)((t / 16) % 2) * 8 + (size_t)slot]",
+     "lane * 16 + (size_t)((t / 16) % 2) * 0 + (size_t)slot]"),
+    ("F16 K dimension-group stride wrong", (F16, F16),
+     "(size_t)(t / 32) * 1024 + lane * 16 + (size_t)(t % 8) * 2);",
+     "(size_t)(t / 32) * 512 + lane * 16 + (size_t)(t % 8) * 2);"),
+    ("F16 V slot order wrong", (F16, F16), "(size_t)(t / 16) * 1024 + lane * 16 + (size_t)slot * 2);",
+     "(size_t)(t / 16) * 1024 + lane * 16 + (size_t)(slot ^ 1) * 2);"),
 ]
 
 
-@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
-def test_planted_oracle_mistake_fails_pin(oracle_mod, tmp_path, name, old, new):
+@pytest.mark.parametrize("name,pair,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_oracle_mistake_fails_pin(oracle_mod, tmp_path, name, pair, old, new):
     """Plant a plausible mistake in a copy of the oracle's C source, build it
     on the CPU, and check that the library-routine pin rejects it."""
     import ctypes
@@ -403,9 +519,9 @@ def test_planted_oracle_mistake_fails_pin(oracle_mod, tmp_path, name, old, new):
                            str(mutated), "-lm"])
     lib = ctypes.CDLL(str(so))
     P, I, Z, Dd = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_double
-    lib.oracle_attend_paged.argtypes = [P, Z, P, Z, P, P, I, I, I, I, P, I, Dd, P, I, P, P, I]
+    lib.oracle_attend_paged.argtypes = [P, Z, P, Z, P, P, I, I, I, I, I, I, P, I, Dd, P, I, P, P, I]
     N, Hq, H, W = 300, 6, 2, 3
-    kv = cache(N, H)
+    kv = cache(N, H, k_type=pair[0], v_type=pair[1])
     q = inputs.draw_queries(W, Hq, 0, 90)
     s = 1 / math.sqrt(D)
     ref, _ = sdpa_reference(kv, q, s)
@@ -414,7 +530,7 @@ def test_planted_oracle_mistake_fails_pin(oracle_mod, tmp_path, name, old, new):
     qn = np.ascontiguousarray(q.numpy())
     out = np.zeros((W, Hq, D))
     lse = np.zeros((W, Hq))
-    rc = lib.oracle_attend_paged(pool.ctypes.data, pool.shape[0], None, 0, None, pt.ctypes.data, N, 256, Hq, H,
-                                 qn.ctypes.data, W, s, None, W, out.ctypes.data, lse.ctypes.data, 1)
+    rc = lib.oracle_attend_paged(pool.ctypes.data, pool.shape[0], None, 0, None, pt.ctypes.data, N, 256, pair[0],
+                                 pair[1], Hq, H, qn.ctypes.data, W, s, None, W, out.ctypes.data, lse.ctypes.data, 1)
     assert rc == 0
     assert not np.max(np.abs(out - ref)) <= 1e-12, f"pin missed the planted mistake: {name}"
