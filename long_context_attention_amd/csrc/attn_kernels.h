@@ -20,6 +20,7 @@ struct SplitArgs {
     uint32_t n_ring_slots;
     size_t page_bytes;
     size_t sec_kd, sec_vc, sec_vd; // section offsets inside a page
+    uint32_t k_type, v_type;      // element types (KVATTN_TYPE_*)
     float qscale;                 // softmax_scale * log2(e)
     const float *q;               // [W][Hq][128]
     float *part_o;                // [splits][W*Hq][128]
@@ -57,9 +58,10 @@ struct WriterArgs {
     uint32_t ring_base, n_ring_slots;
     size_t page_bytes;
     size_t sec_kd, sec_vc, sec_vd;
+    uint32_t k_type, v_type;
 };
 
-size_t kvattn_split_smem_bytes(int rt);
+size_t kvattn_split_smem_bytes(int rt, uint32_t k_type, uint32_t v_type);
 hipError_t kvattn_launch_writer(const WriterArgs &a, hipStream_t s);
 hipError_t kvattn_launch_ring_copy(const RingCopyArgs &a, hipStream_t s);
 hipError_t kvattn_split_setup();

@@ -110,21 +110,43 @@ __device__ __forceinline__ const uint8_t *resolve_page(const SplitArgs &a, uint3
 }
 
 // ---------------------------------------------------------------------------
-// One 32-key chunk of one KV head as staged in LDS (6656 bytes; each section
-// keeps the page's byte order):
-//   [0, 4096)     K codes, two 16-key tiles of 2048 bytes; a 64-lane read of
-//                 16 bytes per lane covers one 1024-byte quarter
-//   [4096, 6144)  V codes, two quarters
-//   [6144, 6400)  K scales, [key][block] binary16
-//   [6400, 6656)  the chunk's V-scale tile
-// Every wave owns a ring of kStages such buffers, filled by direct-to-LDS
-// loads (global_load_lds_dwordx4: 16 bytes per lane, no registers), so
-// kStages - 1 chunks stay in flight while the wave computes on another.
+// Element types (the header's KVATTN_TYPE_* values) and the staged chunk.
+// One 32-key chunk of one KV head as staged in LDS keeps the page's byte
+// order, section by section:
+//   [0, kbytes)            K codes, two 16-key tiles; a 64-lane read of 16
+//                          bytes per lane covers one 1024-byte quarter
+//   [off_v, +vbytes)       V codes (one 32-key tile), in quarters
+//   [off_ks, +256)         K scales, [key][block] binary16 (block K types)
+//   [off_vs, +256)         the chunk's V-scale tile (block V types)
+// Sizes: Q8_0 K / Q4_0 V 6656 bytes, Q8_0 / Q8_0 8704, Q4_0 / Q4_0 4608,
+// F16 / F16 16384.  The chunk arrives by direct-to-LDS loads
+// (global_load_lds_dwordx4: 16 bytes per lane, no registers), `dma` load
+// instructions per chunk: one per code quarter plus one for both scale
+// tiles (lanes 0..15 K, 16..31 V).
 // ---------------------------------------------------------------------------
-constexpr int kChunkBytes = 6656;
-constexpr int kOffV = 4096, kOffKS = 6144, kOffVS = 6400;
+constexpr int kTypeF16 = 1, kTypeQ4_0 = 2, kTypeQ8_0 = 8;
+
+template <int KT, int VT>
+struct Chunk {
+    static_assert((KT == kTypeQ8_0 && VT == kTypeQ4_0) || (KT == kTypeQ8_0 && VT == kTypeQ8_0) ||
+                      (KT == kTypeQ4_0 && VT == kTypeQ4_0) || (KT == kTypeF16 && VT == kTypeF16),
+                  "supported K/V element-type pairs");
+    static constexpr int code_bytes(int t) { return t == kTypeQ8_0 ? 128 : t == kTypeQ4_0 ? 64 : 256; }
+    static constexpr bool kblk = KT != kTypeF16, vblk = VT != kTypeF16;
+    static constexpr int kc = code_bytes(KT), vc = code_bytes(VT);  // code bytes per key
+    static constexpr int k_quarters = 32 * kc / 1024, v_quarters = 32 * vc / 1024;
+    static constexpr int off_v = 32 * kc;
+    static constexpr int off_ks = off_v + 32 * vc;
+    static constexpr int off_vs = off_ks + (kblk ? 256 : 0);
+    static constexpr int bytes = off_vs + (vblk ? 256 : 0);
+    static constexpr int dma = k_quarters + v_quarters + (kblk ? 1 : 0);
+    static constexpr int kw = kc / 8, vw = vc / 8;  // code dwords per lane and chunk
+    static constexpr int pf_blocks = vblk ? 4 : 1;  // distinct P' operands per row tile
+};
+
+// The Q8_0 K / Q4_0 V chunk (the wide kernel's raw-ring default shape).
+constexpr int kChunkBytes = Chunk<kTypeQ8_0, kTypeQ4_0>::bytes;
 constexpr int kStages = 3;  // raw-chunk ring of the wide kernel
-constexpr int kDmaPerChunk = 7;  // 4 K, 2 V, 1 scales
 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
@@ -143,49 +165,61 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// Wait until at most `newer` (< S) chunks issued after the one needed are in
-// flight, for a ring of S stages.
-template <int S>
+// Wait until at most `newer` (< S) chunks of D loads each, issued after the
+// one needed, are in flight, for a ring of S stages.
+template <int S, int D>
 __device__ __forceinline__ void wait_chunk(uint32_t newer) {
     static_assert(S == 2 || S == 3, "rings of two or three stages");
+    static_assert(2 * D <= 63, "vmcnt range");
     if (S == 3 && newer >= 2)
-        wait_vmcnt<2 * kDmaPerChunk>();
+        wait_vmcnt<2 * D>();
     else if (newer >= 1)
-        wait_vmcnt<kDmaPerChunk>();
+        wait_vmcnt<D>();
     else
         wait_vmcnt<0>();
 }
 
-// Wide kernel: a wave issues at most one load per chunk.
-__device__ __forceinline__ void wait_chunk_wide(uint32_t newer) {
-    if (newer >= 2)
-        wait_vmcnt<2>();
-    else if (newer == 1)
-        wait_vmcnt<1>();
-    else
-        wait_vmcnt<0>();
+// Wide kernel: wait until at most n of the wave's loads are in flight (n is
+// wave-uniform and small).
+__device__ __forceinline__ void wait_vmcnt_upto(uint32_t n) {
+    switch (n) {
+        case 0: wait_vmcnt<0>(); break;
+        case 1: wait_vmcnt<1>(); break;
+        case 2: wait_vmcnt<2>(); break;
+        case 3: wait_vmcnt<3>(); break;
+        default: wait_vmcnt<4>(); break;
+    }
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
 }
 
-// Issue the direct-to-LDS loads of chunk `chunk` of KV head kvh (page base
-// `base`) into the buffer at LDS address dst.
-__device__ __forceinline__ void issue_chunk(const SplitArgs &a, const uint8_t *base, uint32_t kvh, uint32_t jj0,
-                                            int lane, uint32_t dst) {
+// Direct-to-LDS load number d (0 <= d < Chunk::dma) of the chunk whose first
+// key is jj0 in KV head kvh of the page at `base`, into the chunk buffer at
+// LDS address dst.
+template <int KT, int VT>
+__device__ __forceinline__ void issue_chunk_part(const SplitArgs &a, const uint8_t *base, uint32_t kvh, uint32_t jj0,
+                                                 int lane, uint32_t dst, int d) {
+    using C = Chunk<KT, VT>;
     const size_t kv = (size_t)kvh * a.T + jj0;  // first key of the chunk in the head's section
-    const uint8_t *kc = base + kv * 128 + lane * 16;
-    const uint8_t *vc = base + a.sec_vc + kv * 64 + lane * 16;
-#pragma unroll
-    for (int q = 0; q < 4; q++) dma16(kc + 1024 * q, dst + 1024 * q);
-#pragma unroll
-    for (int q = 0; q < 2; q++) dma16(vc + 1024 * q, dst + kOffV + 1024 * q);
-    if (lane < 32) {
+    if (d < C::k_quarters) {
+        dma16(base + kv * C::kc + lane * 16 + 1024 * d, dst + 1024 * d);
+    } else if (d < C::k_quarters + C::v_quarters) {
+        const int q = d - C::k_quarters;
+        dma16(base + a.sec_vc + kv * C::vc + lane * 16 + 1024 * q, dst + C::off_v + 1024 * q);
+    } else if (lane < 32) {
         const uint8_t *sp = lane < 16 ? base + a.sec_kd + kv * 8 + lane * 16
                                       : base + a.sec_vd + (size_t)kvh * a.T * 8 + (size_t)(jj0 >> 5) * 256 + (lane - 16) * 16;
-        dma16(sp, dst + kOffKS);
+        dma16(sp, dst + C::off_ks);
     }
+}
+
+template <int KT, int VT>
+__device__ __forceinline__ void issue_chunk(const SplitArgs &a, const uint8_t *base, uint32_t kvh, uint32_t jj0,
+                                            int lane, uint32_t dst) {
+#pragma unroll
+    for (int d = 0; d < Chunk<KT, VT>::dma; d++) issue_chunk_part<KT, VT>(a, base, kvh, jj0, lane, dst, d);
 }
 
 __device__ __forceinline__ void put4(uint32_t *d, const uint4 &x) {
@@ -195,17 +229,37 @@ __device__ __forceinline__ void put4(uint32_t *d, const uint4 &x) {
     d[3] = x.w;
 }
 
-// K codes of the lane: kq[8tt + ...] = dwords of 16-key tile tt (blocks 2k,
-// 2k + 1 of quarter k, 8 codes each).
-__device__ __forceinline__ void read_kcodes(const uint8_t *stg, int lane, uint32_t kq[16]) {
+// K codes of the lane, quarter by quarter: kq[4q .. 4q + 3] = its 16 bytes of
+// quarter q.  Q8_0: quarter q = key tile q / 2, blocks 2 (q mod 2) and +1
+// (8 codes each); Q4_0: quarter = key tile, one dword per block; F16:
+// quarter q = key tile q / 4, block q mod 4, eight binary16.
+template <int KT, int VT>
+__device__ __forceinline__ void read_kcodes(const uint8_t *stg, int lane, uint32_t (&kq)[Chunk<KT, VT>::kw]) {
 #pragma unroll
-    for (int q = 0; q < 4; q++) put4(kq + 4 * q, *reinterpret_cast<const uint4 *>(stg + 1024 * q + 16 * lane));
+    for (int q = 0; q < Chunk<KT, VT>::k_quarters; q++)
+        put4(kq + 4 * q, *reinterpret_cast<const uint4 *>(stg + 1024 * q + 16 * lane));
+}
+
+// The lane's K operand (8 f16: key 16 tt + c16, dims 32 b + 8 g .. +8) of
+// key tile tt and block b, exact: Q8_0 c, Q4_0 n - 8, F16 the value.
+template <int KT>
+__device__ __forceinline__ half8 k_frag(const uint32_t *kq, int tt, int b) {
+    if constexpr (KT == kTypeQ8_0) {
+        const uint32_t *w = kq + 8 * tt + 4 * (b >> 1) + 2 * (b & 1);
+        return q8_to_half8(w[0], w[1]);
+    } else if constexpr (KT == kTypeQ4_0) {
+        return q4_to_half8(kq[4 * tt + b]);
+    } else {
+        const uint32_t *w = kq + 16 * tt + 4 * b;
+        return __builtin_bit_cast(half8, uint4{w[0], w[1], w[2], w[3]});
+    }
 }
 
 // K scales as the lane uses them: kd[8tt + ...] binary16 pairs, key 4g + v
 // of tile tt, block b at half 4v + b.
+template <int KT, int VT>
 __device__ __forceinline__ void read_kscales(const uint8_t *stg, int grp, uint32_t kd[16]) {
-    const uint4 *k4 = reinterpret_cast<const uint4 *>(stg + kOffKS);  // key j at bytes 8j
+    const uint4 *k4 = reinterpret_cast<const uint4 *>(stg + Chunk<KT, VT>::off_ks);  // key j at bytes 8j
     put4(kd + 0, k4[2 * grp]);
     put4(kd + 4, k4[2 * grp + 1]);
     put4(kd + 8, k4[8 + 2 * grp]);
@@ -213,16 +267,48 @@ __device__ __forceinline__ void read_kscales(const uint8_t *stg, int grp, uint32
 }
 
 // V scales: vd[4b + ...] binary16 pairs of block b, operand slots 2i, 2i + 1.
+template <int KT, int VT>
 __device__ __forceinline__ void read_vscales(const uint8_t *stg, int grp, uint32_t vd[16]) {
-    const uint4 *v4 = reinterpret_cast<const uint4 *>(stg + kOffVS);
+    const uint4 *v4 = reinterpret_cast<const uint4 *>(stg + Chunk<KT, VT>::off_vs);
 #pragma unroll
     for (int b = 0; b < 4; b++) put4(vd + 4 * b, v4[b * 4 + grp]);
 }
 
-// V codes of the lane: one dword per 16-dim tile.
-__device__ __forceinline__ void read_vcodes(const uint8_t *stg, int lane, uint32_t vq[8]) {
+// V codes of the lane, quarter by quarter.  Q4_0: one dword per 16-dim tile;
+// Q8_0: two dwords per tile; F16: four (eight binary16).
+template <int KT, int VT>
+__device__ __forceinline__ void read_vcodes(const uint8_t *stg, int lane, uint32_t (&vq)[Chunk<KT, VT>::vw]) {
 #pragma unroll
-    for (int q = 0; q < 2; q++) put4(vq + 4 * q, *reinterpret_cast<const uint4 *>(stg + kOffV + 1024 * q + 16 * lane));
+    for (int q = 0; q < Chunk<KT, VT>::v_quarters; q++)
+        put4(vq + 4 * q, *reinterpret_cast<const uint4 *>(stg + Chunk<KT, VT>::off_v + 1024 * q + 16 * lane));
+}
+
+// The lane's V^T operand of 16-dim tile n (8 f16 over the lane's key slots),
+// exact: Q4_0 n - 8, Q8_0 c, F16 the value.
+template <int VT>
+__device__ __forceinline__ half8 v_frag(const uint32_t *vq, int n) {
+    if constexpr (VT == kTypeQ4_0) {
+        return q4_to_half8(vq[n]);
+    } else if constexpr (VT == kTypeQ8_0) {
+        return q8_to_half8(vq[2 * n], vq[2 * n + 1]);
+    } else {
+        return __builtin_bit_cast(half8, uint4{vq[4 * n], vq[4 * n + 1], vq[4 * n + 2], vq[4 * n + 3]});
+    }
+}
+
+// F16 values carry no scale to clear: keys at or past the history length
+// (page padding, possibly NaN) get value 0 in the lane's operands instead.
+// Operand slot i of group g is key 16 (i / 4) + 4 g + i mod 4; a dword holds
+// slots 2i, 2i + 1.
+template <int KT, int VT>
+__device__ __forceinline__ void clear_padding_vcodes(uint32_t *vq, int grp, uint32_t n_valid) {
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+        const uint32_t key0 = 16 * (w >> 1) + 4 * grp + 2 * (w & 1);
+        const uint32_t keep = (key0 < n_valid ? 0x0000FFFFu : 0u) | (key0 + 1 < n_valid ? 0xFFFF0000u : 0u);
+#pragma unroll
+        for (int n = 0; n < 8; n++) vq[4 * n + w] &= keep;
+    }
 }
 
 // binary16 half `i` of a packed array (lo half = even index)
@@ -245,33 +331,50 @@ struct RowState {
 };
 
 // Scores of one chunk for NT row tiles: s[t][4tt + v] is key 16tt + 4g + v
-// of the chunk for tile t, log2-scaled.  Each K fragment is dequantised once
-// and feeds one MFMA per tile and 32-dim block, scaled by that block's d_K.
-template <int NT>
-__device__ __forceinline__ void chunk_scores(const RowState (&st)[NT], const uint32_t kq[16], const uint32_t kd[16],
+// of the chunk for tile t, log2-scaled.  Each K fragment is converted once
+// and feeds one MFMA per tile and 32-dim block; block types scale each
+// block's fp32 dot by its own binary16 d_K, F16 keys accumulate the four
+// blocks in the MFMA.
+template <int NT, int KT>
+__device__ __forceinline__ void chunk_scores(const RowState (&st)[NT], const uint32_t *kq, const uint32_t kd[16],
                                              float (&s)[NT][8]) {
 #pragma unroll
     for (int tt = 0; tt < 2; tt++) {
-        // all MFMAs of the key tile first, so none waits on the one before
-        floatx4 d[4][NT];
+        if constexpr (KT == kTypeF16) {
+            floatx4 d[NT];
 #pragma unroll
-        for (int b = 0; b < 4; b++) {
-            const uint32_t *w = kq + 8 * tt + 4 * (b >> 1) + 2 * (b & 1);
-            const half8 kf = q8_to_half8(w[0], w[1]);
+            for (int t = 0; t < NT; t++) d[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int b = 0; b < 4; b++) {
+                const half8 kf = k_frag<KT>(kq, tt, b);
+#pragma unroll
+                for (int t = 0; t < NT; t++) d[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, st[t].qf[b], d[t], 0, 0, 0);
+            }
 #pragma unroll
             for (int t = 0; t < NT; t++)
-                d[b][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, st[t].qf[b], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        }
 #pragma unroll
-        for (int t = 0; t < NT; t++)
+                for (int v = 0; v < 4; v++) s[t][4 * tt + v] = d[t][v];
+        } else {
+            // all MFMAs of the key tile first, so none waits on the one before
+            floatx4 d[4][NT];
 #pragma unroll
-            for (int v = 0; v < 4; v++) {
-                // fma with the binary16 operand read in place (v_fma_mix_f32)
-                float acc = half_of(kd + 8 * tt, 4 * v) * d[0][t][v];
+            for (int b = 0; b < 4; b++) {
+                const half8 kf = k_frag<KT>(kq, tt, b);
 #pragma unroll
-                for (int b = 1; b < 4; b++) acc = __builtin_fmaf(half_of(kd + 8 * tt, 4 * v + b), d[b][t][v], acc);
-                s[t][4 * tt + v] = acc;
+                for (int t = 0; t < NT; t++)
+                    d[b][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, st[t].qf[b], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
             }
+#pragma unroll
+            for (int t = 0; t < NT; t++)
+#pragma unroll
+                for (int v = 0; v < 4; v++) {
+                    // fma with the binary16 operand read in place (v_fma_mix_f32)
+                    float acc = half_of(kd + 8 * tt, 4 * v) * d[0][t][v];
+#pragma unroll
+                    for (int b = 1; b < 4; b++) acc = __builtin_fmaf(half_of(kd + 8 * tt, 4 * v + b), d[b][t][v], acc);
+                    s[t][4 * tt + v] = acc;
+                }
+        }
     }
 }
 
@@ -292,8 +395,9 @@ __device__ __forceinline__ void mask_scores(const RowState (&st)[NT], uint32_t k
 // for those keys (their P is 0).  Lane l owns tile bytes 4l .. 4l + 3:
 // block l / 16, keys 16 hi + 4 q + r with q = (l / 4) mod 4, hi = (l mod 4) / 2,
 // r = 2 (l mod 2) + i for the dword's half i.
+template <int KT, int VT>
 __device__ __forceinline__ void sanitize_vscales(uint8_t *stg, int lane, uint32_t n_valid) {
-    uint32_t *w = reinterpret_cast<uint32_t *>(stg + kOffVS) + lane;
+    uint32_t *w = reinterpret_cast<uint32_t *>(stg + Chunk<KT, VT>::off_vs) + lane;
     const uint32_t key0 = 16 * ((lane & 3) >> 1) + 4 * ((lane >> 2) & 3) + 2 * (lane & 1);
     uint32_t v = *w;
     if (key0 >= n_valid) v &= 0xFFFF0000u;
@@ -303,9 +407,11 @@ __device__ __forceinline__ void sanitize_vscales(uint8_t *stg, int lane, uint32_
 
 // Softmax step of one chunk for one row tile: lazy reference update
 // (rescaling the accumulators, which already hold every earlier chunk),
-// probabilities, the denominator, and the P' operands P * d_V of the four
-// value blocks.
-__device__ __forceinline__ void chunk_probs(RowState &st, const float s[8], const uint32_t vd[16], half8 pf[4]) {
+// probabilities, the denominator, and the P' operands: P * d_V per value
+// block for block V types, P itself for F16 values.
+template <int VT>
+__device__ __forceinline__ void chunk_probs(RowState &st, const float s[8], const uint32_t vd[16],
+                                            half8 (&pf)[VT == kTypeF16 ? 1 : 4]) {
     float m = s[0];
 #pragma unroll
     for (int i = 1; i < 8; i++) m = fmaxf(m, s[i]);
@@ -328,26 +434,33 @@ __device__ __forceinline__ void chunk_probs(RowState &st, const float s[8], cons
         lsum += p[i];
     }
     st.l_run += lsum;
+    if constexpr (VT == kTypeF16) {
+        pf[0] = half8{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3],
+                      (_Float16)p[4], (_Float16)p[5], (_Float16)p[6], (_Float16)p[7]};
+    } else {
 #pragma unroll
-    for (int b = 0; b < 4; b++) {
-        float e[8];
+        for (int b = 0; b < 4; b++) {
+            float e[8];
 #pragma unroll
-        for (int i = 0; i < 8; i++) e[i] = __builtin_fmaf(p[i], half_of(vd + 4 * b, i), 0.0f);
-        pf[b] = half8{(_Float16)e[0], (_Float16)e[1], (_Float16)e[2], (_Float16)e[3],
-                      (_Float16)e[4], (_Float16)e[5], (_Float16)e[6], (_Float16)e[7]};
+            for (int i = 0; i < 8; i++) e[i] = __builtin_fmaf(p[i], half_of(vd + 4 * b, i), 0.0f);
+            pf[b] = half8{(_Float16)e[0], (_Float16)e[1], (_Float16)e[2], (_Float16)e[3],
+                          (_Float16)e[4], (_Float16)e[5], (_Float16)e[6], (_Float16)e[7]};
+        }
     }
 }
 
 // O^T += V^T P'^T for one chunk and NT row tiles: dim tile n = 2b + nn of
-// value block b; each V fragment is dequantised once.
-template <int NT>
-__device__ __forceinline__ void chunk_pv(RowState (&st)[NT], const uint32_t vq[8], const half8 (&pf)[NT][4]) {
+// value block b; each V fragment is converted once.
+template <int NT, int VT>
+__device__ __forceinline__ void chunk_pv(RowState (&st)[NT], const uint32_t *vq,
+                                         const half8 (&pf)[NT][VT == kTypeF16 ? 1 : 4]) {
 #pragma unroll
     for (int n = 0; n < 8; n++) {
-        const half8 vf = q4_to_half8(vq[n]);
+        const half8 vf = v_frag<VT>(vq, n);
 #pragma unroll
         for (int t = 0; t < NT; t++)
-            st[t].acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[t][n >> 1], st[t].acc[n], 0, 0, 0);
+            st[t].acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[t][VT == kTypeF16 ? 0 : (n >> 1)], st[t].acc[n],
+                                                                  0, 0, 0);
     }
 }
 

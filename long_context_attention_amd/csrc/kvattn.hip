@@ -38,14 +38,27 @@ struct Layout {
     size_t page_bytes, sec_kd, sec_vc, sec_vd;
 };
 
-Layout page_layout(uint32_t H, uint32_t T) {
+bool pair_supported(uint32_t kt, uint32_t vt) {
+    return (kt == KVATTN_TYPE_Q8_0 && vt == KVATTN_TYPE_Q4_0) || (kt == KVATTN_TYPE_Q8_0 && vt == KVATTN_TYPE_Q8_0) ||
+           (kt == KVATTN_TYPE_Q4_0 && vt == KVATTN_TYPE_Q4_0) || (kt == KVATTN_TYPE_F16 && vt == KVATTN_TYPE_F16);
+}
+
+// Code bytes per (token, head) row and scale bytes (4 binary16 block scales;
+// none for F16).
+size_t code_bytes(uint32_t t) { return t == KVATTN_TYPE_Q8_0 ? kHeadDim : t == KVATTN_TYPE_Q4_0 ? kHeadDim / 2 : 2 * kHeadDim; }
+size_t scale_bytes(uint32_t t) { return t == KVATTN_TYPE_F16 ? 0 : 8; }
+
+// Sections of a page: K codes, K scales, V codes, V scales.
+Layout page_layout(uint32_t H, uint32_t T, uint32_t kt, uint32_t vt) {
     Layout l;
-    l.sec_kd = (size_t)H * T * kHeadDim;
-    l.sec_vc = l.sec_kd + (size_t)H * T * 8;
-    l.sec_vd = l.sec_vc + (size_t)H * T * (kHeadDim / 2);
-    l.page_bytes = l.sec_vd + (size_t)H * T * 8;
+    l.sec_kd = (size_t)H * T * code_bytes(kt);
+    l.sec_vc = l.sec_kd + (size_t)H * T * scale_bytes(kt);
+    l.sec_vd = l.sec_vc + (size_t)H * T * code_bytes(vt);
+    l.page_bytes = l.sec_vd + (size_t)H * T * scale_bytes(vt);
     return l;
 }
+
+Layout page_layout(const kvattn_params &p) { return page_layout(p.n_kv_heads, p.page_tokens, p.k_type, p.v_type); }
 
 // Reads the caller's params honouring struct_size (append-only struct).
 bool read_params(const kvattn_params *in, kvattn_params *out) {
@@ -61,8 +74,8 @@ int check_params(const kvattn_params &p, std::string &why) {
         why = "n_layers, n_q_heads, n_kv_heads, max_pages_per_layer and max_rows must be >= 1";
         return KVATTN_E_ARG;
     }
-    if (p.k_type != KVATTN_TYPE_Q8_0 || p.v_type != KVATTN_TYPE_Q4_0) {
-        why = "only the Q8_0 K / Q4_0 V pair is implemented";
+    if (!pair_supported(p.k_type, p.v_type)) {
+        why = "unsupported K/V element-type pair (supported: Q8_0/Q4_0, Q8_0/Q8_0, Q4_0/Q4_0, F16/F16)";
         return KVATTN_E_UNSUPPORTED;
     }
     if (p.head_dim != kHeadDim) {
@@ -116,7 +129,7 @@ WsLayout workspace_layout(const kvattn_params &p) {
     w.tables = 0;
     w.lists = align_up(ents);
     w.staging = w.lists + align_up(ents);
-    w.part_ml = w.staging + align_up(page_layout(p.n_kv_heads, p.page_tokens).page_bytes);
+    w.part_ml = w.staging + align_up(page_layout(p).page_bytes);
     w.part_o = w.part_ml + align_up(units * 2 * sizeof(float));
     w.total = w.part_o + align_up(units * kHeadDim * sizeof(float));
     return w;
@@ -234,6 +247,8 @@ SplitArgs base_args(kvattn_t h, uint32_t layer, uint32_t W, const float *q) {
     a.sec_kd = h->lay.sec_kd;
     a.sec_vc = h->lay.sec_vc;
     a.sec_vd = h->lay.sec_vd;
+    a.k_type = h->p.k_type;
+    a.v_type = h->p.v_type;
     a.qscale = h->qscale;
     a.q = q;
     a.part_o = h->part_o();
@@ -534,14 +549,14 @@ int attend(kvattn_t h, uint32_t layer, const float *q, uint32_t W, float *out, b
 extern "C" {
 
 int kvattn_supported(uint32_t k_type, uint32_t v_type, uint32_t head_dim) {
-    return k_type == KVATTN_TYPE_Q8_0 && v_type == KVATTN_TYPE_Q4_0 && head_dim == kHeadDim;
+    return pair_supported(k_type, v_type) && head_dim == kHeadDim;
 }
 
 size_t kvattn_page_bytes(const kvattn_params *params) {
     kvattn_params p;
     std::string why;
     if (!read_params(params, &p) || check_params(p, why) != KVATTN_OK) return 0;
-    return page_layout(p.n_kv_heads, p.page_tokens).page_bytes;
+    return page_layout(p).page_bytes;
 }
 
 size_t kvattn_workspace_bytes(const kvattn_params *params) {
@@ -560,7 +575,7 @@ int kvattn_create(const kvattn_params *params, void *d_pool, size_t pool_bytes, 
     std::string why;
     int rc = check_params(p, why);
     if (rc) return fail(nullptr, rc, "%s", why.c_str());
-    const Layout lay = page_layout(p.n_kv_heads, p.page_tokens);
+    const Layout lay = page_layout(p);
     const WsLayout ws = workspace_layout(p);
     if (p.n_pool_pages && !d_pool) return fail(nullptr, KVATTN_E_ARG, "null pool with n_pool_pages > 0");
     if (p.n_ring_slots && !d_ring) return fail(nullptr, KVATTN_E_ARG, "null ring with n_ring_slots > 0");
@@ -763,6 +778,8 @@ int kvattn_append(kvattn_t h, uint32_t layer, const float *d_k, const float *d_v
     w.sec_kd = h->lay.sec_kd;
     w.sec_vc = h->lay.sec_vc;
     w.sec_vd = h->lay.sec_vd;
+    w.k_type = h->p.k_type;
+    w.v_type = h->p.v_type;
     HIP_TRY(h, kvattn_launch_writer(w, h->compute));
     if (h_publish) {
         const size_t pb = h->lay.page_bytes;

@@ -1,5 +1,7 @@
 // split_kernel.hip -- the split-KV kernel for calls with up to 32 rows per KV
 // head (decode, verify) and the log-sum-exp merge of the split partials.
+#include <type_traits>
+
 #include "kernels_common.h"
 
 namespace kvattn_dev {
@@ -13,24 +15,33 @@ namespace kvattn_dev {
 // Each wave streams its chunks through its own LDS ring and overlaps chunk
 // i's Q.K^T with chunk i-1's P.V, whose operands it carries over.
 // ---------------------------------------------------------------------------
-// Shape per row-tile count: one tile (<= 16 rows per KV head) needs few
-// registers, so 12 waves (three per SIMD) with two-stage rings; two tiles
-// need about 250 registers, so 8 waves with three-stage rings.  Both fill
-// 159,744 bytes of LDS.
-template <int NT>
+// Shape per row-tile count and element-type pair, each filling most of the
+// 160 KiB of LDS with chunk rings: Q8_0 K / Q4_0 V and Q4_0 / Q4_0 with one
+// tile (<= 16 rows per KV head) need few registers, so 12 waves (three per
+// SIMD) with two-stage rings; two tiles need about 250 registers, so 8 waves
+// with three-stage rings.  The larger Q8_0 / Q8_0 chunks take 8 waves with
+// two stages, F16 / F16 chunks (16 KiB) 4 waves with two stages.
+template <int NT, int KT, int VT>
 struct SplitCfg {
-    static constexpr int waves = NT == 1 ? 12 : 8;
-    static constexpr int stages = NT == 1 ? 2 : 3;
-    static constexpr int ring_bytes = stages * kChunkBytes;
-    static constexpr int lds_bytes = waves * ring_bytes;
+    using C = Chunk<KT, VT>;
+    static constexpr bool big = C::bytes > 8192;
+    static constexpr int waves = C::bytes > 12288 ? 4 : (NT == 1 && !big) ? 12 : 8;
+    static constexpr int stages = (NT == 1 || big) ? 2 : 3;
+    static constexpr int ring_bytes = stages * C::bytes;
+    // the combine after the loop reuses the rings: per wave and row m, l and
+    // a padded 132-float accumulator row
+    static constexpr int combine_bytes = waves * 16 * NT * (2 + 132) * 4;
+    static constexpr int lds_bytes = waves * ring_bytes > combine_bytes ? waves * ring_bytes : combine_bytes;
+    static_assert(lds_bytes <= 163840, "LDS budget");
 };
 
-template <int NT>
-__global__ __launch_bounds__(64 * SplitCfg<NT>::waves, 1) void split_kernel(const SplitArgs a) {
-    constexpr int kSplitWaves = SplitCfg<NT>::waves;
-    constexpr int kStages = SplitCfg<NT>::stages;
-    constexpr int kWaveRingBytes = SplitCfg<NT>::ring_bytes;
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // rings; reused by the combine and merge
+template <int NT, int KT, int VT>
+__global__ __launch_bounds__((64 * SplitCfg<NT, KT, VT>::waves), 1) void split_kernel(const SplitArgs a) {
+    using C = Chunk<KT, VT>;
+    constexpr int kSplitWaves = SplitCfg<NT, KT, VT>::waves;
+    constexpr int kStages = SplitCfg<NT, KT, VT>::stages;
+    constexpr int kWaveRingBytes = SplitCfg<NT, KT, VT>::ring_bytes;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // rings; reused by the combine
 
     const int lane = threadIdx.x & 63;
     // wave index, made visibly uniform so chunk bookkeeping stays scalar
@@ -66,7 +77,7 @@ __global__ __launch_bounds__(64 * SplitCfg<NT>::waves, 1) void split_kernel(cons
     auto issue = [&](uint32_t k, uint32_t entry, uint32_t stage) {
         const uint32_t chunk = first + kSplitWaves * k;
         const uint32_t jj0 = (chunk - (chunk / cpp) * cpp) << 5;
-        issue_chunk(a, page_base(a, entry), kvh, jj0, lane, ring_lds + stage * kChunkBytes);
+        issue_chunk<KT, VT>(a, page_base(a, entry), kvh, jj0, lane, ring_lds + stage * C::bytes);
     };
 
     // ---- query loads and the first page entries, one round trip together;
@@ -126,8 +137,8 @@ __global__ __launch_bounds__(64 * SplitCfg<NT>::waves, 1) void split_kernel(cons
     uint32_t entry_next = entry0[kStages - 1];
 
     if (n_local > 0) {
-        uint32_t pv_vq[8];
-        half8 pv_pf[NT][4];
+        uint32_t pv_vq[C::vw];
+        half8 pv_pf[NT][C::pf_blocks];
         uint32_t stage = 0;
         for (uint32_t k = 0; k < n_local; k++) {
             // refill the buffer chunk k - 1 used (its reads are complete)
@@ -136,24 +147,29 @@ __global__ __launch_bounds__(64 * SplitCfg<NT>::waves, 1) void split_kernel(cons
                 issue(k + kStages - 1, entry_next, stage == 0 ? kStages - 1 : stage - 1);
                 if (k + kStages < n_local) entry_next = table_at(a.page_table, chunk_page(k + kStages));
             }
-            wait_chunk<kStages>(min((uint32_t)(kStages - 1), n_local - 1 - k));
-            const uint8_t *stg = ring + stage * kChunkBytes;
+            wait_chunk<kStages, C::dma>(min((uint32_t)(kStages - 1), n_local - 1 - k));
+            uint8_t *stg = ring + stage * C::bytes;
             const uint32_t c = first + kSplitWaves * k;
-            uint32_t kq[16], kd[16], vd[16];
+            const bool tail = 32 * c + 32 > a.n_tokens;  // chunk reaches into page padding
+            uint32_t kq[C::kw], kd[16], vd[16];
             float s[NT][8];
-            read_kcodes(stg, lane, kq);
-            read_kscales(stg, grp, kd);
-            chunk_scores<NT>(st, kq, kd, s);
+            read_kcodes<KT, VT>(stg, lane, kq);
+            if constexpr (C::kblk) read_kscales<KT, VT>(stg, grp, kd);
+            chunk_scores<NT, KT>(st, kq, kd, s);
             if (c >= clean_end) mask_scores<NT>(st, 32 * c, grp, s);
-            if (k > 0) chunk_pv<NT>(st, pv_vq, pv_pf);
-            if (32 * c + 32 > a.n_tokens) sanitize_vscales(ring + stage * kChunkBytes, lane, a.n_tokens - 32 * c);
-            read_vscales(stg, grp, vd);
+            if (k > 0) chunk_pv<NT, VT>(st, pv_vq, pv_pf);
+            if constexpr (C::vblk) {
+                if (tail) sanitize_vscales<KT, VT>(stg, lane, a.n_tokens - 32 * c);
+                read_vscales<KT, VT>(stg, grp, vd);
+            }
 #pragma unroll
-            for (int t = 0; t < NT; t++) chunk_probs(st[t], s[t], vd, pv_pf[t]);
-            read_vcodes(stg, lane, pv_vq);
+            for (int t = 0; t < NT; t++) chunk_probs<VT>(st[t], s[t], vd, pv_pf[t]);
+            read_vcodes<KT, VT>(stg, lane, pv_vq);
+            if constexpr (!C::vblk)
+                if (tail) clear_padding_vcodes<KT, VT>(pv_vq, grp, a.n_tokens - 32 * c);
             stage = stage == kStages - 1 ? 0 : stage + 1;
         }
-        chunk_pv<NT>(st, pv_vq, pv_pf);
+        chunk_pv<NT, VT>(st, pv_vq, pv_pf);
     }
 
     // ---- combine the waves (fixed wave order) and write the partials; the
@@ -338,19 +354,55 @@ __global__ __launch_bounds__(128 * U) void merge_kernel(const MergeArgs a) {
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-size_t kvattn_split_smem_bytes(int rt) {
-    return rt == 1 ? (size_t)kvattn_dev::SplitCfg<1>::lds_bytes : (size_t)kvattn_dev::SplitCfg<2>::lds_bytes;
+namespace {
+
+// Calls f(kernel, waves, lds bytes) with the split kernel of row tiles rt and
+// the element-type pair; false for an unsupported pair.
+template <class F>
+bool with_split_kernel(int rt, uint32_t kt, uint32_t vt, F f) {
+    using namespace kvattn_dev;
+    auto pick = [&](auto nt, auto ktc, auto vtc) {
+        constexpr int NT = decltype(nt)::value, KT = decltype(ktc)::value, VT = decltype(vtc)::value;
+        using Cfg = SplitCfg<NT, KT, VT>;
+        f(&split_kernel<NT, KT, VT>, Cfg::waves, (uint32_t)Cfg::lds_bytes);
+        return true;
+    };
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using F16 = std::integral_constant<int, kTypeF16>;
+    using Q4 = std::integral_constant<int, kTypeQ4_0>;
+    using Q8 = std::integral_constant<int, kTypeQ8_0>;
+    if (kt == kTypeQ8_0 && vt == kTypeQ4_0) return rt == 1 ? pick(I1{}, Q8{}, Q4{}) : pick(I2{}, Q8{}, Q4{});
+    if (kt == kTypeQ8_0 && vt == kTypeQ8_0) return rt == 1 ? pick(I1{}, Q8{}, Q8{}) : pick(I2{}, Q8{}, Q8{});
+    if (kt == kTypeQ4_0 && vt == kTypeQ4_0) return rt == 1 ? pick(I1{}, Q4{}, Q4{}) : pick(I2{}, Q4{}, Q4{});
+    if (kt == kTypeF16 && vt == kTypeF16) return rt == 1 ? pick(I1{}, F16{}, F16{}) : pick(I2{}, F16{}, F16{});
+    return false;
+}
+
+}  // namespace
+
+size_t kvattn_split_smem_bytes(int rt, uint32_t k_type, uint32_t v_type) {
+    size_t bytes = 0;
+    with_split_kernel(rt, k_type, v_type, [&](auto, int, uint32_t lds) { bytes = lds; });
+    return bytes;
 }
 
 uint32_t kvattn_merge_max_splits() { return kvattn_dev::kMergeMaxSplits; }
 
 hipError_t kvattn_split_setup() {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kvattn_dev::split_kernel<1>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kvattn_split_smem_bytes(1));
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kvattn_dev::split_kernel<2>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kvattn_split_smem_bytes(2));
-    return e;
+    const uint32_t pairs[4][2] = {{kvattn_dev::kTypeQ8_0, kvattn_dev::kTypeQ4_0},
+                                  {kvattn_dev::kTypeQ8_0, kvattn_dev::kTypeQ8_0},
+                                  {kvattn_dev::kTypeQ4_0, kvattn_dev::kTypeQ4_0},
+                                  {kvattn_dev::kTypeF16, kvattn_dev::kTypeF16}};
+    hipError_t err = hipSuccess;
+    for (const auto &pr : pairs)
+        for (int rt = 1; rt <= 2; rt++)
+            with_split_kernel(rt, pr[0], pr[1], [&](auto kern, int, uint32_t lds) {
+                if (err == hipSuccess)
+                    err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            });
+    return err;
 }
 
 // rt: row tiles of 16 per workgroup (1 or 2); n_row_blocks blocks of 16 * rt rows.
@@ -359,19 +411,14 @@ hipError_t kvattn_split_setup() {
 hipError_t kvattn_launch_split(const SplitArgs &a, uint32_t n_items, uint32_t n_row_blocks, int rt, hipStream_t s,
                                hipEvent_t ev_start, hipEvent_t ev_stop) {
     (void)hipGetLastError();  // clear a stale error so the check below reports this launch
-    dim3 grid(n_items, a.Hkv, n_row_blocks);
-    dim3 block(64 * (rt == 1 ? kvattn_dev::SplitCfg<1>::waves : kvattn_dev::SplitCfg<2>::waves));
-    const uint32_t smem = (uint32_t)kvattn_split_smem_bytes(rt);
-    if (ev_start) {
-        if (rt == 1)
-            hipExtLaunchKernelGGL(kvattn_dev::split_kernel<1>, grid, block, smem, s, ev_start, ev_stop, 0, a);
+    const dim3 grid(n_items, a.Hkv, n_row_blocks);
+    const bool ok = with_split_kernel(rt, a.k_type, a.v_type, [&](auto kern, int waves, uint32_t lds) {
+        if (ev_start)
+            hipExtLaunchKernelGGL(kern, grid, dim3(64 * waves), lds, s, ev_start, ev_stop, 0, a);
         else
-            hipExtLaunchKernelGGL(kvattn_dev::split_kernel<2>, grid, block, smem, s, ev_start, ev_stop, 0, a);
-    } else if (rt == 1) {
-        hipLaunchKernelGGL(kvattn_dev::split_kernel<1>, grid, block, smem, s, a);
-    } else {
-        hipLaunchKernelGGL(kvattn_dev::split_kernel<2>, grid, block, smem, s, a);
-    }
+            hipLaunchKernelGGL(kern, grid, dim3(64 * waves), lds, s, a);
+    });
+    if (!ok) return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

@@ -89,33 +89,62 @@ __device__ __forceinline__ half8 h8_mul(half8 x, uint4 sc) {
     return half8{x[0] * a.x, x[1] * a.y, x[2] * b.x, x[3] * b.y, x[4] * c.x, x[5] * c.y, x[6] * d.x, x[7] * d.y};
 }
 
-// Dequantise one staged raw chunk into the f16 view.  Threads 0..255: K
-// quarter q = t / 64 of lane l = t mod 64 (key tile q / 2, blocks 2 (q mod 2)
-// and +1); threads 256..511: V dwords 2h, 2h + 1 of lane l (value block h).
-// n_valid < 32 marks the chunk holding the end of the history: V' of keys at
-// or past it is zeroed (their scales are page padding).
+// Dequantise one staged raw chunk into the f16 view.  Threads 0..255: key
+// tile tt = q / 2 and blocks b0 = 2 (q mod 2), b0 + 1 of lane l (q = t / 64,
+// l = t mod 64); threads 256..511: value block h = (t - 256) / 64, dim tiles
+// 2h and 2h + 1 of lane l.  n_valid < 32 marks the chunk holding the end of
+// the history: V' of keys at or past it is zeroed (their codes and scales
+// are page padding).  F16 data are copied as they are.
+template <int KT, int VT>
 __device__ __forceinline__ void dequant_view(const uint8_t *raw, uint8_t *view, uint32_t n_valid) {
+    using C = Chunk<KT, VT>;
     const int t = threadIdx.x, l = t & 63;
     if (t < 256) {
         const int q = t >> 6, tt = q >> 1, b0 = 2 * (q & 1);
-        const uint4 w = *reinterpret_cast<const uint4 *>(raw + q * 1024 + l * 16);
-        const uint32_t key = 16 * tt + (l & 15);
-        const uint32_t sc = *reinterpret_cast<const uint32_t *>(raw + kOffKS + key * 8 + b0 * 2);
-        const half8 k0 = q8_to_half8(w.x, w.y), k1 = q8_to_half8(w.z, w.w);
-        const _Float16 d0 = bits_h2(sc).x, d1 = bits_h2(sc).y;
         half8 o0, o1;
+        if constexpr (KT == kTypeF16) {
+            o0 = *reinterpret_cast<const half8 *>(raw + tt * 4096 + b0 * 1024 + l * 16);
+            o1 = *reinterpret_cast<const half8 *>(raw + tt * 4096 + (b0 + 1) * 1024 + l * 16);
+        } else {
+            half8 k0, k1;
+            if constexpr (KT == kTypeQ8_0) {
+                const uint4 w = *reinterpret_cast<const uint4 *>(raw + q * 1024 + l * 16);
+                k0 = q8_to_half8(w.x, w.y);
+                k1 = q8_to_half8(w.z, w.w);
+            } else {
+                const uint2 w = *reinterpret_cast<const uint2 *>(raw + tt * 1024 + l * 16 + b0 * 4);
+                k0 = q4_to_half8(w.x);
+                k1 = q4_to_half8(w.y);
+            }
+            const uint32_t key = 16 * tt + (l & 15);
+            const uint32_t sc = *reinterpret_cast<const uint32_t *>(raw + C::off_ks + key * 8 + b0 * 2);
+            const _Float16 d0 = bits_h2(sc).x, d1 = bits_h2(sc).y;
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            o0[i] = k0[i] * d0;
-            o1[i] = k1[i] * d1;
+            for (int i = 0; i < 8; i++) {
+                o0[i] = k0[i] * d0;
+                o1[i] = k1[i] * d1;
+            }
         }
         *reinterpret_cast<half8 *>(view + ((tt * 4 + b0) * 64 + l) * 16) = o0;
         *reinterpret_cast<half8 *>(view + ((tt * 4 + b0 + 1) * 64 + l) * 16) = o1;
     } else {
         const int h = (t - 256) >> 6, g = l >> 4;
-        const uint2 w = *reinterpret_cast<const uint2 *>(raw + kOffV + (h >> 1) * 1024 + l * 16 + (h & 1) * 8);
-        const uint4 sc = *reinterpret_cast<const uint4 *>(raw + kOffVS + (h * 4 + g) * 16);
-        half8 v0 = h8_mul(q4_to_half8(w.x), sc), v1 = h8_mul(q4_to_half8(w.y), sc);
+        half8 v0, v1;
+        if constexpr (VT == kTypeF16) {
+            v0 = *reinterpret_cast<const half8 *>(raw + C::off_v + (2 * h) * 1024 + l * 16);
+            v1 = *reinterpret_cast<const half8 *>(raw + C::off_v + (2 * h + 1) * 1024 + l * 16);
+        } else {
+            const uint4 sc = *reinterpret_cast<const uint4 *>(raw + C::off_vs + (h * 4 + g) * 16);
+            if constexpr (VT == kTypeQ4_0) {
+                const uint2 w = *reinterpret_cast<const uint2 *>(raw + C::off_v + (h >> 1) * 1024 + l * 16 + (h & 1) * 8);
+                v0 = h8_mul(q4_to_half8(w.x), sc);
+                v1 = h8_mul(q4_to_half8(w.y), sc);
+            } else {
+                const uint4 w = *reinterpret_cast<const uint4 *>(raw + C::off_v + h * 1024 + l * 16);
+                v0 = h8_mul(q8_to_half8(w.x, w.y), sc);
+                v1 = h8_mul(q8_to_half8(w.z, w.w), sc);
+            }
+        }
         if (n_valid < 32) {
 #pragma unroll
             for (int j = 0; j < 8; j++) {
@@ -131,9 +160,13 @@ __device__ __forceinline__ void dequant_view(const uint8_t *raw, uint8_t *view, 
     }
 }
 
+template <int KT, int VT>
 __global__ __launch_bounds__(512, 1) void wide_kernel(const SplitArgs a) {
+    using C = Chunk<KT, VT>;
     constexpr int NT = 2;
-    __shared__ __attribute__((aligned(16))) uint8_t raw_ring[kStages][kChunkBytes];
+    // a chunk's loads, spread over the 8 waves: wave w issues loads w and w + 8
+    constexpr int kLoadsMax = (C::dma + 7) / 8;
+    __shared__ __attribute__((aligned(16))) uint8_t raw_ring[kStages][C::bytes];
     __shared__ __attribute__((aligned(16))) uint8_t views[2][kViewBytes];
 
     const int lane = threadIdx.x & 63;
@@ -153,25 +186,20 @@ __global__ __launch_bounds__(512, 1) void wide_kernel(const SplitArgs a) {
     const uint32_t clean_end = (a.n_tokens - a.W + 1) >> 5;
     const bool active = wave_row0 < rows_kv;  // wave has rows to compute
 
-    // this wave's share of a chunk's seven direct-to-LDS loads
+    // this wave's share of a chunk's direct-to-LDS loads
+    const uint32_t my_loads = (uint32_t)(wave < C::dma) + (uint32_t)(wave + 8 < C::dma);
     auto issue = [&](uint32_t p) {
-        if (wave >= kDmaPerChunk) return;
+        if (my_loads == 0) return;
         const uint32_t chunk = c_begin + p;
         const uint32_t page = chunk / cpp;
         const uint32_t jj0 = (chunk - page * cpp) << 5;
         const uint8_t *base = resolve_page(a, page);
-        const size_t kv = (size_t)kvh * a.T + jj0;
         const uint32_t dst = lds_addr(raw_ring[p % kStages]);
-        if (wave < 4) {
-            dma16(base + kv * 128 + lane * 16 + 1024 * wave, dst + 1024 * wave);
-        } else if (wave < 6) {
-            dma16(base + a.sec_vc + kv * 64 + lane * 16 + 1024 * (wave - 4), dst + kOffV + 1024 * (wave - 4));
-        } else if (lane < 32) {
-            const uint8_t *sp = lane < 16 ? base + a.sec_kd + kv * 8 + lane * 16
-                                          : base + a.sec_vd + (size_t)kvh * a.T * 8 + (size_t)(jj0 >> 5) * 256 + (lane - 16) * 16;
-            dma16(sp, dst + kOffKS);
-        }
+#pragma unroll
+        for (int i = 0; i < kLoadsMax; i++)
+            if (wave + 8 * i < C::dma) issue_chunk_part<KT, VT>(a, base, kvh, jj0, lane, dst, wave + 8 * i);
     };
+    static_assert(2 * kLoadsMax <= 4, "wait_vmcnt_upto range");
     auto n_valid_of = [&](uint32_t p) {
         const uint32_t c = c_begin + p;
         return 32 * c + 32 > a.n_tokens ? a.n_tokens - 32 * c : 32u;
@@ -217,16 +245,16 @@ __global__ __launch_bounds__(512, 1) void wide_kernel(const SplitArgs a) {
 #pragma unroll
     for (uint32_t p = 0; p < kStages; p++)
         if (p < n) issue(p);
-    wait_chunk_wide(min(n - 1, 2u));
+    wait_vmcnt_upto(min(n - 1, 2u) * my_loads);
     __syncthreads();
-    dequant_view(raw_ring[0], views[0], n_valid_of(0));
+    dequant_view<KT, VT>(raw_ring[0], views[0], n_valid_of(0));
 
     for (uint32_t p = 0; p < n; p++) {
         // raw chunk p + 1 landed (every wave waited for its own share)
-        if (p + 1 < n) wait_chunk_wide(min(n - 2 - p, 1u));
+        if (p + 1 < n) wait_vmcnt_upto(min(n - 2 - p, 1u) * my_loads);
         __syncthreads();
         if (p + kStages < n) issue(p + kStages);
-        if (p + 1 < n) dequant_view(raw_ring[(p + 1) % kStages], views[(p + 1) & 1], n_valid_of(p + 1));
+        if (p + 1 < n) dequant_view<KT, VT>(raw_ring[(p + 1) % kStages], views[(p + 1) & 1], n_valid_of(p + 1));
         if (active) {
             const uint8_t *view = views[p & 1];
             const uint32_t c = c_begin + p;
@@ -270,12 +298,25 @@ __global__ __launch_bounds__(512, 1) void wide_kernel(const SplitArgs a) {
 // ---------------------------------------------------------------------------
 hipError_t kvattn_launch_wide(const SplitArgs &a, uint32_t n_splits, uint32_t n_row_blocks, hipStream_t s,
                               hipEvent_t ev_start, hipEvent_t ev_stop) {
+    using namespace kvattn_dev;
     (void)hipGetLastError();
-    dim3 grid(n_splits, a.Hkv, n_row_blocks), block(512);
-    if (ev_start)
-        hipExtLaunchKernelGGL(kvattn_dev::wide_kernel, grid, block, 0, s, ev_start, ev_stop, 0, a);
+    const dim3 grid(n_splits, a.Hkv, n_row_blocks), block(512);
+    auto go = [&](auto kern) {
+        if (ev_start)
+            hipExtLaunchKernelGGL(kern, grid, block, 0, s, ev_start, ev_stop, 0, a);
+        else
+            hipLaunchKernelGGL(kern, grid, block, 0, s, a);
+    };
+    if (a.k_type == kTypeQ8_0 && a.v_type == kTypeQ4_0)
+        go(wide_kernel<kTypeQ8_0, kTypeQ4_0>);
+    else if (a.k_type == kTypeQ8_0 && a.v_type == kTypeQ8_0)
+        go(wide_kernel<kTypeQ8_0, kTypeQ8_0>);
+    else if (a.k_type == kTypeQ4_0 && a.v_type == kTypeQ4_0)
+        go(wide_kernel<kTypeQ4_0, kTypeQ4_0>);
+    else if (a.k_type == kTypeF16 && a.v_type == kTypeF16)
+        go(wide_kernel<kTypeF16, kTypeF16>);
     else
-        hipLaunchKernelGGL(kvattn_dev::wide_kernel, grid, block, 0, s, a);
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libkvattn.so")
 OK, E_ARG, E_UNSUPPORTED, E_RANGE, E_PLAN, E_NOSPACE, E_STATE, E_HIP = 0, -1, -2, -3, -4, -5, -6, -7
 STATUS_NAMES = {0: "OK", -1: "E_ARG", -2: "E_UNSUPPORTED", -3: "E_RANGE", -4: "E_PLAN", -5: "E_NOSPACE",
                 -6: "E_STATE", -7: "E_HIP"}
-TYPE_Q4_0, TYPE_Q8_0 = 2, 8
+TYPE_F16, TYPE_Q4_0, TYPE_Q8_0 = 1, 2, 8
 PT_RING_FLAG = 0x80000000
 PT_HOST = 0xFFFFFFFF
 HEAD_DIM = 128

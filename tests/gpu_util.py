@@ -21,9 +21,10 @@ def say(*a):
 
 
 def handle(Hq, Hkv, n_pool, max_pages, max_rows, n_ring=0, split_pages=0, chunk_slots=0, n_layers=1,
-           page_tokens=256):
+           page_tokens=256, k_type=kv.TYPE_Q8_0, v_type=kv.TYPE_Q4_0):
     p = kv.make_params(n_layers, Hq, Hkv, n_pool, max_pages, max_rows, n_ring_slots=n_ring,
-                       split_pages=split_pages, chunk_slots=chunk_slots, page_tokens=page_tokens)
+                       split_pages=split_pages, chunk_slots=chunk_slots, page_tokens=page_tokens,
+                       k_type=k_type, v_type=v_type)
     return kv.allocate(p)
 
 
@@ -49,7 +50,8 @@ def place(h, layer, kvl, table, history=None, page_tokens=256):
 def oracle_out(kvl, q, Hq, Hkv, rows=None, page_tokens=256):
     n = kvl.pages.shape[0]
     out, _ = oracle.attend_paged(np.arange(n, dtype=np.uint32), kvl.kc.shape[0], page_tokens, Hq, Hkv,
-                                 q.cpu().numpy(), inputs.scale_for(), pool=kvl.pages.cpu().numpy(), rows=rows)
+                                 q.cpu().numpy(), inputs.scale_for(), pool=kvl.pages.cpu().numpy(), rows=rows,
+                                 k_type=kvl.k_type, v_type=kvl.v_type)
     return out
 
 

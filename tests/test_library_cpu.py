@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 
 import long_context_attention_amd as kv
+import oracle
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -30,7 +31,14 @@ def test_library_exports_every_declared_symbol():
 
 def test_supported_and_sizes():
     assert kv.supported()
-    assert not kv.supported(kv.TYPE_Q8_0, kv.TYPE_Q8_0)
+    for pair in [(kv.TYPE_Q8_0, kv.TYPE_Q8_0), (kv.TYPE_Q4_0, kv.TYPE_Q4_0), (kv.TYPE_F16, kv.TYPE_F16)]:
+        assert kv.supported(*pair)
+        q = kv.make_params(4, 40, 8, 16, 16, 6, k_type=pair[0], v_type=pair[1])
+        assert kv.page_bytes(q) == oracle.page_bytes(8, 256, *pair) > 0
+        assert kv.workspace_bytes(q) > 0
+    for pair in [(kv.TYPE_Q4_0, kv.TYPE_Q8_0), (kv.TYPE_F16, kv.TYPE_Q4_0), (kv.TYPE_Q8_0, kv.TYPE_F16), (3, 3)]:
+        assert not kv.supported(*pair)
+        assert kv.page_bytes(kv.make_params(4, 40, 8, 16, 16, 6, k_type=pair[0], v_type=pair[1])) == 0
     assert not kv.supported(kv.TYPE_Q8_0, kv.TYPE_Q4_0, 64)
     p = kv.make_params(64, 40, 8, 10240, 160, 6)
     assert kv.page_bytes(p) == 425984
@@ -59,7 +67,7 @@ def create_status(params, pool=1 << 40, ring=0, ws=None, null_ws=False, null_out
 def test_create_rejections():
     p = kv.make_params(2, 40, 8, 4, 10, 6)
     assert create_status(p, null_out=True) == kv.E_ARG
-    assert create_status(kv.make_params(2, 40, 8, 4, 10, 6, k_type=kv.TYPE_Q4_0)) == kv.E_UNSUPPORTED
+    assert create_status(kv.make_params(2, 40, 8, 4, 10, 6, k_type=kv.TYPE_Q4_0, v_type=kv.TYPE_Q8_0)) == kv.E_UNSUPPORTED
     assert "Q8_0" in kv.global_error()
     assert create_status(kv.make_params(2, 40, 8, 4, 10, 6, head_dim=96)) == kv.E_UNSUPPORTED
     assert create_status(kv.make_params(2, 40, 6, 4, 10, 6)) == kv.E_UNSUPPORTED   # 40 % 6 != 0
