@@ -37,6 +37,9 @@ METRIC = "attn tokens/s and quantized-KV GB/s (% of HBM peak) at 40k-256k ctx, 1
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, vendor figure
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix, vendor figure
 BYTES_PER_TOKEN_HEAD = 208    # Q8_0 K (4 x 34 B) + Q4_0 V (4 x 18 B) per token per KV head
+# K/V element-type pairs: name -> (k_type, v_type, label, bytes per token per KV head)
+KV_TYPES = {"q8_0-q4_0": (8, 2, "Q8_0 K / Q4_0 V", 208), "q8_0-q8_0": (8, 8, "Q8_0 K / Q8_0 V", 272),
+            "q4_0-q4_0": (2, 2, "Q4_0 K / Q4_0 V", 144), "f16-f16": (1, 1, "F16 K / F16 V", 512)}
 
 
 def log(*a):
@@ -61,13 +64,15 @@ def parse():
     ap.add_argument("--writer", action="store_true",
                     help="also time the KV writer: one captured graph of one kvattn_append of the step's rows per "
                          "layer (decode / verify workloads)")
+    ap.add_argument("--kv-types", choices=sorted(KV_TYPES), default="q8_0-q4_0",
+                    help="K/V element-type pair of the cache (default: the workloads' Q8_0 K / Q4_0 V)")
     ap.add_argument("--h2d-ceiling", action="store_true",
                     help="only measure the host-to-device ceiling (pinned copies) and print it as JSON")
     return ap.parse_args()
 
 
 # --------------------------------------------------------------------------- setup
-def build(w, width, n_layers, torch, kv, inputs):
+def build(w, width, n_layers, torch, kv, inputs, types=KV_TYPES["q8_0-q4_0"]):
     """Create the handle and place every layer's pages.  Returns (handle,
     queries, outputs, call kind, rows, host histories)."""
     dev = "cuda"
@@ -79,14 +84,14 @@ def build(w, width, n_layers, torch, kv, inputs):
     compute = torch.cuda.Stream()
     copy = torch.cuda.Stream()
     params = kv.make_params(n_layers, w.n_q_heads, w.n_kv_heads, n_pool, n, max(rows, 1),
-                            n_ring_slots=w.ring_slots)
+                            n_ring_slots=w.ring_slots, k_type=types[0], v_type=types[1])
     h = kv.allocate(params, compute_stream=compute, copy_stream=copy)
     pb = kv.page_bytes(params)
     pool = h.pool.view(n_pool, pb)
     perm = np.random.default_rng(inputs.derive_seed(inputs.BASE_SEED, w.wid, 0, inputs.T_PERM)).permutation(n_pool)
     hist = []
     for l in range(n_layers):
-        kvl = inputs.draw_layer(w.n_tokens, w.n_kv_heads, l, w.wid, device=dev)
+        kvl = inputs.draw_layer(w.n_tokens, w.n_kv_heads, l, w.wid, device=dev, k_type=types[0], v_type=types[1])
         table = np.empty(n, dtype=np.uint32)
         if streamed:
             res = inputs.resident_subset(n, n_res, l, w.wid)
@@ -148,7 +153,7 @@ def measured_traffic(workload, rows):
 
 
 # --------------------------------------------------------------------------- KV writer
-def time_writer(h, w, rows, n_layers, steps, torch, inputs, stream):
+def time_writer(h, w, rows, n_layers, steps, torch, inputs, stream, bytes_per_token_head=BYTES_PER_TOKEN_HEAD):
     """Each layer's history is shortened by two steps' rows, then one pass of
     kvattn_append (the step's rows, one call per layer) warms up and one is
     captured; replays of the captured pass rewrite the same positions, the
@@ -177,7 +182,7 @@ def time_writer(h, w, rows, n_layers, steps, torch, inputs, stream):
         e1.record(stream)
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / (steps * n_layers)
-    bytes_per_call = rows * w.n_kv_heads * BYTES_PER_TOKEN_HEAD
+    bytes_per_call = rows * w.n_kv_heads * bytes_per_token_head
     return {"us_per_call": round(us, 3), "rows_per_call": rows,
             "quantised_bytes_per_call": bytes_per_call,
             "timing": "HIP events around replays of a captured pass of one append per layer"}
@@ -213,7 +218,7 @@ def h2d_ceiling(torch, mb=436, reps=3):
 
 
 # --------------------------------------------------------------------------- cpu baseline
-def cpu_baseline(w, rows, kind, inputs, budget_s=10.0):
+def cpu_baseline(w, rows, kind, inputs, budget_s=10.0, types=KV_TYPES["q8_0-q4_0"]):
     """The oracle (fp64 C, OpenMP over (row, head)) on a bounded sample of the
     same workload: whole layers (a seeded sample of rows for prefill) until
     about budget_s seconds of CPU work, scaled to tokens/s of the full
@@ -228,25 +233,28 @@ def cpu_baseline(w, rows, kind, inputs, budget_s=10.0):
         sample_rows = list(range(rows))
     spent, layers = 0.0, 0
     while layers < w.n_layers and spent < budget_s:
-        kvl = inputs.draw_layer(w.n_tokens, w.n_kv_heads, layers, w.wid, device="cuda")
+        kvl = inputs.draw_layer(w.n_tokens, w.n_kv_heads, layers, w.wid, device="cuda", k_type=types[0],
+                                v_type=types[1])
         pages = kvl.pages.cpu().numpy()
         q = inputs.draw_queries(rows, w.n_q_heads, layers, w.wid, device="cuda").cpu().numpy()
         del kvl
         t0 = time.perf_counter()
         oracle.attend_paged(np.arange(pages.shape[0], dtype=np.uint32), w.n_tokens, 256, w.n_q_heads,
-                            w.n_kv_heads, q, inputs.scale_for(), pool=pages, rows=sample_rows, n_threads=threads)
+                            w.n_kv_heads, q, inputs.scale_for(), pool=pages, rows=sample_rows, n_threads=threads,
+                            k_type=types[0], v_type=types[1])
         spent += time.perf_counter() - t0
         layers += 1
     # full pass = n_layers layers x rows rows; sample = `layers` layers x len(sample_rows) rows
     pass_s = spent * (w.n_layers / layers) * rows / len(sample_rows)
     # one core: the first sampled row of one layer (the oracle is linear in rows and layers)
-    kvl = inputs.draw_layer(w.n_tokens, w.n_kv_heads, 0, w.wid, device="cuda")
+    kvl = inputs.draw_layer(w.n_tokens, w.n_kv_heads, 0, w.wid, device="cuda", k_type=types[0], v_type=types[1])
     pages = kvl.pages.cpu().numpy()
     q = inputs.draw_queries(rows, w.n_q_heads, 0, w.wid, device="cuda").cpu().numpy()
     del kvl
     t0 = time.perf_counter()
     oracle.attend_paged(np.arange(pages.shape[0], dtype=np.uint32), w.n_tokens, 256, w.n_q_heads, w.n_kv_heads, q,
-                        inputs.scale_for(), pool=pages, rows=sample_rows[:1], n_threads=1)
+                        inputs.scale_for(), pool=pages, rows=sample_rows[:1], n_threads=1, k_type=types[0],
+                        v_type=types[1])
     one = time.perf_counter() - t0
     one_pass_s = one * w.n_layers * rows
     return {"value": rows / pass_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
@@ -282,7 +290,9 @@ def main():
         sys.exit(2)
     log(f"bench: workload {w.name}, {n_layers} layers, mode {mode}: building inputs")
     t0 = time.perf_counter()
-    h, qs, outs, kind, rows, hist = build(w, args.width, n_layers, torch, kv, inputs)
+    types = KV_TYPES[args.kv_types]
+    default_types = args.kv_types == "q8_0-q4_0"
+    h, qs, outs, kind, rows, hist = build(w, args.width, n_layers, torch, kv, inputs, types)
     log(f"bench: inputs ready in {time.perf_counter() - t0:.1f} s; {kind} rows={rows}")
     stream = h.compute_stream
 
@@ -353,13 +363,13 @@ def main():
 
     writer = None
     if args.writer and kind != "prefill" and not streamed:
-        writer = time_writer(h, w, rows, n_layers, args.steps, torch, inputs, stream)
+        writer = time_writer(h, w, rows, n_layers, args.steps, torch, inputs, stream, types[3])
 
     # ---- figures
     tokens_per_step = rows
     value = tokens_per_step / (ms_per_step / 1e3)
     keys_per_layer = w.n_tokens  # every key of the history is read once per layer (all rows share it)
-    kv_bytes_layer = keys_per_layer * w.n_kv_heads * BYTES_PER_TOKEN_HEAD
+    kv_bytes_layer = keys_per_layer * w.n_kv_heads * types[3]
     kv_gbps = kv_bytes_layer * n_layers / (ms_per_step / 1e3) / 1e9
     flops_layer = 4.0 * w.n_q_heads * 128 * sum(w.n_tokens - rows + r + 1 for r in range(rows))
     result = {
@@ -377,7 +387,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "layers": n_layers, "context": w.n_tokens, "page_tokens": 256,
                    "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": 128, "rows": rows,
-                   "kv_types": "Q8_0 K / Q4_0 V", "mode": mode,
+                   "kv_types": types[2], "mode": mode,
                    "resident_fraction": w.resident_fraction, "ring_slots": w.ring_slots},
         "layers_per_s": round(n_layers / (ms_per_step / 1e3), 1),
         "kv_gbps": round(kv_gbps, 1),
@@ -390,7 +400,7 @@ def main():
     }
     if streamed:
         n_str = w.n_pages - w.n_resident
-        h2d = n_str * w.page_bytes * n_layers / (ms_per_step / 1e3) / 1e9
+        h2d = n_str * 256 * w.n_kv_heads * types[3] * n_layers / (ms_per_step / 1e3) / 1e9
         result["h2d_gbps"] = round(h2d, 2)
     if streamed:
         # the pass is bound by the host link: report it against the measured ceiling
@@ -411,7 +421,7 @@ def main():
         else:
             result["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                                   "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                                  "traffic": measured_traffic(w.name, rows)}
+                                  "traffic": measured_traffic(w.name, rows) if default_types else None}
             # the contraction runs on the matrix cores at every width: its rate
             tflops = flops_layer * n_layer_calls / (layer_ms / 1e3) / 1e12
             result["mfma_tflops"] = round(tflops, 2)
@@ -432,7 +442,7 @@ def main():
         result["copy_kernel_bytes"] = {"read": a.numel() * 4, "write": b.numel() * 4}
     if not args.no_cpu_baseline:
         log("bench: timing the oracle on a CPU sample")
-        result["cpu_baseline"] = cpu_baseline(w, rows, kind, inputs)
+        result["cpu_baseline"] = cpu_baseline(w, rows, kind, inputs, types=types)
     h.destroy()
     print(json.dumps(result), flush=True)
 
