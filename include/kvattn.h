@@ -1,6 +1,7 @@
 /*
  * kvattn.h -- exact attention over a block-paged KV cache with Q8_0 keys and
- * Q4_0 values, on AMD Instinct MI355X (gfx950).
+ * Q4_0 values (and the Q8_0/Q8_0, Q4_0/Q4_0 and F16/F16 pairs), on AMD
+ * Instinct MI355X (gfx950).
  *
  * What the library computes: for each query row, softmax attention over the
  * complete, logically ordered KV history of a layer.  Where a page lives
@@ -121,7 +122,8 @@ typedef struct kvattn_params {
     uint32_t chunk_slots;         /* ring slots per streamed chunk; 0 => 16 (clamped to the ring) */
 } kvattn_params;
 
-/* 1 if the K/V type pair and head_dim are implemented, else 0. */
+/* 1 if the K/V type pair and head_dim are implemented (the four pairs above,
+ * head_dim 128), else 0. */
 int kvattn_supported(uint32_t k_type, uint32_t v_type, uint32_t head_dim);
 
 /* Bytes of one page (0 if the parameters are invalid). */
