@@ -66,6 +66,8 @@ def parse():
                          "layer (decode / verify workloads)")
     ap.add_argument("--split-pages", type=int, default=0,
                     help="pages per split for calls of <= 32 rows per KV head (0: the library's choice)")
+    ap.add_argument("--deterministic", action="store_true",
+                    help="fixed chunk order inside splits (same bits every call) instead of waves claiming chunks")
     ap.add_argument("--kv-types", choices=sorted(KV_TYPES), default="q8_0-q4_0",
                     help="K/V element-type pair of the cache (default: the workloads' Q8_0 K / Q4_0 V)")
     ap.add_argument("--h2d-ceiling", action="store_true",
@@ -74,7 +76,7 @@ def parse():
 
 
 # --------------------------------------------------------------------------- setup
-def build(w, width, n_layers, torch, kv, inputs, types=KV_TYPES["q8_0-q4_0"], split_pages=0):
+def build(w, width, n_layers, torch, kv, inputs, types=KV_TYPES["q8_0-q4_0"], split_pages=0, deterministic=False):
     """Create the handle and place every layer's pages.  Returns (handle,
     queries, outputs, call kind, rows, host histories)."""
     dev = "cuda"
@@ -86,7 +88,8 @@ def build(w, width, n_layers, torch, kv, inputs, types=KV_TYPES["q8_0-q4_0"], sp
     compute = torch.cuda.Stream()
     copy = torch.cuda.Stream()
     params = kv.make_params(n_layers, w.n_q_heads, w.n_kv_heads, n_pool, n, max(rows, 1),
-                            n_ring_slots=w.ring_slots, k_type=types[0], v_type=types[1], split_pages=split_pages)
+                            n_ring_slots=w.ring_slots, k_type=types[0], v_type=types[1], split_pages=split_pages,
+                            deterministic=int(deterministic))
     h = kv.allocate(params, compute_stream=compute, copy_stream=copy)
     pb = kv.page_bytes(params)
     pool = h.pool.view(n_pool, pb)
@@ -294,7 +297,8 @@ def main():
     t0 = time.perf_counter()
     types = KV_TYPES[args.kv_types]
     default_types = args.kv_types == "q8_0-q4_0"
-    h, qs, outs, kind, rows, hist = build(w, args.width, n_layers, torch, kv, inputs, types, args.split_pages)
+    h, qs, outs, kind, rows, hist = build(w, args.width, n_layers, torch, kv, inputs, types, args.split_pages,
+                                          args.deterministic)
     log(f"bench: inputs ready in {time.perf_counter() - t0:.1f} s; {kind} rows={rows}")
     stream = h.compute_stream
 
@@ -390,6 +394,7 @@ def main():
         "config": {"workload": w.name, "layers": n_layers, "context": w.n_tokens, "page_tokens": 256,
                    "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": 128, "rows": rows,
                    "kv_types": types[2], "mode": mode, "split_pages": args.split_pages or "auto",
+                   "chunk_order": "static" if args.deterministic else "claimed in splits of >= 96 chunks, else static",
                    "resident_fraction": w.resident_fraction, "ring_slots": w.ring_slots},
         "layers_per_s": round(n_layers / (ms_per_step / 1e3), 1),
         "kv_gbps": round(kv_gbps, 1),

@@ -120,6 +120,13 @@ typedef struct kvattn_params {
     uint32_t split_pages;         /* pages per split for narrow calls (rows per KV head <= 32);
                                      0 => chosen from the page count and the CU count */
     uint32_t chunk_slots;         /* ring slots per streamed chunk; 0 => 16 (clamped to the ring) */
+    uint32_t deterministic;       /* 1 => every call gives the same bits for the same history and
+                                     queries (fixed chunk-to-wave order inside a split); 0 =>
+                                     narrow calls over resident pages with long splits (>= 96
+                                     chunks of 32 keys) let a split's waves claim chunks as their
+                                     buffers free up, which balances them but changes the
+                                     summation order from run to run (results stay within
+                                     rounding of each other) */
 } kvattn_params;
 
 /* 1 if the K/V type pair and head_dim are implemented (the four pairs above,

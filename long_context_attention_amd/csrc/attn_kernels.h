@@ -21,6 +21,7 @@ struct SplitArgs {
     size_t page_bytes;
     size_t sec_kd, sec_vc, sec_vd; // section offsets inside a page
     uint32_t k_type, v_type;      // element types (KVATTN_TYPE_*)
+    uint32_t dynamic_order;       // split kernel: waves claim chunks as buffers free (else static order)
     float qscale;                 // softmax_scale * log2(e)
     const float *q;               // [W][Hq][128]
     float *part_o;                // [splits][W*Hq][128]

@@ -153,7 +153,11 @@ constexpr int kStages = 3;  // raw-chunk ring of the wide kernel
 // 16 bytes per lane from g to LDS bytes [lds + 16 lane, +16).  m0 holds the
 // wave's LDS destination; one wait state separates its write from the load.
 __device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+    // the destination is wave-uniform; readfirstlane keeps it in an SGPR even
+    // where the compiler cannot prove that
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g),
+                 "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory", "m0");
 }
 #pragma clang diagnostic pop
 

@@ -27,6 +27,7 @@ namespace {
 constexpr uint32_t kHeadDim = 128;
 constexpr uint32_t kNarrowRows = 32;      // rows per KV head handled with the verify split plan
 constexpr uint32_t kPrefillMaxSplits = 16;
+constexpr uint32_t kClaimMinChunks = 96;  // splits at least this long use the claimed chunk order
 constexpr uint32_t kEntryStream = 0xC0000000u;  // device entry tag: streamed ordinal
 constexpr size_t kAlign = 256;
 
@@ -249,6 +250,7 @@ SplitArgs base_args(kvattn_t h, uint32_t layer, uint32_t W, const float *q) {
     a.sec_vd = h->lay.sec_vd;
     a.k_type = h->p.k_type;
     a.v_type = h->p.v_type;
+    a.dynamic_order = 0;
     a.qscale = h->qscale;
     a.q = q;
     a.part_o = h->part_o();
@@ -362,6 +364,9 @@ int attend_resident(kvattn_t h, uint32_t layer, const float *q, uint32_t W, floa
     Plan pl = plan_resident(h->p, L.n_tokens, L.n_pages, W, h->n_cus);
     SplitArgs a = base_args(h, layer, W, q);
     a.split_chunks = pl.split_chunks;
+    // long splits let waves claim chunks (balances them, measured faster);
+    // short ones keep the static order, which was as fast or faster there
+    a.dynamic_order = (!h->p.deterministic && pl.split_chunks >= kClaimMinChunks) ? 1u : 0u;
     const int rc = pl.wide ? launch_wide(h, a, pl.n_splits, pl.n_row_blocks)
                            : launch_split(h, a, pl.n_splits, pl.n_row_blocks, pl.nrt);
     return rc != KVATTN_OK ? rc : run_merge(h, W, pl.n_splits, out);

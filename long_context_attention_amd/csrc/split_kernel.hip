@@ -67,15 +67,36 @@ __global__ __launch_bounds__((64 * SplitCfg<NT, KT, VT>::waves), 1) void split_k
     }
     // chunks whose keys every row sees (keys <= n_tokens - W) need no mask
     const uint32_t clean_end = (a.n_tokens - a.W + 1) >> 5;
-    // this wave's chunks: first + kSplitWaves * k, k < n_local
+    // Chunk order.  A wave's first kStages - 1 chunks are first + kSplitWaves
+    // * k; later ones continue that sequence (static order: the chunk-to-wave
+    // map and so the bits are fixed) or are claimed from the workgroup's
+    // counter as ring buffers free up (dynamic order: waves whose data arrive
+    // early take more chunks, so the waves finish together).
+    constexpr uint32_t kNone = 0xFFFFFFFFu;
     const uint32_t first = c_begin + wave;
-    const uint32_t n_local = first < c_end ? (c_end - 1 - first) / kSplitWaves + 1 : 0;
+    __shared__ uint32_t next_claim;
+    const bool dynamic = a.dynamic_order != 0;
+    if (dynamic) {
+        if (threadIdx.x == 0) next_claim = c_begin + kSplitWaves * (kStages - 1);
+        __syncthreads();
+    }
+    uint32_t static_k = 0;  // the wave's next index in the static sequence
+    auto next_chunk = [&]() -> uint32_t {
+        uint32_t c;
+        if (!dynamic || static_k < kStages - 1) {
+            c = first + kSplitWaves * static_k;
+            static_k++;
+        } else {
+            uint32_t claimed = 0;
+            if (lane == 0) claimed = atomicAdd(&next_claim, 1u);
+            c = __builtin_amdgcn_readfirstlane(claimed);
+        }
+        return c < c_end ? c : kNone;
+    };
 
     uint8_t *ring = smem + wave * kWaveRingBytes;
     const uint32_t ring_lds = lds_addr(ring);
-    auto chunk_page = [&](uint32_t k) { return (first + kSplitWaves * k) / cpp; };
-    auto issue = [&](uint32_t k, uint32_t entry, uint32_t stage) {
-        const uint32_t chunk = first + kSplitWaves * k;
+    auto issue = [&](uint32_t chunk, uint32_t entry, uint32_t stage) {
         const uint32_t jj0 = (chunk - (chunk / cpp) * cpp) << 5;
         issue_chunk<KT, VT>(a, page_base(a, entry), kvh, jj0, lane, ring_lds + stage * C::bytes);
     };
@@ -107,9 +128,18 @@ __global__ __launch_bounds__((64 * SplitCfg<NT, KT, VT>::waves), 1) void split_k
             }
         }
     }
-    uint32_t entry0[kStages];
+    // the ring's chunks in stage order from the one computed next (q[0]);
+    // `pend` is issued at the next refill, its page entry already loaded
+    uint32_t q[kStages], pend, pend_entry = 0;
+    uint32_t entry0[kStages - 1];
 #pragma unroll
-    for (uint32_t k = 0; k < kStages; k++) entry0[k] = k < n_local ? table_at(a.page_table, chunk_page(k)) : 0u;
+    for (int i = 0; i < kStages - 1; i++) {
+        q[i] = next_chunk();
+        entry0[i] = q[i] != kNone ? table_at(a.page_table, q[i] / cpp) : 0u;
+    }
+    q[kStages - 1] = kNone;
+    pend = next_chunk();
+    if (pend != kNone) pend_entry = table_at(a.page_table, pend / cpp);
 
     // ---- query fragments: lane (row c16, group g) holds dims 32b + 8g .. +8
     // of block b, pre-scaled by softmax_scale * log2(e)
@@ -129,27 +159,32 @@ __global__ __launch_bounds__((64 * SplitCfg<NT, KT, VT>::waves), 1) void split_k
 #pragma unroll
         for (int b = 0; b < 4; b++) asm volatile("" ::"v"(st[t].qf[b]) : "memory");
 
-    // ---- ring prologue: chunks 0 .. kStages - 2 in flight; page entries
-    // (scalar loads) run one chunk ahead of their use
+    // ---- ring prologue: the first kStages - 1 chunks in flight; page
+    // entries (scalar loads) run one chunk ahead of their use
 #pragma unroll
-    for (uint32_t k = 0; k < kStages - 1; k++)
-        if (k < n_local) issue(k, entry0[k], k);
-    uint32_t entry_next = entry0[kStages - 1];
+    for (int i = 0; i < kStages - 1; i++)
+        if (q[i] != kNone) issue(q[i], entry0[i], i);
 
-    if (n_local > 0) {
+    if (q[0] != kNone) {
         uint32_t pv_vq[C::vw];
         half8 pv_pf[NT][C::pf_blocks];
         uint32_t stage = 0;
-        for (uint32_t k = 0; k < n_local; k++) {
-            // refill the buffer chunk k - 1 used (its reads are complete)
-            if (k + kStages - 1 < n_local) {
+        bool have_pv = false;
+        while (q[0] != kNone) {
+            // refill the buffer the previous chunk used (its reads are complete)
+            if (pend != kNone) {
                 wait_lgkmcnt0();
-                issue(k + kStages - 1, entry_next, stage == 0 ? kStages - 1 : stage - 1);
-                if (k + kStages < n_local) entry_next = table_at(a.page_table, chunk_page(k + kStages));
+                issue(pend, pend_entry, stage == 0 ? kStages - 1 : stage - 1);
+                q[kStages - 1] = pend;
+                pend = next_chunk();
+                if (pend != kNone) pend_entry = table_at(a.page_table, pend / cpp);
             }
-            wait_chunk<kStages, C::dma>(min((uint32_t)(kStages - 1), n_local - 1 - k));
+            uint32_t newer = 0;  // chunks issued after this one
+#pragma unroll
+            for (int i = 1; i < kStages; i++) newer += q[i] != kNone ? 1u : 0u;
+            wait_chunk<kStages, C::dma>(newer);
             uint8_t *stg = ring + stage * C::bytes;
-            const uint32_t c = first + kSplitWaves * k;
+            const uint32_t c = q[0];
             const bool tail = 32 * c + 32 > a.n_tokens;  // chunk reaches into page padding
             uint32_t kq[C::kw], kd[16], vd[16];
             float s[NT][8];
@@ -157,7 +192,7 @@ __global__ __launch_bounds__((64 * SplitCfg<NT, KT, VT>::waves), 1) void split_k
             if constexpr (C::kblk) read_kscales<KT, VT>(stg, grp, kd);
             chunk_scores<NT, KT>(st, kq, kd, s);
             if (c >= clean_end) mask_scores<NT>(st, 32 * c, grp, s);
-            if (k > 0) chunk_pv<NT, VT>(st, pv_vq, pv_pf);
+            if (have_pv) chunk_pv<NT, VT>(st, pv_vq, pv_pf);
             if constexpr (C::vblk) {
                 if (tail) sanitize_vscales<KT, VT>(stg, lane, a.n_tokens - 32 * c);
                 read_vscales<KT, VT>(stg, grp, vd);
@@ -167,6 +202,10 @@ __global__ __launch_bounds__((64 * SplitCfg<NT, KT, VT>::waves), 1) void split_k
             read_vcodes<KT, VT>(stg, lane, pv_vq);
             if constexpr (!C::vblk)
                 if (tail) clear_padding_vcodes<KT, VT>(pv_vq, grp, a.n_tokens - 32 * c);
+            have_pv = true;
+#pragma unroll
+            for (int i = 0; i < kStages - 1; i++) q[i] = q[i + 1];
+            q[kStages - 1] = kNone;
             stage = stage == kStages - 1 ? 0 : stage + 1;
         }
         chunk_pv<NT, VT>(st, pv_vq, pv_pf);

@@ -39,12 +39,13 @@ class Params(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint32) for n in (
         "struct_size", "n_layers", "n_q_heads", "n_kv_heads", "head_dim", "page_tokens", "k_type", "v_type",
         "n_pool_pages", "n_ring_slots", "max_pages_per_layer", "max_rows")] + [
-        ("softmax_scale", ctypes.c_float), ("split_pages", ctypes.c_uint32), ("chunk_slots", ctypes.c_uint32)]
+        ("softmax_scale", ctypes.c_float), ("split_pages", ctypes.c_uint32), ("chunk_slots", ctypes.c_uint32),
+        ("deterministic", ctypes.c_uint32)]
 
 
 def make_params(n_layers, n_q_heads, n_kv_heads, n_pool_pages, max_pages_per_layer, max_rows, n_ring_slots=0,
                 page_tokens=256, softmax_scale=0.0, split_pages=0, chunk_slots=0, head_dim=HEAD_DIM,
-                k_type=TYPE_Q8_0, v_type=TYPE_Q4_0) -> Params:
+                k_type=TYPE_Q8_0, v_type=TYPE_Q4_0, deterministic=0) -> Params:
     p = Params()
     p.struct_size = ctypes.sizeof(Params)
     p.n_layers, p.n_q_heads, p.n_kv_heads, p.head_dim = n_layers, n_q_heads, n_kv_heads, head_dim
@@ -52,6 +53,7 @@ def make_params(n_layers, n_q_heads, n_kv_heads, n_pool_pages, max_pages_per_lay
     p.n_pool_pages, p.n_ring_slots, p.max_pages_per_layer, p.max_rows = n_pool_pages, n_ring_slots, \
         max_pages_per_layer, max_rows
     p.softmax_scale, p.split_pages, p.chunk_slots = softmax_scale, split_pages, chunk_slots
+    p.deterministic = deterministic
     return p
 
 

@@ -97,7 +97,7 @@ def test_placement_bitwise_invariance():
     outs = []
     for seed in range(6):
         rng = np.random.default_rng(seed)
-        h = handle(Hq, Hkv, 2 * n, n, 8, n_ring=n + 2, split_pages=2)
+        h = handle(Hq, Hkv, 2 * n, n, 8, n_ring=n + 2, split_pages=2, deterministic=1)
         table = np.empty(n, dtype=np.uint32)
         pool_ids = rng.permutation(2 * n)[:n]
         ring_ids = rng.permutation(n + 2)[:n]
@@ -131,6 +131,31 @@ def test_split_count_sweep():
         h.destroy()
 
 
+@pytest.mark.parametrize("W", [1, 6])
+def test_chunk_order_modes(W):
+    """Deterministic mode repeats its bits exactly; the default (waves claim
+    chunks as buffers free) stays within rounding of it and of the oracle."""
+    N, Hq, Hkv = 48 * 256 + 77, 40, 8
+    say(f"case chunk order N={N} W={W}")
+    kvl = layer_kv(N, Hkv, wid=62, pad="garbage")
+    q = inputs.draw_queries(W, Hq, 0, 62)
+    n = kvl.pages.shape[0]
+    ref = oracle_out(kvl, q, Hq, Hkv)
+    outs = {}
+    for det in (1, 0):
+        h = handle(Hq, Hkv, n, n, 8, split_pages=12, deterministic=det)   # 96 chunks per split
+        place(h, 0, kvl, perm_table(n, 9))
+        outs[det] = [run(h, 0, q, W, "verify" if W > 1 else "decode") for _ in range(3)]
+        h.destroy()
+    for o in outs[1][1:]:
+        assert np.array_equal(o, outs[1][0])
+    for o in outs[0]:
+        assert np.max(np.abs(o - ref)) <= TOL
+        assert np.max(np.abs(o - outs[1][0])) <= 1e-4
+    say(f"  deterministic err {np.max(np.abs(outs[1][0] - ref)):.3e}; dynamic vs deterministic "
+        f"{max(np.max(np.abs(o - outs[1][0])) for o in outs[0]):.3e}")
+
+
 # ------------------------------------------------------------------ streaming
 @pytest.mark.parametrize("pinned", [True, False], ids=["pinned-history", "pageable-history"])
 def test_streamed_matches_resident_bitwise(pinned):
@@ -144,7 +169,7 @@ def test_streamed_matches_resident_bitwise(pinned):
     layers = [layer_kv(N, Hkv, wid=70, layer=l) for l in range(L)]
     qs = [inputs.draw_queries(W, Hq, l, 70) for l in range(L)]
     hs = handle(Hq, Hkv, L * n, n, 8, n_ring=5, chunk_slots=2, n_layers=L)
-    hr = handle(Hq, Hkv, L * n, n, 8, split_pages=1, n_layers=L)
+    hr = handle(Hq, Hkv, L * n, n, 8, split_pages=1, n_layers=L, deterministic=1)
     hist = []
     for l in range(L):
         res = inputs.resident_subset(n, int(round(0.4 * n)), l, 70)
