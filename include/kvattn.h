@@ -284,6 +284,100 @@ int kvattn_profile(kvattn_t h, uint32_t max_launches);
 int kvattn_profile_read(kvattn_t h, int reset, double *split_ms, uint32_t *n_split, double *merge_ms,
                         uint32_t *n_merge);
 
+/*
+ * Adaptive resident/ring partition ("troed's fork ...", sections "KV data
+ * movement and attention" and "Backend-neutral memory and streaming
+ * contracts"): when everything fits, every page is resident; under pressure
+ * resident pages are traded for ring slots, streaming one or a few whole
+ * layers first, more pages as the context grows; the pool/ring split is
+ * adjusted with hysteresis from sampled readiness misses, ring occupancy
+ * and copy-stream busy time.  kvattn_policy_step is a pure host function:
+ * it proposes a split and moves no bytes.  The caller applies a decision by
+ * re-placing pages (kvattn_upload_pages, kvattn_set_layer) and sizing the
+ * ring (kvattn_set_ring_slots).
+ *
+ * Feedback rule (the pages name the signals, not the rule):
+ *   pressure  = misses / chunks > miss_rate_high with copy_busy < busy_high:
+ *               the ring limits prefetch -> grow by ring_step after
+ *               grow_after such samples in a row;
+ *   saturated = copy_busy >= busy_high: a larger ring cannot help the link,
+ *               fewer streamed pages can -> shrink by ring_step after
+ *               shrink_after samples in a row;
+ *   idle ring = no misses and ring_occupancy < occupancy_low -> shrink after
+ *               shrink_after samples in a row.
+ * Other samples reset the streaks; the ring stays in [min_ring_slots,
+ * min(max_ring_slots, budget_pages - 1)] while anything streams.
+ * Residency: the pool gets budget_pages - ring pages; the deficit streams
+ * from whole layers in layer order (layer 0 first), one layer possibly in
+ * part.
+ */
+enum { KVATTN_POLICY_FITS = 0,        /* the history fits: all resident, no ring */
+       KVATTN_POLICY_HOLD = 1,        /* split unchanged */
+       KVATTN_POLICY_CONTEXT = 2,     /* streaming started or the context length changed the residency */
+       KVATTN_POLICY_GROW_RING = 3,
+       KVATTN_POLICY_SHRINK_RING = 4 };
+
+typedef struct kvattn_policy_config {
+    uint32_t n_layers;
+    uint32_t page_tokens;
+    uint32_t budget_pages;        /* device pages for pool + ring together */
+    uint32_t min_ring_slots;      /* >= 1 */
+    uint32_t max_ring_slots;      /* >= min_ring_slots */
+    uint32_t ring_step;           /* slots added or removed per adjustment (>= 1) */
+    uint32_t grow_after;          /* consecutive pressure samples before growing (>= 1) */
+    uint32_t shrink_after;        /* consecutive saturated or idle samples before shrinking (>= 1) */
+    float miss_rate_high;         /* [0, 1] */
+    float busy_high;              /* (0, 1] */
+    float occupancy_low;          /* [0, 1] */
+} kvattn_policy_config;
+
+typedef struct kvattn_policy_state {  /* zero-initialise before the first step */
+    uint32_t ring_slots;
+    uint32_t pages_per_layer;
+    uint32_t pressure_streak, saturated_streak, idle_streak;
+} kvattn_policy_state;
+
+typedef struct kvattn_policy_observation {
+    uint32_t n_tokens;            /* current history length (every layer) */
+    uint32_t chunks;              /* streamed chunks computed in the sample (0: no feedback) */
+    uint32_t ready_misses;        /* of those, chunks whose compute reached the ready fence before the copy ended */
+    float ring_occupancy;         /* peak fraction of ring slots holding copied, not yet consumed pages */
+    float copy_busy;              /* fraction of the sampled interval the copy stream was copying */
+} kvattn_policy_observation;
+
+typedef struct kvattn_policy_decision {
+    uint32_t reason;              /* KVATTN_POLICY_* */
+    uint32_t changed;             /* 1 if ring size or pages per layer differ from the previous state */
+    uint32_t ring_slots;
+    uint32_t pages_per_layer;
+    uint32_t resident_pages;      /* sum over layers */
+    uint32_t streamed_pages;      /* per pass */
+    uint32_t streamed_layers;     /* layers with at least one streamed page */
+} kvattn_policy_decision;
+
+/* One step: next state, decision, and resident_per_layer[n_layers] (pages of
+ * each layer to keep resident).  KVATTN_E_ARG for an invalid config or null
+ * pointers, KVATTN_E_NOSPACE when the budget cannot hold one page per layer
+ * or a minimal ring beside the pool. */
+int kvattn_policy_step(const kvattn_policy_config *config, const kvattn_policy_state *previous,
+                       const kvattn_policy_observation *observation, kvattn_policy_state *next,
+                       kvattn_policy_decision *decision, uint32_t *resident_per_layer);
+
+/* Observation of streamed calls.  kvattn_observe(h, n) with n > 0 records
+ * timing events around the next n streamed chunks (copy start and end on the
+ * copy stream; compute reaching the ready fence and finishing the chunk on
+ * the compute stream); n = 0 stops.  kvattn_observe_read waits for both
+ * streams and fills chunks, ready_misses, ring_occupancy and copy_busy over
+ * the recorded chunks (n_tokens is left to the caller); reset != 0 starts a
+ * new sample. */
+int kvattn_observe(kvattn_t h, uint32_t max_chunks);
+int kvattn_observe_read(kvattn_t h, int reset, kvattn_policy_observation *out);
+
+/* Ring slots the scheduler uses from now on (1 .. params.n_ring_slots).
+ * Drains both streams and restarts the streaming schedule; pages of caller-
+ * placed ring slots must lie below the new count. */
+int kvattn_set_ring_slots(kvattn_t h, uint32_t n_slots);
+
 /* Drain both streams, release events, free the handle (NULL is a no-op). */
 int kvattn_destroy(kvattn_t h);
 

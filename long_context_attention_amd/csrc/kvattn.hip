@@ -14,12 +14,15 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
+#include <tuple>
 #include <new>
 #include <string>
 #include <vector>
 
 #include "../../include/kvattn.h"
 #include "attn_kernels.h"
+#include "policy.h"
 #include "sched.h"
 
 namespace {
@@ -191,6 +194,15 @@ struct kvattn {
     std::vector<LayerState> layers;
     StreamScheduler sched;
     bool any_streamed = false, any_ring_slots = false;
+    uint32_t ring_slots = 0;           // ring slots the scheduler uses (<= p.n_ring_slots)
+    // optional observation of streamed chunks: per chunk, copy start / end on
+    // the copy stream, compute reaching its ready wait / finishing the chunk
+    bool observing = false;
+    std::vector<hipEvent_t> obs_ev;    // [4i + 0..3] for chunk i
+    std::vector<uint32_t> obs_pages;   // pages of chunk i
+    std::vector<uint8_t> obs_marks;    // events recorded for chunk i (bit k: event 4i + k)
+    std::map<std::tuple<uint32_t, uint64_t, uint32_t>, size_t> obs_of;  // (layer, ordinal base, first) -> i
+    size_t obs_used = 0;
     std::string err;
     float qscale = 0.f;
     // optional per-launch timing of the split and merge kernels
@@ -243,7 +255,7 @@ SplitArgs base_args(kvattn_t h, uint32_t layer, uint32_t W, const float *q) {
     a.G = h->p.n_q_heads / h->p.n_kv_heads;
     a.split_chunks = h->p.page_tokens / 32;
     a.ring_base = 0;
-    a.n_ring_slots = std::max<uint32_t>(1, h->p.n_ring_slots);
+    a.n_ring_slots = std::max<uint32_t>(1, h->ring_slots);
     a.page_bytes = h->lay.page_bytes;
     a.sec_kd = h->lay.sec_kd;
     a.sec_vc = h->lay.sec_vc;
@@ -420,9 +432,39 @@ struct HipExec {
     // A pinned history is gathered by the ring-copy kernel in one launch;
     // otherwise runs of consecutive logical pages landing in consecutive
     // ring slots become one hipMemcpyAsync each.
+    // observation slot of a chunk (its copy and, possibly in a later call,
+    // its compute), -1 when not observing or the pool is full
+    long obs_slot(const ChunkRef &c, bool for_copy) {
+        if (!h->observing) return -1;
+        const auto key = std::make_tuple(c.layer, c.ordinal_base, c.first);
+        if (for_copy) {
+            if (h->obs_used >= h->obs_pages.size()) return -1;
+            h->obs_of[key] = h->obs_used;
+            h->obs_pages[h->obs_used] = c.count;
+            h->obs_marks[h->obs_used] = 0;
+            return (long)h->obs_used++;
+        }
+        auto it = h->obs_of.find(key);
+        return it == h->obs_of.end() ? -1 : (long)it->second;
+    }
+    int obs_record(long ob, int k, hipStream_t s) {
+        HIP_TRY(h, hipEventRecord(h->obs_ev[4 * ob + k], s));
+        h->obs_marks[ob] |= (uint8_t)(1u << k);
+        return KVATTN_OK;
+    }
+
     int copy(const ChunkRef &c) {
         const LayerState &L = h->layers[c.layer];
         if (c.wait_event >= 0) HIP_TRY(h, hipStreamWaitEvent(h->copy, h->sched.consumed_event(c.wait_event), 0));
+        const long ob = obs_slot(c, true);
+        int rc;
+        if (ob >= 0 && (rc = obs_record(ob, 0, h->copy))) return rc;
+        if ((rc = copy_pages(c, L))) return rc;
+        if (ob >= 0 && (rc = obs_record(ob, 1, h->copy))) return rc;
+        HIP_TRY(h, hipEventRecord(h->sched.ready_event(c.event), h->copy));
+        return KVATTN_OK;
+    }
+    int copy_pages(const ChunkRef &c, const LayerState &L) {
         const size_t pb = h->lay.page_bytes;
         if (L.history_dev) {
             RingCopyArgs r;
@@ -431,23 +473,21 @@ struct HipExec {
             r.ring = h->ring;
             r.first = c.first;
             r.count = c.count;
-            r.ring_base = (uint32_t)(c.ordinal_base % h->p.n_ring_slots);
-            r.n_slots = h->p.n_ring_slots;
+            r.ring_base = (uint32_t)(c.ordinal_base % h->ring_slots);
+            r.n_slots = h->ring_slots;
             r.page_bytes = pb;
             HIP_TRY(h, kvattn_launch_ring_copy(r, h->copy));
-            HIP_TRY(h, hipEventRecord(h->sched.ready_event(c.event), h->copy));
             return KVATTN_OK;
         }
         uint32_t o = c.first;
         while (o < c.first + c.count) {
-            const uint32_t slot = (uint32_t)((c.ordinal_base + o) % h->p.n_ring_slots);
+            const uint32_t slot = (uint32_t)((c.ordinal_base + o) % h->ring_slots);
             uint32_t run = 1;
-            while (o + run < c.first + c.count && L.streamed[o + run] == L.streamed[o] + run && slot + run < h->p.n_ring_slots) run++;
+            while (o + run < c.first + c.count && L.streamed[o + run] == L.streamed[o] + run && slot + run < h->ring_slots) run++;
             HIP_TRY(h, hipMemcpyAsync(h->ring + (size_t)slot * pb, L.history + (size_t)L.streamed[o] * pb, (size_t)run * pb,
                                       hipMemcpyHostToDevice, h->copy));
             o += run;
         }
-        HIP_TRY(h, hipEventRecord(h->sched.ready_event(c.event), h->copy));
         return KVATTN_OK;
     }
     int resident(uint32_t layer) {
@@ -458,11 +498,14 @@ struct HipExec {
     }
     int compute(const ChunkRef &c) {
         const LayerState &L = h->layers[c.layer];
+        const long ob = obs_slot(c, false);
+        int rc;
+        if (ob >= 0 && (rc = obs_record(ob, 2, h->compute))) return rc;
         HIP_TRY(h, hipStreamWaitEvent(h->compute, h->sched.ready_event(c.event), 0));
         a.list_offset = L.n_resident + c.first;
-        a.ring_base = (uint32_t)(c.ordinal_base % h->p.n_ring_slots);
-        int rc = launch_split(h, a, c.count, 1, nrt);
-        if (rc) return rc;
+        a.ring_base = (uint32_t)(c.ordinal_base % h->ring_slots);
+        if ((rc = launch_split(h, a, c.count, 1, nrt))) return rc;
+        if (ob >= 0 && (rc = obs_record(ob, 3, h->compute))) return rc;
         HIP_TRY(h, hipEventRecord(h->sched.consumed_event(c.event), h->compute));
         return KVATTN_OK;
     }
@@ -524,7 +567,7 @@ int validate_table(kvattn_t h, const kvattn_params &p, const uint32_t *page_tabl
     const uint32_t n_pages = (uint32_t)(((uint64_t)n_tokens + T - 1) / T);
     if (n_pages > p.max_pages_per_layer)
         return fail(h, KVATTN_E_NOSPACE, "%u pages exceed max_pages_per_layer %u", n_pages, p.max_pages_per_layer);
-    int rc = check_page_table(page_table, n_pages, p.n_pool_pages, p.n_ring_slots, chk);
+    int rc = check_page_table(page_table, n_pages, p.n_pool_pages, h ? h->ring_slots : p.n_ring_slots, chk);
     if (rc == PT_BAD_POOL) return fail(h, KVATTN_E_RANGE, "page %u: pool page out of range", chk->bad_index);
     if (rc == PT_BAD_RING) return fail(h, KVATTN_E_RANGE, "page %u: ring slot out of range", chk->bad_index);
     if (rc == PT_DUPLICATE)
@@ -620,6 +663,7 @@ int kvattn_create(const kvattn_params *params, void *d_pool, size_t pool_bytes, 
         return code;
     }
     const uint32_t chunk = p.chunk_slots ? p.chunk_slots : 16;
+    h->ring_slots = p.n_ring_slots;
     if (p.n_ring_slots) {
         if (!h->sched.init(p.n_layers, p.n_ring_slots, std::min(chunk, p.n_ring_slots))) {
             (void)hipEventDestroy(h->upload_done);
@@ -639,7 +683,7 @@ int kvattn_upload_pages(kvattn_t h, const void *h_pages, const uint32_t *dst, ui
         uint32_t e = dst[i];
         if (e & KVATTN_PT_RING_FLAG) {
             uint32_t s = e & ~KVATTN_PT_RING_FLAG;
-            if (e == KVATTN_PT_HOST || s >= h->p.n_ring_slots) return fail(h, KVATTN_E_RANGE, "destination %u: ring slot out of range", i);
+            if (e == KVATTN_PT_HOST || s >= h->ring_slots) return fail(h, KVATTN_E_RANGE, "destination %u: ring slot out of range", i);
             if (h->any_streamed) return fail(h, KVATTN_E_PLAN, "the ring belongs to the streaming scheduler on this handle");
         } else if (e >= h->p.n_pool_pages) {
             return fail(h, KVATTN_E_RANGE, "destination %u: pool page %u out of range (%u pages)", i, e, h->p.n_pool_pages);
@@ -710,6 +754,12 @@ int install_layer(kvattn_t h, uint32_t layer, const uint32_t *page_table, uint32
     if (h->p.n_ring_slots) h->sched.set_layer_counts(counts);
     return KVATTN_OK;
 }
+
+std::vector<uint32_t> streamed_counts(kvattn_t h) {
+    std::vector<uint32_t> counts(h->p.n_layers, 0);
+    for (uint32_t l = 0; l < h->p.n_layers; l++) counts[l] = h->layers[l].set ? h->layers[l].n_streamed : 0;
+    return counts;
+}
 }  // namespace
 
 int kvattn_set_layer(kvattn_t h, uint32_t layer, const uint32_t *page_table, uint32_t n_tokens, const void *h_history) {
@@ -778,7 +828,7 @@ int kvattn_append(kvattn_t h, uint32_t layer, const float *d_k, const float *d_v
     w.T = T;
     w.Hkv = h->p.n_kv_heads;
     w.ring_base = 0;
-    w.n_ring_slots = h->p.n_ring_slots;
+    w.n_ring_slots = std::max<uint32_t>(1, h->ring_slots);
     w.page_bytes = h->lay.page_bytes;
     w.sec_kd = h->lay.sec_kd;
     w.sec_vc = h->lay.sec_vc;
@@ -822,7 +872,7 @@ int kvattn_debug_read_page(kvattn_t h, uint32_t layer, uint32_t logical_page, vo
     if (logical_page >= h->layers[layer].n_pages) return fail(h, KVATTN_E_RANGE, "logical page %u out of range", logical_page);
     if (!h_out) return fail(h, KVATTN_E_ARG, "null output");
     SplitArgs a = base_args(h, layer, 1, nullptr);
-    a.ring_base = (uint32_t)(h->sched.last_ordinal_base(layer) % std::max<uint32_t>(1, h->p.n_ring_slots));
+    a.ring_base = (uint32_t)(h->sched.last_ordinal_base(layer) % std::max<uint32_t>(1, h->ring_slots));
     uint8_t *staging = h->wsp + h->ws.staging;
     HIP_TRY(h, kvattn_launch_read_page(a, logical_page, staging, h->compute));
     HIP_TRY(h, hipMemcpyAsync(h_out, staging, h->lay.page_bytes, hipMemcpyDeviceToHost, h->compute));
@@ -869,6 +919,117 @@ int kvattn_profile_read(kvattn_t h, int reset, double *split_ms, uint32_t *n_spl
     return KVATTN_OK;
 }
 
+int kvattn_policy_step(const kvattn_policy_config *config, const kvattn_policy_state *previous,
+                       const kvattn_policy_observation *observation, kvattn_policy_state *next,
+                       kvattn_policy_decision *decision, uint32_t *resident_per_layer) {
+    if (!config || !previous || !observation || !next || !decision || !resident_per_layer)
+        return fail(nullptr, KVATTN_E_ARG, "null policy argument");
+    const int rc = kvattn_policy::step(*config, *previous, *observation, next, decision, resident_per_layer);
+    if (rc == KVATTN_E_ARG) return fail(nullptr, rc, "invalid policy config");
+    if (rc == KVATTN_E_NOSPACE) return fail(nullptr, rc, "budget too small for one page per layer and a ring");
+    return rc;
+}
+
+int kvattn_observe(kvattn_t h, uint32_t max_chunks) {
+    if (!h) return fail(nullptr, KVATTN_E_ARG, "null handle");
+    HIP_TRY(h, hipStreamSynchronize(h->copy));
+    HIP_TRY(h, hipStreamSynchronize(h->compute));
+    h->obs_used = 0;
+    h->obs_of.clear();
+    if (max_chunks == 0) {
+        h->observing = false;
+        return KVATTN_OK;
+    }
+    if (h->obs_ev.size() < 4 * (size_t)max_chunks) {
+        for (hipEvent_t e : h->obs_ev) (void)hipEventDestroy(e);
+        h->obs_ev.assign(4 * (size_t)max_chunks, nullptr);
+        for (hipEvent_t &e : h->obs_ev) HIP_TRY(h, hipEventCreate(&e));
+    }
+    h->obs_pages.assign(max_chunks, 0);
+    h->obs_marks.assign(max_chunks, 0);
+    h->observing = true;
+    return KVATTN_OK;
+}
+
+// Readiness misses, copy-stream busy fraction and peak ring occupancy over
+// the observed chunks (times from timing events, relative to the first copy).
+int kvattn_observe_read(kvattn_t h, int reset, kvattn_policy_observation *out) {
+    if (!h) return fail(nullptr, KVATTN_E_ARG, "null handle");
+    if (!out) return fail(h, KVATTN_E_ARG, "null output");
+    HIP_TRY(h, hipStreamSynchronize(h->copy));
+    HIP_TRY(h, hipStreamSynchronize(h->compute));
+    const uint32_t n_tokens = out->n_tokens;
+    *out = kvattn_policy_observation{};
+    out->n_tokens = n_tokens;
+    struct T {
+        double cs, ce, reach, done;
+        uint32_t pages;
+    };
+    std::vector<T> t;
+    hipEvent_t ref = nullptr;
+    for (size_t i = 0; i < h->obs_used; i++)
+        if (h->obs_marks[i] & 1u) {
+            ref = h->obs_ev[4 * i];
+            break;
+        }
+    double copy_sum = 0.0, lo = 1e300, hi = -1e300;
+    for (size_t i = 0; ref && i < h->obs_used; i++) {
+        if ((h->obs_marks[i] & 3u) != 3u) continue;
+        float a = 0.f, b = 0.f;
+        HIP_TRY(h, hipEventElapsedTime(&a, ref, h->obs_ev[4 * i]));
+        HIP_TRY(h, hipEventElapsedTime(&b, ref, h->obs_ev[4 * i + 1]));
+        copy_sum += b - a;
+        lo = std::min(lo, (double)a);
+        hi = std::max(hi, (double)b);
+        if (h->obs_marks[i] != 15u) continue;  // compute not enqueued yet
+        float r = 0.f, d = 0.f;
+        HIP_TRY(h, hipEventElapsedTime(&r, ref, h->obs_ev[4 * i + 2]));
+        HIP_TRY(h, hipEventElapsedTime(&d, ref, h->obs_ev[4 * i + 3]));
+        t.push_back({a, b, r, d, h->obs_pages[i]});
+    }
+    out->chunks = (uint32_t)t.size();
+    for (const T &x : t) out->ready_misses += x.ce > x.reach ? 1u : 0u;
+    out->copy_busy = hi > lo ? (float)std::min(1.0, copy_sum / (hi - lo)) : 0.f;
+    double peak = 0.0;
+    for (const T &x : t) {  // pages copied and not yet consumed when chunk x's copy ends
+        double held = 0.0;
+        for (const T &y : t)
+            if (y.ce <= x.ce && y.done > x.ce) held += y.pages;
+        peak = std::max(peak, held);
+    }
+    out->ring_occupancy = h->ring_slots ? (float)std::min(1.0, peak / h->ring_slots) : 0.f;
+    if (reset) {
+        h->obs_used = 0;
+        h->obs_of.clear();
+    }
+    return KVATTN_OK;
+}
+
+int kvattn_set_ring_slots(kvattn_t h, uint32_t n_slots) {
+    if (!h) return fail(nullptr, KVATTN_E_ARG, "null handle");
+    if (n_slots == 0 || n_slots > h->p.n_ring_slots)
+        return fail(h, KVATTN_E_RANGE, "ring slots %u outside 1..%u", n_slots, h->p.n_ring_slots);
+    for (uint32_t l = 0; l < h->p.n_layers; l++) {
+        const LayerState &L = h->layers[l];
+        if (!L.set || !L.uses_ring_slots) continue;
+        for (uint32_t e : L.table)
+            if (e != KVATTN_PT_HOST && (e & KVATTN_PT_RING_FLAG) && (e & ~KVATTN_PT_RING_FLAG) >= n_slots)
+                return fail(h, KVATTN_E_RANGE, "layer %u places a page in ring slot %u >= %u", l, e & ~KVATTN_PT_RING_FLAG,
+                            n_slots);
+    }
+    if (n_slots == h->ring_slots) return KVATTN_OK;
+    HIP_TRY(h, hipStreamSynchronize(h->copy));
+    HIP_TRY(h, hipStreamSynchronize(h->compute));
+    const uint32_t chunk = h->p.chunk_slots ? h->p.chunk_slots : 16;
+    h->sched.destroy();
+    if (!h->sched.init(h->p.n_layers, n_slots, std::min(chunk, n_slots))) return fail(h, KVATTN_E_HIP, "ring event setup failed");
+    h->sched.set_layer_counts(streamed_counts(h));
+    h->ring_slots = n_slots;
+    h->obs_of.clear();  // chunk keys of the old schedule
+    h->obs_used = 0;
+    return KVATTN_OK;
+}
+
 int kvattn_destroy(kvattn_t h) {
     if (!h) return KVATTN_OK;
     int rc = KVATTN_OK;
@@ -877,6 +1038,8 @@ int kvattn_destroy(kvattn_t h) {
     h->sched.destroy();
     if (h->upload_done) (void)hipEventDestroy(h->upload_done);
     for (hipEvent_t e : h->prof_ev)
+        if (e) (void)hipEventDestroy(e);
+    for (hipEvent_t e : h->obs_ev)
         if (e) (void)hipEventDestroy(e);
     delete h;
     return rc;

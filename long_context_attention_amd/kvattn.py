@@ -57,12 +57,43 @@ def make_params(n_layers, n_q_heads, n_kv_heads, n_pool_pages, max_pages_per_lay
     return p
 
 
+POLICY_FITS, POLICY_HOLD, POLICY_CONTEXT, POLICY_GROW_RING, POLICY_SHRINK_RING = 0, 1, 2, 3, 4
+
+
+class PolicyConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint32) for n in (
+        "n_layers", "page_tokens", "budget_pages", "min_ring_slots", "max_ring_slots", "ring_step", "grow_after",
+        "shrink_after")] + [(n, ctypes.c_float) for n in ("miss_rate_high", "busy_high", "occupancy_low")]
+
+
+class PolicyState(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint32) for n in (
+        "ring_slots", "pages_per_layer", "pressure_streak", "saturated_streak", "idle_streak")]
+
+
+class PolicyObservation(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint32) for n in ("n_tokens", "chunks", "ready_misses")] + [
+        (n, ctypes.c_float) for n in ("ring_occupancy", "copy_busy")]
+
+
+class PolicyDecision(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint32) for n in (
+        "reason", "changed", "ring_slots", "pages_per_layer", "resident_pages", "streamed_pages", "streamed_layers")]
+
+
+def policy_config(n_layers, page_tokens, budget_pages, min_ring_slots=16, max_ring_slots=256, ring_step=16,
+                  grow_after=2, shrink_after=4, miss_rate_high=0.25, busy_high=0.9, occupancy_low=0.5):
+    return PolicyConfig(n_layers, page_tokens, budget_pages, min_ring_slots, max_ring_slots, ring_step, grow_after,
+                        shrink_after, miss_rate_high, busy_high, occupancy_low)
+
+
 _lib = None
 EXPORTS = ["kvattn_supported", "kvattn_page_bytes", "kvattn_workspace_bytes", "kvattn_create",
            "kvattn_upload_pages", "kvattn_set_layer", "kvattn_decode", "kvattn_verify", "kvattn_prefill_chunk",
            "kvattn_append",
            "kvattn_synchronize", "kvattn_debug_read_page", "kvattn_validate_page_table", "kvattn_sched_simulate",
-           "kvattn_profile", "kvattn_profile_read", "kvattn_destroy",
+           "kvattn_profile", "kvattn_profile_read", "kvattn_policy_step", "kvattn_observe", "kvattn_observe_read",
+           "kvattn_set_ring_slots", "kvattn_destroy",
            "kvattn_last_error", "kvattn_global_error"]
 
 
@@ -110,6 +141,16 @@ def lib():
     L.kvattn_profile_read.argtypes = [P, I, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(U),
                                       ctypes.POINTER(ctypes.c_double), ctypes.POINTER(U)]
     L.kvattn_profile_read.restype = I
+    L.kvattn_policy_step.argtypes = [ctypes.POINTER(PolicyConfig), ctypes.POINTER(PolicyState),
+                                     ctypes.POINTER(PolicyObservation), ctypes.POINTER(PolicyState),
+                                     ctypes.POINTER(PolicyDecision), P]
+    L.kvattn_policy_step.restype = I
+    L.kvattn_observe.argtypes = [P, U]
+    L.kvattn_observe.restype = I
+    L.kvattn_observe_read.argtypes = [P, I, ctypes.POINTER(PolicyObservation)]
+    L.kvattn_observe_read.restype = I
+    L.kvattn_set_ring_slots.argtypes = [P, U]
+    L.kvattn_set_ring_slots.restype = I
     L.kvattn_destroy.argtypes = [P]
     L.kvattn_destroy.restype = I
     L.kvattn_last_error.argtypes = [P]
@@ -137,6 +178,16 @@ def _addr(t):
 
 
 # ---------------------------------------------------------------- free functions
+def policy_step(config: PolicyConfig, state: PolicyState, observation: PolicyObservation):
+    """One step of the resident/ring policy: (next state, decision, resident
+    pages per layer)."""
+    nxt, dec = PolicyState(), PolicyDecision()
+    resident = np.zeros(config.n_layers, dtype=np.uint32)
+    _check(lib().kvattn_policy_step(ctypes.byref(config), ctypes.byref(state), ctypes.byref(observation),
+                                    ctypes.byref(nxt), ctypes.byref(dec), resident.ctypes.data))
+    return nxt, dec, resident
+
+
 def supported(k_type=TYPE_Q8_0, v_type=TYPE_Q4_0, head_dim=HEAD_DIM) -> bool:
     return bool(lib().kvattn_supported(k_type, v_type, head_dim))
 
@@ -243,6 +294,18 @@ class Handle:
         _check(lib().kvattn_profile_read(self.h, int(reset), ctypes.byref(a), ctypes.byref(na), ctypes.byref(b),
                                          ctypes.byref(nb)), self.h)
         return a.value, na.value, b.value, nb.value
+
+    def observe(self, max_chunks):
+        _check(lib().kvattn_observe(self.h, max_chunks), self.h)
+
+    def observe_read(self, n_tokens=0, reset=True) -> PolicyObservation:
+        o = PolicyObservation()
+        o.n_tokens = n_tokens
+        _check(lib().kvattn_observe_read(self.h, int(reset), ctypes.byref(o)), self.h)
+        return o
+
+    def set_ring_slots(self, n_slots):
+        _check(lib().kvattn_set_ring_slots(self.h, n_slots), self.h)
 
     def destroy(self):
         if self.h:
