@@ -68,6 +68,9 @@ def parse():
                     help="pages per split for calls of <= 32 rows per KV head (0: the library's choice)")
     ap.add_argument("--deterministic", action="store_true",
                     help="fixed chunk order inside splits (same bits every call) instead of waves claiming chunks")
+    ap.add_argument("--adaptive", action="store_true",
+                    help="streamed workloads: afterwards run the adaptive resident/ring policy in closed loop on the "
+                         "same device-page budget and time its final split")
     ap.add_argument("--kv-types", choices=sorted(KV_TYPES), default="q8_0-q4_0",
                     help="K/V element-type pair of the cache (default: the workloads' Q8_0 K / Q4_0 V)")
     ap.add_argument("--h2d-ceiling", action="store_true",
@@ -222,6 +225,84 @@ def h2d_ceiling(torch, mb=436, reps=3):
     return {"contiguous_gbps": round(best, 2), "page_pieces_gbps": round(piece_rate, 2), "bytes": n}
 
 
+# --------------------------------------------------------------------------- adaptive partition
+def adaptive_run(h, w, hist, qs, outs, kind, rows, n_layers, steps, torch, kv, max_iters=8):
+    """Closed loop of kvattn_policy_step on the streamed workload: the device
+    budget is the fixed split's pool plus a minimal ring; each iteration runs
+    one observed pass, steps the policy and applies a changed decision
+    (resident pages re-placed from the pinned histories, ring resized).
+    Returns the trajectory and the final split's pass time."""
+    dev = "cuda"
+    n = w.n_pages
+    pb = kv.page_bytes(h.params)
+    n_pool_alloc = n_layers * w.n_resident
+    pool = h.pool.view(n_pool_alloc, pb)
+    min_ring = 32
+    c = kv.policy_config(n_layers, 256, n_pool_alloc + min_ring, min_ring_slots=min_ring,
+                         max_ring_slots=w.ring_slots, ring_step=16, grow_after=1, shrink_after=2, busy_high=0.85)
+
+    def apply(res, ring):
+        h.set_ring_slots(ring)
+        nxt = 0
+        for l in range(n_layers):
+            r = int(res[l])
+            table = np.full(n, kv.PT_HOST, dtype=np.uint32)
+            ids = np.arange(nxt, nxt + r, dtype=np.int64)
+            table[n - r:] = ids
+            if r:
+                pool[torch.from_numpy(ids).to(dev)] = hist[l][n - r:].to(dev)
+            torch.cuda.synchronize()
+            h.set_layer(l, table, w.n_tokens, hist[l])
+            nxt += r
+        return nxt
+
+    o = kv.PolicyObservation()
+    o.n_tokens = w.n_tokens
+    st, d, res = kv.policy_step(c, kv.PolicyState(), o)
+    apply(res, d.ring_slots)
+    traj = [{"reason": int(d.reason), "ring_slots": int(d.ring_slots), "streamed_layers": int(d.streamed_layers),
+             "streamed_pages": int(d.streamed_pages)}]
+    stream = h.compute_stream
+    holds = 0
+    for it in range(max_iters):
+        with torch.cuda.stream(stream):
+            one_pass(h, qs, outs, kind, rows)
+        torch.cuda.synchronize()
+        h.observe(1 << 14)
+        with torch.cuda.stream(stream):
+            one_pass(h, qs, outs, kind, rows)
+        ob = h.observe_read(w.n_tokens)
+        h.observe(0)
+        st, d, res = kv.policy_step(c, st, ob)
+        traj.append({"chunks": int(ob.chunks), "misses": int(ob.ready_misses),
+                     "occupancy": round(float(ob.ring_occupancy), 3), "copy_busy": round(float(ob.copy_busy), 3),
+                     "reason": int(d.reason), "ring_slots": int(d.ring_slots),
+                     "streamed_layers": int(d.streamed_layers), "streamed_pages": int(d.streamed_pages)})
+        log(f"bench: adaptive iteration {it}: {traj[-1]}")
+        if d.changed:
+            apply(res, d.ring_slots)
+            holds = 0
+        else:
+            holds += 1
+            if holds >= 2:
+                break
+    with torch.cuda.stream(stream):
+        one_pass(h, qs, outs, kind, rows)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(steps):
+            one_pass(h, qs, outs, kind, rows)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"budget_pages": int(c.budget_pages), "trajectory": traj, "final_ring_slots": int(d.ring_slots),
+            "final_streamed_layers": int(d.streamed_layers), "ms_per_step": round(ms, 3),
+            "tokens_per_s": round(rows / (ms / 1e3), 3),
+            "h2d_gbps": round(d.streamed_pages * pb / (ms / 1e3) / 1e9, 2)}
+
+
 # --------------------------------------------------------------------------- cpu baseline
 def cpu_baseline(w, rows, kind, inputs, budget_s=10.0, types=KV_TYPES["q8_0-q4_0"]):
     """The oracle (fp64 C, OpenMP over (row, head)) on a bounded sample of the
@@ -367,6 +448,10 @@ def main():
     torch.cuda.synchronize()
     step_ms = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
 
+    adaptive = None
+    if args.adaptive and streamed:
+        adaptive = adaptive_run(h, w, hist, qs, outs, kind, rows, n_layers, max(2, min(args.steps, 5)), torch, kv)
+
     writer = None
     if args.writer and kind != "prefill" and not streamed:
         writer = time_writer(h, w, rows, n_layers, args.steps, torch, inputs, stream, types[3])
@@ -440,6 +525,8 @@ def main():
                                         "merge_launches": n_merge})
     if writer is not None:
         result["writer"] = writer
+    if adaptive is not None:
+        result["adaptive"] = adaptive
     if args.with_copy_kernel:
         a = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device="cuda")
         b = torch.empty_like(a)
