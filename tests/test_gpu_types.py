@@ -139,3 +139,46 @@ def test_pair_append_bitexact(pair, N0, R, Hkv):
     say(f"  decode after append: max-abs err {err:.3e}")
     assert err <= TOL
     h.destroy()
+
+
+# ------------------------------------------------------------------ full size, the benchmark's launch configuration
+@pytest.mark.parametrize("pair", PAIRS, ids=IDS)
+@pytest.mark.parametrize("wname,W", [("decode-40k", 1), ("verify-160k", 6)])
+def test_pair_full_size(pair, wname, W):
+    """`bench.py --kv-types` workloads at full size with the automatic split
+    plan: one seeded layer, every output element against the oracle."""
+    w = inputs.WORKLOADS[wname]
+    say(f"case full-size types k={pair[0]} v={pair[1]} {wname} W={W}")
+    n = w.n_pages
+    h = handle(w.n_q_heads, w.n_kv_heads, n, n, 8, k_type=pair[0], v_type=pair[1])
+    kvl = inputs.draw_layer(w.n_tokens, w.n_kv_heads, 23, w.wid, device="cuda", k_type=pair[0], v_type=pair[1])
+    place(h, 0, kvl, inputs.seeded_permutation(n, 23, w.wid))
+    q = inputs.draw_queries(W, w.n_q_heads, 23, w.wid, device="cuda")
+    got = run(h, 0, q, W, "decode" if W == 1 else "verify")
+    ref = oracle_out(kvl, q, w.n_q_heads, w.n_kv_heads)
+    err = np.max(np.abs(got - ref))
+    say(f"  max-abs err {err:.3e}")
+    assert err <= TOL
+    h.destroy()
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=IDS)
+def test_pair_full_size_prefill_rows(pair):
+    """The 256-row prefill chunk over 123,136 keys per pair: four seeded rows
+    (first and last included) against the oracle, every output finite."""
+    w = inputs.WORKLOADS["prefill-120k"]
+    R = w.prefill_rows
+    say(f"case full-size types k={pair[0]} v={pair[1]} prefill R={R}")
+    n = w.n_pages
+    h = handle(w.n_q_heads, w.n_kv_heads, n, n, R, k_type=pair[0], v_type=pair[1])
+    kvl = inputs.draw_layer(w.n_tokens, w.n_kv_heads, 4, w.wid, device="cuda", k_type=pair[0], v_type=pair[1])
+    place(h, 0, kvl, inputs.seeded_permutation(n, 4, w.wid))
+    q = inputs.draw_queries(R, w.n_q_heads, 4, w.wid, device="cuda")
+    got = run(h, 0, q, R, "prefill")
+    assert np.isfinite(got).all()
+    rows = sorted({0, R - 1, *np.random.default_rng(12).choice(R, 2, replace=False).tolist()})
+    ref = oracle_out(kvl, q, w.n_q_heads, w.n_kv_heads, rows=rows)
+    err = np.max(np.abs(got[rows] - ref))
+    say(f"  rows {rows}: max-abs err {err:.3e}")
+    assert err <= TOL
+    h.destroy()
