@@ -990,11 +990,18 @@ int kvattn_observe_read(kvattn_t h, int reset, kvattn_policy_observation *out) {
     out->chunks = (uint32_t)t.size();
     for (const T &x : t) out->ready_misses += x.ce > x.reach ? 1u : 0u;
     out->copy_busy = hi > lo ? (float)std::min(1.0, copy_sum / (hi - lo)) : 0.f;
-    double peak = 0.0;
-    for (const T &x : t) {  // pages copied and not yet consumed when chunk x's copy ends
-        double held = 0.0;
-        for (const T &y : t)
-            if (y.ce <= x.ce && y.done > x.ce) held += y.pages;
+    // peak of pages copied and not yet consumed: sweep the copy-end (+pages)
+    // and chunk-done (-pages) times in order, releases first at equal times
+    std::vector<std::pair<double, double>> steps;
+    steps.reserve(2 * t.size());
+    for (const T &x : t) {
+        steps.emplace_back(x.ce, (double)x.pages);
+        steps.emplace_back(x.done, -(double)x.pages);
+    }
+    std::sort(steps.begin(), steps.end());
+    double peak = 0.0, held = 0.0;
+    for (const auto &st : steps) {
+        held += st.second;
         peak = std::max(peak, held);
     }
     out->ring_occupancy = h->ring_slots ? (float)std::min(1.0, peak / h->ring_slots) : 0.f;
