@@ -279,8 +279,9 @@ SplitArgs base_args(kvattn_t h, uint32_t layer, uint32_t W, const float *q) {
 // buffer.
 struct Plan {
     uint32_t split_chunks, n_splits, n_row_blocks;
-    int nrt;    // split kernel: 16-row tiles per workgroup
-    bool wide;  // wide kernel
+    int nrt;         // split kernel: 16-row tiles per workgroup
+    bool wide;       // wide kernel
+    int wide_waves;  // wide kernel: waves per workgroup (8 or 12)
 };
 
 Plan plan_resident(const kvattn_params &p, uint32_t n_tokens, uint32_t n_pages, uint32_t W, int n_cus) {
@@ -290,6 +291,7 @@ Plan plan_resident(const kvattn_params &p, uint32_t n_tokens, uint32_t n_pages, 
     const uint32_t cpp = p.page_tokens / 32;
     const uint64_t cus = (uint64_t)std::max(n_cus, 1);
     Plan pl;
+    pl.wide_waves = 8;
     pl.wide = rows > kNarrowRows;
     if (!pl.wide) {
         pl.nrt = rows <= 16 ? 1 : 2;
@@ -303,7 +305,13 @@ Plan plan_resident(const kvattn_params &p, uint32_t n_tokens, uint32_t n_pages, 
         }
     } else {
         pl.nrt = 2;
-        pl.n_row_blocks = (rows + kvattn_wide_rows() - 1) / kvattn_wide_rows();
+        // 12-wave workgroups (384-row blocks) run a row about 1.37x as fast as
+        // 8-wave ones (256-row blocks, measured on the 1,280-row prefill
+        // chunk); take them unless their partly empty last block costs more
+        const uint32_t rpw = kvattn_wide_rows_per_wave();
+        const uint64_t b8 = (rows + 8 * rpw - 1) / (8 * rpw), b12 = (rows + 12 * rpw - 1) / (12 * rpw);
+        pl.wide_waves = b12 * 12 * 100 < b8 * 8 * 137 ? 12 : 8;
+        pl.n_row_blocks = (uint32_t)(pl.wide_waves == 12 ? b12 : b8);
         const uint64_t per = (uint64_t)p.n_kv_heads * pl.n_row_blocks;
         uint32_t splits = (uint32_t)std::min<uint64_t>(kPrefillMaxSplits, std::max<uint64_t>(1, cus / per));
         splits = std::min(splits, n_pages);
@@ -342,10 +350,10 @@ int launch_split(kvattn_t h, const SplitArgs &a, uint32_t n_items, uint32_t n_ro
     return KVATTN_OK;
 }
 
-int launch_wide(kvattn_t h, const SplitArgs &a, uint32_t n_splits, uint32_t n_row_blocks) {
+int launch_wide(kvattn_t h, const SplitArgs &a, uint32_t n_splits, uint32_t n_row_blocks, int waves) {
     hipEvent_t e0, e1;
     prof_slot(h, 0, &e0, &e1);
-    HIP_TRY(h, kvattn_launch_wide(a, n_splits, n_row_blocks, h->compute, e0, e1));
+    HIP_TRY(h, kvattn_launch_wide(a, n_splits, n_row_blocks, waves, h->compute, e0, e1));
     return KVATTN_OK;
 }
 
@@ -379,7 +387,7 @@ int attend_resident(kvattn_t h, uint32_t layer, const float *q, uint32_t W, floa
     // long splits let waves claim chunks (balances them, measured faster);
     // short ones keep the static order, which was as fast or faster there
     a.dynamic_order = (!h->p.deterministic && pl.split_chunks >= kClaimMinChunks) ? 1u : 0u;
-    const int rc = pl.wide ? launch_wide(h, a, pl.n_splits, pl.n_row_blocks)
+    const int rc = pl.wide ? launch_wide(h, a, pl.n_splits, pl.n_row_blocks, pl.wide_waves)
                            : launch_split(h, a, pl.n_splits, pl.n_row_blocks, pl.nrt);
     return rc != KVATTN_OK ? rc : run_merge(h, W, pl.n_splits, out);
 }

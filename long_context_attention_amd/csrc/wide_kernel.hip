@@ -19,7 +19,10 @@ namespace kvattn_dev {
 // compute p.  Raw chunks land in a 3-stage ring by direct-to-LDS loads, the
 // seven load instructions of a chunk spread over waves 0..6.
 // ---------------------------------------------------------------------------
-constexpr int kWideRows = 256;
+// Workgroup shapes: 8 waves (256-row blocks) or 12 waves (384-row blocks;
+// three waves per SIMD overlap matrix-core and vector work better, measured
+// +14 % on the 1,280-row prefill chunk despite its partly empty last block).
+constexpr int kWideRowsPerWave = 32;
 constexpr int kViewBytes = 16384;  // K' [tt][b][lane] x 16 B, then V' [n][lane] x 16 B
 
 // Scores for NT row tiles from the f16 view: S^T = K' Q^T, four blocks
@@ -127,7 +130,7 @@ __device__ __forceinline__ void dequant_view(const uint8_t *raw, uint8_t *view, 
         }
         *reinterpret_cast<half8 *>(view + ((tt * 4 + b0) * 64 + l) * 16) = o0;
         *reinterpret_cast<half8 *>(view + ((tt * 4 + b0 + 1) * 64 + l) * 16) = o1;
-    } else {
+    } else if (t < 512) {
         const int h = (t - 256) >> 6, g = l >> 4;
         half8 v0, v1;
         if constexpr (VT == kTypeF16) {
@@ -160,12 +163,13 @@ __device__ __forceinline__ void dequant_view(const uint8_t *raw, uint8_t *view, 
     }
 }
 
-template <int KT, int VT>
-__global__ __launch_bounds__(512, 1) void wide_kernel(const SplitArgs a) {
+template <int KT, int VT, int WAVES>
+__global__ __launch_bounds__((64 * WAVES), 1) void wide_kernel(const SplitArgs a) {
     using C = Chunk<KT, VT>;
     constexpr int NT = 2;
-    // a chunk's loads, spread over the 8 waves: wave w issues loads w and w + 8
-    constexpr int kLoadsMax = (C::dma + 7) / 8;
+    constexpr int kRows = kWideRowsPerWave * WAVES;
+    // a chunk's loads, spread over the waves: wave w issues loads w, w + WAVES, ...
+    constexpr int kLoadsMax = (C::dma + WAVES - 1) / WAVES;
     __shared__ __attribute__((aligned(16))) uint8_t raw_ring[kStages][C::bytes];
     __shared__ __attribute__((aligned(16))) uint8_t views[2][kViewBytes];
 
@@ -174,8 +178,8 @@ __global__ __launch_bounds__(512, 1) void wide_kernel(const SplitArgs a) {
     const int grp = lane >> 4;
     const int c16 = lane & 15;
     const uint32_t kvh = blockIdx.y;
-    const uint32_t block_row0 = blockIdx.z * kWideRows;
-    const uint32_t wave_row0 = block_row0 + 32 * wave;
+    const uint32_t block_row0 = blockIdx.z * kRows;
+    const uint32_t wave_row0 = block_row0 + kWideRowsPerWave * wave;
     const uint32_t rows_kv = a.W * a.G;
     const uint32_t n_chunks_all = (a.n_tokens + 31) >> 5;
     const uint32_t cpp = a.T >> 5;
@@ -187,7 +191,9 @@ __global__ __launch_bounds__(512, 1) void wide_kernel(const SplitArgs a) {
     const bool active = wave_row0 < rows_kv;  // wave has rows to compute
 
     // this wave's share of a chunk's direct-to-LDS loads
-    const uint32_t my_loads = (uint32_t)(wave < C::dma) + (uint32_t)(wave + 8 < C::dma);
+    uint32_t my_loads = 0;
+#pragma unroll
+    for (int i = 0; i < kLoadsMax; i++) my_loads += (uint32_t)(wave + WAVES * i < C::dma);
     auto issue = [&](uint32_t p) {
         if (my_loads == 0) return;
         const uint32_t chunk = c_begin + p;
@@ -197,7 +203,7 @@ __global__ __launch_bounds__(512, 1) void wide_kernel(const SplitArgs a) {
         const uint32_t dst = lds_addr(raw_ring[p % kStages]);
 #pragma unroll
         for (int i = 0; i < kLoadsMax; i++)
-            if (wave + 8 * i < C::dma) issue_chunk_part<KT, VT>(a, base, kvh, jj0, lane, dst, wave + 8 * i);
+            if (wave + WAVES * i < C::dma) issue_chunk_part<KT, VT>(a, base, kvh, jj0, lane, dst, wave + WAVES * i);
     };
     static_assert(2 * kLoadsMax <= 4, "wait_vmcnt_upto range");
     auto n_valid_of = [&](uint32_t p) {
@@ -296,28 +302,35 @@ __global__ __launch_bounds__(512, 1) void wide_kernel(const SplitArgs a) {
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-hipError_t kvattn_launch_wide(const SplitArgs &a, uint32_t n_splits, uint32_t n_row_blocks, hipStream_t s,
+hipError_t kvattn_launch_wide(const SplitArgs &a, uint32_t n_splits, uint32_t n_row_blocks, int waves, hipStream_t s,
                               hipEvent_t ev_start, hipEvent_t ev_stop) {
     using namespace kvattn_dev;
     (void)hipGetLastError();
-    const dim3 grid(n_splits, a.Hkv, n_row_blocks), block(512);
+    if (waves != 8 && waves != 12) return hipErrorInvalidValue;
+    const dim3 grid(n_splits, a.Hkv, n_row_blocks), block(64 * waves);
     auto go = [&](auto kern) {
         if (ev_start)
             hipExtLaunchKernelGGL(kern, grid, block, 0, s, ev_start, ev_stop, 0, a);
         else
             hipLaunchKernelGGL(kern, grid, block, 0, s, a);
     };
+    auto pick = [&](auto kern8, auto kern12) {
+        if (waves == 8)
+            go(kern8);
+        else
+            go(kern12);
+    };
     if (a.k_type == kTypeQ8_0 && a.v_type == kTypeQ4_0)
-        go(wide_kernel<kTypeQ8_0, kTypeQ4_0>);
+        pick(wide_kernel<kTypeQ8_0, kTypeQ4_0, 8>, wide_kernel<kTypeQ8_0, kTypeQ4_0, 12>);
     else if (a.k_type == kTypeQ8_0 && a.v_type == kTypeQ8_0)
-        go(wide_kernel<kTypeQ8_0, kTypeQ8_0>);
+        pick(wide_kernel<kTypeQ8_0, kTypeQ8_0, 8>, wide_kernel<kTypeQ8_0, kTypeQ8_0, 12>);
     else if (a.k_type == kTypeQ4_0 && a.v_type == kTypeQ4_0)
-        go(wide_kernel<kTypeQ4_0, kTypeQ4_0>);
+        pick(wide_kernel<kTypeQ4_0, kTypeQ4_0, 8>, wide_kernel<kTypeQ4_0, kTypeQ4_0, 12>);
     else if (a.k_type == kTypeF16 && a.v_type == kTypeF16)
-        go(wide_kernel<kTypeF16, kTypeF16>);
+        pick(wide_kernel<kTypeF16, kTypeF16, 8>, wide_kernel<kTypeF16, kTypeF16, 12>);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
-uint32_t kvattn_wide_rows() { return kvattn_dev::kWideRows; }
+uint32_t kvattn_wide_rows_per_wave() { return kvattn_dev::kWideRowsPerWave; }
