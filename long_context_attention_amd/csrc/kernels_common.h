@@ -144,9 +144,6 @@ struct Chunk {
     static constexpr int pf_blocks = vblk ? 4 : 1;  // distinct P' operands per row tile
 };
 
-// The Q8_0 K / Q4_0 V chunk (the wide kernel's raw-ring default shape).
-constexpr int kChunkBytes = Chunk<kTypeQ8_0, kTypeQ4_0>::bytes;
-constexpr int kStages = 3;  // raw-chunk ring of the wide kernel
 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
@@ -191,7 +188,11 @@ __device__ __forceinline__ void wait_vmcnt_upto(uint32_t n) {
         case 1: wait_vmcnt<1>(); break;
         case 2: wait_vmcnt<2>(); break;
         case 3: wait_vmcnt<3>(); break;
-        default: wait_vmcnt<4>(); break;
+        case 4: wait_vmcnt<4>(); break;
+        case 5: wait_vmcnt<5>(); break;
+        case 6: wait_vmcnt<6>(); break;
+        case 7: wait_vmcnt<7>(); break;
+        default: wait_vmcnt<8>(); break;
     }
 }
 

@@ -6,23 +6,28 @@ namespace kvattn_dev {
 
 // ---------------------------------------------------------------------------
 // Wide kernel (prefill chunks, and any call with more than 32 rows per KV
-// head).  A workgroup of 8 waves handles one split of one KV head for a block
-// of 256 rows; wave w owns rows 32w .. 32w + 31 (two 16-row tiles) over every
-// chunk of the split, so no combine across waves is needed.
+// head).  A workgroup of 8 or 12 waves handles one split of one KV head for a
+// block of 256 or 384 rows; wave w owns rows 32w .. 32w + 31 (two 16-row
+// tiles) over every chunk of the split, so no combine across waves is needed.
 // Per 32-key chunk the workgroup first turns the staged codes into binary16
 // K' = c * d_K and V' = (n - 8) * d_V once (the f16 working view of the
 // pages' wide-prefill path), shared through LDS by all 256 rows; the matrix
 // cores then run on K' and V' with no per-block scale work in the row loop.
 // Each of K', V' is one rounding from the exact product (relative 2^-11).
-// Pipeline per chunk p (one barrier): wait for raw chunk p + 1, barrier,
-// issue raw chunk p + 3, dequantise p + 1 into the other view buffer,
-// compute p.  Raw chunks land in a 3-stage ring by direct-to-LDS loads, the
-// seven load instructions of a chunk spread over waves 0..6.
+// Pipeline per step of two chunks (one barrier): wait for the raw chunks of
+// the next step, barrier, issue the raw chunks of the step after, dequantise
+// the next step's chunks into their views, compute this step's chunks.  Raw
+// chunks land in a ring of four buffers by direct-to-LDS loads, a chunk's load
+// instructions spread over the waves.
 // ---------------------------------------------------------------------------
 // Workgroup shapes: 8 waves (256-row blocks) or 12 waves (384-row blocks;
 // three waves per SIMD overlap matrix-core and vector work better, measured
 // +14 % on the 1,280-row prefill chunk despite its partly empty last block).
 constexpr int kWideRowsPerWave = 32;
+// Two chunks per barrier halve the barriers and let a wave's matrix-core work
+// on one chunk overlap its vector work on the other (measured +7 % on the
+// prefill chunk against one; three were faster for Q8_0/Q4_0 but slower for
+// Q8_0/Q8_0 and do not fit the LDS for F16).
 constexpr int kViewBytes = 16384;  // K' [tt][b][lane] x 16 B, then V' [n][lane] x 16 B
 
 // Scores for NT row tiles from the f16 view: S^T = K' Q^T, four blocks
@@ -170,8 +175,9 @@ __global__ __launch_bounds__((64 * WAVES), 1) void wide_kernel(const SplitArgs a
     constexpr int kRows = kWideRowsPerWave * WAVES;
     // a chunk's loads, spread over the waves: wave w issues loads w, w + WAVES, ...
     constexpr int kLoadsMax = (C::dma + WAVES - 1) / WAVES;
-    __shared__ __attribute__((aligned(16))) uint8_t raw_ring[kStages][C::bytes];
-    __shared__ __attribute__((aligned(16))) uint8_t views[2][kViewBytes];
+    // two chunks per barrier: raw chunks and f16 views in rings of four
+    __shared__ __attribute__((aligned(16))) uint8_t raw_ring[4][C::bytes];
+    __shared__ __attribute__((aligned(16))) uint8_t views[4][kViewBytes];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -200,12 +206,12 @@ __global__ __launch_bounds__((64 * WAVES), 1) void wide_kernel(const SplitArgs a
         const uint32_t page = chunk / cpp;
         const uint32_t jj0 = (chunk - page * cpp) << 5;
         const uint8_t *base = resolve_page(a, page);
-        const uint32_t dst = lds_addr(raw_ring[p % kStages]);
+        const uint32_t dst = lds_addr(raw_ring[p & 3]);
 #pragma unroll
         for (int i = 0; i < kLoadsMax; i++)
             if (wave + WAVES * i < C::dma) issue_chunk_part<KT, VT>(a, base, kvh, jj0, lane, dst, wave + WAVES * i);
     };
-    static_assert(2 * kLoadsMax <= 4, "wait_vmcnt_upto range");
+    static_assert(2 * kLoadsMax <= 8, "wait_vmcnt_upto range");
     auto n_valid_of = [&](uint32_t p) {
         const uint32_t c = c_begin + p;
         return 32 * c + 32 > a.n_tokens ? a.n_tokens - 32 * c : 32u;
@@ -247,30 +253,40 @@ __global__ __launch_bounds__((64 * WAVES), 1) void wide_kernel(const SplitArgs a
             asm volatile("" ::"v"(st[t].qf[b]) : "memory");
         }
 
-    // ---- prologue: raw chunks 0..2 in flight, chunk 0 into view 0
+    // ---- prologue: raw chunks 0..3 in flight, chunks 0 and 1 into views 0, 1
 #pragma unroll
-    for (uint32_t p = 0; p < kStages; p++)
+    for (uint32_t p = 0; p < 4; p++)
         if (p < n) issue(p);
-    wait_vmcnt_upto(min(n - 1, 2u) * my_loads);
+    wait_vmcnt_upto((min(n, 4u) - min(n, 2u)) * my_loads);
     __syncthreads();
     dequant_view<KT, VT>(raw_ring[0], views[0], n_valid_of(0));
+    if (1 < n) dequant_view<KT, VT>(raw_ring[1], views[1], n_valid_of(1));
 
-    for (uint32_t p = 0; p < n; p++) {
-        // raw chunk p + 1 landed (every wave waited for its own share)
-        if (p + 1 < n) wait_vmcnt_upto(min(n - 2 - p, 1u) * my_loads);
-        __syncthreads();
-        if (p + kStages < n) issue(p + kStages);
-        if (p + 1 < n) dequant_view<KT, VT>(raw_ring[(p + 1) % kStages], views[(p + 1) & 1], n_valid_of(p + 1));
-        if (active) {
-            const uint8_t *view = views[p & 1];
-            const uint32_t c = c_begin + p;
-            float s[NT][8];
-            half8 pf[NT];
-            view_scores<NT>(st, view, lane, s);
-            if (c >= clean_end) mask_scores<NT>(st, 32 * c, grp, s);
+    auto compute_chunk = [&](uint32_t p) {
+        const uint8_t *view = views[p & 3];
+        const uint32_t c = c_begin + p;
+        float s[NT][8];
+        half8 pf[NT];
+        view_scores<NT>(st, view, lane, s);
+        if (c >= clean_end) mask_scores<NT>(st, 32 * c, grp, s);
 #pragma unroll
-            for (int t = 0; t < NT; t++) view_probs(st[t], s[t], pf[t]);
-            view_pv<NT>(st, view, lane, pf);
+        for (int t = 0; t < NT; t++) view_probs(st[t], s[t], pf[t]);
+        view_pv<NT>(st, view, lane, pf);
+    };
+    // step of two chunks: p and p + 1 are computed from their views while
+    // p + 2, p + 3 are dequantised and p + 4, p + 5 are loaded (chunk q's raw
+    // buffer and view: q mod 4)
+    for (uint32_t p = 0; p < n; p += 2) {
+        // raw chunks p + 2, p + 3 landed (nothing was issued after them)
+        if (p + 2 < n) wait_vmcnt_upto(0);
+        __syncthreads();
+        if (p + 4 < n) issue(p + 4);
+        if (p + 5 < n) issue(p + 5);
+        if (p + 2 < n) dequant_view<KT, VT>(raw_ring[(p + 2) & 3], views[(p + 2) & 3], n_valid_of(p + 2));
+        if (p + 3 < n) dequant_view<KT, VT>(raw_ring[(p + 3) & 3], views[(p + 3) & 3], n_valid_of(p + 3));
+        if (active) {
+            compute_chunk(p);
+            if (p + 1 < n) compute_chunk(p + 1);
         }
     }
 
