@@ -335,20 +335,29 @@ struct RowState {
     floatx4 acc[8];  // O^T tile n: dims 16n + 4g + v of the lane's row
 };
 
-// Scores of one chunk for NT row tiles: s[t][4tt + v] is key 16tt + 4g + v
-// of the chunk for tile t, log2-scaled.  Each K fragment is converted once
-// and feeds one MFMA per tile and 32-dim block; block types scale each
-// block's fp32 dot by its own binary16 d_K, F16 keys accumulate the four
-// blocks in the MFMA.
+// The softmax reference a tile's scores are taken relative to: the row's
+// lazy reference, or 0 before the first key.
+__device__ __forceinline__ float score_ref(const RowState &st) { return st.m_ref == kNegInf ? 0.f : st.m_ref; }
+
+// Scores of one chunk for NT row tiles, relative to the tile's reference:
+// s[t][4tt + v] = score(key 16tt + 4g + v of the chunk) - score_ref(tile t),
+// log2-scaled.  Each K fragment is converted once and feeds one MFMA per tile
+// and 32-dim block; block types scale each block's fp32 dot by its own
+// binary16 d_K, F16 keys accumulate the four blocks in the MFMA.  The
+// reference enters as the start of the sum, so the softmax needs no
+// subtraction.
 template <int NT, int KT>
 __device__ __forceinline__ void chunk_scores(const RowState (&st)[NT], const uint32_t *kq, const uint32_t kd[16],
                                              float (&s)[NT][8]) {
+    float ref[NT];
+#pragma unroll
+    for (int t = 0; t < NT; t++) ref[t] = score_ref(st[t]);
 #pragma unroll
     for (int tt = 0; tt < 2; tt++) {
         if constexpr (KT == kTypeF16) {
             floatx4 d[NT];
 #pragma unroll
-            for (int t = 0; t < NT; t++) d[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int t = 0; t < NT; t++) d[t] = floatx4{-ref[t], -ref[t], -ref[t], -ref[t]};
 #pragma unroll
             for (int b = 0; b < 4; b++) {
                 const half8 kf = k_frag<KT>(kq, tt, b);
@@ -374,12 +383,39 @@ __device__ __forceinline__ void chunk_scores(const RowState (&st)[NT], const uin
 #pragma unroll
                 for (int v = 0; v < 4; v++) {
                     // fma with the binary16 operand read in place (v_fma_mix_f32)
-                    float acc = half_of(kd + 8 * tt, 4 * v) * d[0][t][v];
+                    float acc = __builtin_fmaf(half_of(kd + 8 * tt, 4 * v), d[0][t][v], -ref[t]);
 #pragma unroll
                     for (int b = 1; b < 4; b++) acc = __builtin_fmaf(half_of(kd + 8 * tt, 4 * v + b), d[b][t][v], acc);
                     s[t][4 * tt + v] = acc;
                 }
         }
+    }
+}
+
+// Lazy reference update of one row tile from its relative scores s (mask:
+// -inf): when some score exceeds the reference by more than kRescale (or
+// before the first key) the reference moves to the row maximum, the
+// accumulators and the denominator are rescaled, and s is shifted to the new
+// reference.
+__device__ __forceinline__ void update_reference(RowState &st, float (&s)[8]) {
+    float m = s[0];
+#pragma unroll
+    for (int i = 1; i < 8; i++) m = fmaxf(m, s[i]);
+    const float thr = st.m_ref == kNegInf ? kNegInf : kRescale;
+    if (__any(m > thr)) {
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        const float ref = score_ref(st);
+        const float m_new = fmaxf(st.m_ref, ref + m);
+        const float alpha = (st.m_ref == kNegInf) ? 0.f : fast_exp2(st.m_ref - m_new);
+        st.l_run *= alpha;
+#pragma unroll
+        for (int n = 0; n < 8; n++) st.acc[n] *= alpha;
+        st.m_ref = m_new;
+        // a row with no visible key yet keeps -inf scores (no shift by inf)
+        const float shift = m_new == kNegInf ? 0.f : ref - m_new;
+#pragma unroll
+        for (int i = 0; i < 8; i++) s[i] += shift;
     }
 }
 
@@ -410,32 +446,19 @@ __device__ __forceinline__ void sanitize_vscales(uint8_t *stg, int lane, uint32_
     *w = v;
 }
 
-// Softmax step of one chunk for one row tile: lazy reference update
-// (rescaling the accumulators, which already hold every earlier chunk),
-// probabilities, the denominator, and the P' operands: P * d_V per value
-// block for block V types, P itself for F16 values.
+// Softmax step of one chunk for one row tile from its relative scores: lazy
+// reference update, probabilities P = 2^s, the denominator, and the P'
+// operands: P * d_V per value block for block V types, P itself for F16
+// values.
 template <int VT>
-__device__ __forceinline__ void chunk_probs(RowState &st, const float s[8], const uint32_t vd[16],
+__device__ __forceinline__ void chunk_probs(RowState &st, float (&s)[8], const uint32_t vd[16],
                                             half8 (&pf)[VT == kTypeF16 ? 1 : 4]) {
-    float m = s[0];
-#pragma unroll
-    for (int i = 1; i < 8; i++) m = fmaxf(m, s[i]);
-    if (__any(m > st.m_ref + kRescale)) {
-        m = fmaxf(m, __shfl_xor(m, 16));
-        m = fmaxf(m, __shfl_xor(m, 32));
-        const float m_new = fmaxf(st.m_ref, m);
-        const float alpha = (st.m_ref == kNegInf) ? 0.f : fast_exp2(st.m_ref - m_new);
-        st.l_run *= alpha;
-#pragma unroll
-        for (int n = 0; n < 8; n++) st.acc[n] *= alpha;
-        st.m_ref = m_new;
-    }
-    const float mu = (st.m_ref == kNegInf) ? 0.f : st.m_ref;
+    update_reference(st, s);
     float p[8];
     float lsum = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-        p[i] = fast_exp2(s[i] - mu);
+        p[i] = fast_exp2(s[i]);
         lsum += p[i];
     }
     st.l_run += lsum;

@@ -30,8 +30,9 @@ constexpr int kWideRowsPerWave = 32;
 // Q8_0/Q8_0 and do not fit the LDS for F16).
 constexpr int kViewBytes = 16384;  // K' [tt][b][lane] x 16 B, then V' [n][lane] x 16 B
 
-// Scores for NT row tiles from the f16 view: S^T = K' Q^T, four blocks
-// accumulated in the MFMA.
+// Scores for NT row tiles from the f16 view, relative to each tile's
+// reference (the MFMA accumulator starts at -reference): S^T = K' Q^T, four
+// blocks accumulated in the MFMA.
 template <int NT>
 __device__ __forceinline__ void view_scores(const RowState (&st)[NT], const uint8_t *view, int lane,
                                             float (&s)[NT][8]) {
@@ -39,7 +40,10 @@ __device__ __forceinline__ void view_scores(const RowState (&st)[NT], const uint
     for (int tt = 0; tt < 2; tt++) {
         floatx4 d[NT];
 #pragma unroll
-        for (int t = 0; t < NT; t++) d[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < NT; t++) {
+            const float ref = score_ref(st[t]);
+            d[t] = floatx4{-ref, -ref, -ref, -ref};
+        }
 #pragma unroll
         for (int b = 0; b < 4; b++) {
             const half8 kf = *reinterpret_cast<const half8 *>(view + ((tt * 4 + b) * 64 + lane) * 16);
@@ -53,28 +57,15 @@ __device__ __forceinline__ void view_scores(const RowState (&st)[NT], const uint
     }
 }
 
-// Softmax step of one chunk for one row tile (lazy reference as in
-// chunk_probs); P rounded to binary16 once.
-__device__ __forceinline__ void view_probs(RowState &st, const float s[8], half8 &pf) {
-    float m = s[0];
-#pragma unroll
-    for (int i = 1; i < 8; i++) m = fmaxf(m, s[i]);
-    if (__any(m > st.m_ref + kRescale)) {
-        m = fmaxf(m, __shfl_xor(m, 16));
-        m = fmaxf(m, __shfl_xor(m, 32));
-        const float m_new = fmaxf(st.m_ref, m);
-        const float alpha = (st.m_ref == kNegInf) ? 0.f : fast_exp2(st.m_ref - m_new);
-        st.l_run *= alpha;
-#pragma unroll
-        for (int n = 0; n < 8; n++) st.acc[n] *= alpha;
-        st.m_ref = m_new;
-    }
-    const float mu = (st.m_ref == kNegInf) ? 0.f : st.m_ref;
+// Softmax step of one chunk for one row tile from its relative scores (lazy
+// reference as in chunk_probs); P rounded to binary16 once.
+__device__ __forceinline__ void view_probs(RowState &st, float (&s)[8], half8 &pf) {
+    update_reference(st, s);
     float p[8];
     float lsum = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-        p[i] = fast_exp2(s[i] - mu);
+        p[i] = fast_exp2(s[i]);
         lsum += p[i];
     }
     st.l_run += lsum;
