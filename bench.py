@@ -303,6 +303,36 @@ def adaptive_run(h, w, hist, qs, outs, kind, rows, n_layers, steps, torch, kv, m
             "h2d_gbps": round(d.streamed_pages * pb / (ms / 1e3) / 1e9, 2)}
 
 
+# --------------------------------------------------------------------------- machine
+def gpu_info(torch):
+    """Device name and CU count, plus the current clocks rocm-smi reports (best
+    effort: absent when the tool is not there)."""
+    props = torch.cuda.get_device_properties(0)
+    info = {"name": props.name, "compute_units": props.multi_processor_count}
+    try:
+        import subprocess
+        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            low = line.lower()
+            for key in ("sclk", "mclk", "fclk"):
+                if f"{key} clock level" in low and "mhz" in low:
+                    info.setdefault(f"{key}_mhz", line.split("(")[-1].split("Mhz")[0].split("MHz")[0].strip())
+    except Exception:
+        pass
+    return info
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 # --------------------------------------------------------------------------- cpu baseline
 def cpu_baseline(w, rows, kind, inputs, budget_s=10.0, types=KV_TYPES["q8_0-q4_0"]):
     """The oracle (fp64 C, OpenMP over (row, head)) on a bounded sample of the
@@ -344,6 +374,7 @@ def cpu_baseline(w, rows, kind, inputs, budget_s=10.0, types=KV_TYPES["q8_0-q4_0
     one = time.perf_counter() - t0
     one_pass_s = one * w.n_layers * rows
     return {"value": rows / pass_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu": {"model": cpu_model(), "logical_cpus": os.cpu_count()},
             "sample": f"{layers} of {w.n_layers} layers of {w.name} ({w.n_tokens} keys, {w.n_q_heads} query heads, "
                       f"{len(sample_rows)} of {rows} rows), {spent:.1f} s measured, scaled to the full pass",
             "one_core": {"value": rows / one_pass_s, "unit": "tokens/s",
@@ -481,6 +512,7 @@ def main():
                    "kv_types": types[2], "mode": mode, "split_pages": args.split_pages or "auto",
                    "chunk_order": "static" if args.deterministic else "claimed in splits of >= 96 chunks, else static",
                    "resident_fraction": w.resident_fraction, "ring_slots": w.ring_slots},
+        "gpu": gpu_info(torch),
         "layers_per_s": round(n_layers / (ms_per_step / 1e3), 1),
         "kv_gbps": round(kv_gbps, 1),
         "kv_frac_hbm_peak": round(kv_gbps / HBM_PEAK_GBPS, 4),
