@@ -308,7 +308,7 @@ def gpu_info(torch):
     """Device name and CU count, plus the current clocks rocm-smi reports (best
     effort: absent when the tool is not there)."""
     props = torch.cuda.get_device_properties(0)
-    info = {"name": props.name, "compute_units": props.multi_processor_count}
+    info = {"name": props.name, "arch": getattr(props, "gcnArchName", ""), "compute_units": props.multi_processor_count}
     try:
         import subprocess
         out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=10).stdout

@@ -388,6 +388,75 @@ __global__ __launch_bounds__(128 * U) void merge_kernel(const MergeArgs a) {
                row_ml);
 }
 
+// Merge of calls with many splits (streamed layers and resident layers split
+// one page per split: one split per page): one unit per workgroup of 512
+// threads.  M, the weights w_s and L as in merge_rows, reduced over the
+// threads in a fixed order; dimension d is summed in four parts (splits
+// congruent to q mod 4, in split order), which then add in part order, so
+// each thread waits for a quarter of the batches of 32 loads.
+constexpr int kManyParts = 4;
+constexpr uint32_t kManyMinSplits = 65;  // more splits than this take merge_many_kernel
+
+__global__ __launch_bounds__(128 * kManyParts) void merge_many_kernel(const MergeArgs a) {
+    __shared__ float2 wl[kMergeMaxSplits];
+    __shared__ float part_sum[kManyParts][128];
+    __shared__ float wave_red[2 * kManyParts];
+    const uint32_t unit = blockIdx.x, tid = threadIdx.x, nt = blockDim.x, ns = a.n_splits;
+    const uint32_t lane = tid & 63, wave = tid >> 6;
+    const size_t mls = (size_t)a.units * 2, pos = (size_t)a.units * 128;
+    const uint32_t d = tid & 127, q = tid >> 7;
+    const float *po = a.part_o + (size_t)unit * 128 + d;
+    // first batch of this thread's values, issued before anything waits
+    float first[kMergeBatch];
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; k++) first[k] = po[(size_t)min(q + kManyParts * k, ns - 1) * pos];
+    for (uint32_t s = tid; s < ns; s += nt) wl[s] = *reinterpret_cast<const float2 *>(a.part_ml + s * mls + (size_t)unit * 2);
+    __syncthreads();
+    float M = kNegInf;
+    for (uint32_t s = tid; s < ns; s += nt)
+        if (wl[s].y > 0.f) M = fmaxf(M, wl[s].x);
+    M = wave_max(M);
+    if (lane == 0) wave_red[wave] = M;
+    __syncthreads();
+    M = wave_red[0];
+    for (uint32_t w = 1; w < nt / 64; w++) M = fmaxf(M, wave_red[w]);
+    __syncthreads();  // wave_red is reused below
+    float L = 0.f;
+    for (uint32_t s = tid; s < ns; s += nt) {
+        const float2 v = wl[s];
+        const float w = v.y > 0.f ? fast_exp2(v.x - M) : 0.f;
+        wl[s].x = w;
+        L += w * v.y;
+    }
+    L = wave_sum(L);
+    if (lane == 0) wave_red[wave] = L;
+    __syncthreads();
+    L = 0.f;
+    for (uint32_t w = 0; w < nt / 64; w++) L += wave_red[w];
+    // dimension d, part q: splits q, q + 4, ... in order
+    float A = 0.f;
+    const uint32_t nq = ns > q ? (ns - q + kManyParts - 1) / kManyParts : 0;  // splits in this part
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; k++)
+        if ((uint32_t)k < nq) A += wl[q + kManyParts * k].x * first[k];
+    for (uint32_t k0 = kMergeBatch; k0 < nq; k0 += kMergeBatch) {
+        float ob[kMergeBatch];
+#pragma unroll
+        for (int k = 0; k < kMergeBatch; k++) ob[k] = po[(size_t)min(q + kManyParts * (k0 + k), ns - 1) * pos];
+#pragma unroll
+        for (int k = 0; k < kMergeBatch; k++)
+            if (k0 + k < nq) A += wl[q + kManyParts * (k0 + k)].x * ob[k];
+    }
+    part_sum[q][d] = A;
+    __syncthreads();
+    if (q == 0) {
+        float t = part_sum[0][d];
+#pragma unroll
+        for (int p = 1; p < kManyParts; p++) t += part_sum[p][d];
+        a.out[(size_t)unit * 128 + d] = t / L;
+    }
+}
+
 }  // namespace kvattn_dev
 
 // ---------------------------------------------------------------------------
@@ -463,9 +532,16 @@ hipError_t kvattn_launch_split(const SplitArgs &a, uint32_t n_items, uint32_t n_
 
 hipError_t kvattn_launch_merge(const MergeArgs &a, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
     (void)hipGetLastError();
-    // few units (decode, verify): one per workgroup, the most parallel
-    // latency; thousands (prefill chunks): four per workgroup
-    if (a.units >= 1024 && a.n_splits <= kvattn_dev::kMergeWideSplits) {
+    // many splits (one per page): one unit per 512-thread workgroup; few
+    // units (decode, verify): one per workgroup, the most parallel latency;
+    // thousands (prefill chunks): four per workgroup
+    if (a.n_splits >= kvattn_dev::kManyMinSplits) {
+        dim3 grid(a.units), block(128 * kvattn_dev::kManyParts);
+        if (ev_start)
+            hipExtLaunchKernelGGL(kvattn_dev::merge_many_kernel, grid, block, 0, s, ev_start, ev_stop, 0, a);
+        else
+            hipLaunchKernelGGL(kvattn_dev::merge_many_kernel, grid, block, 0, s, a);
+    } else if (a.units >= 1024 && a.n_splits <= kvattn_dev::kMergeWideSplits) {
         constexpr int U = kvattn_dev::kMergeWideUnits;
         dim3 grid((a.units + U - 1) / U), block(128 * U);
         if (ev_start)

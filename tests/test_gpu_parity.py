@@ -66,6 +66,8 @@ CASES = [
     (1000, 8, 1, 100, "prefill", 0),
     (256, 16, 2, 256, "prefill", 0),     # row 0 sees one key
     (3000, 40, 8, 37, "prefill", 0),
+    (100 * 256 - 17, 40, 8, 4, "verify", 1),   # 100 splits: the many-split merge
+    (300 * 256, 8, 1, 1, "decode", 1),         # 300 splits
 ]
 
 
