@@ -66,6 +66,8 @@ def parse():
                          "layer (decode / verify workloads)")
     ap.add_argument("--split-pages", type=int, default=0,
                     help="pages per split for calls of <= 32 rows per KV head (0: the library's choice)")
+    ap.add_argument("--chunk-slots", type=int, default=0,
+                    help="streamed workloads: ring slots per streamed chunk (0: the library's default, 16)")
     ap.add_argument("--deterministic", action="store_true",
                     help="fixed chunk order inside splits (same bits every call) instead of waves claiming chunks")
     ap.add_argument("--adaptive", action="store_true",
@@ -79,7 +81,8 @@ def parse():
 
 
 # --------------------------------------------------------------------------- setup
-def build(w, width, n_layers, torch, kv, inputs, types=KV_TYPES["q8_0-q4_0"], split_pages=0, deterministic=False):
+def build(w, width, n_layers, torch, kv, inputs, types=KV_TYPES["q8_0-q4_0"], split_pages=0, deterministic=False,
+          chunk_slots=0):
     """Create the handle and place every layer's pages.  Returns (handle,
     queries, outputs, call kind, rows, host histories)."""
     dev = "cuda"
@@ -92,7 +95,7 @@ def build(w, width, n_layers, torch, kv, inputs, types=KV_TYPES["q8_0-q4_0"], sp
     copy = torch.cuda.Stream()
     params = kv.make_params(n_layers, w.n_q_heads, w.n_kv_heads, n_pool, n, max(rows, 1),
                             n_ring_slots=w.ring_slots, k_type=types[0], v_type=types[1], split_pages=split_pages,
-                            deterministic=int(deterministic))
+                            deterministic=int(deterministic), chunk_slots=chunk_slots)
     h = kv.allocate(params, compute_stream=compute, copy_stream=copy)
     pb = kv.page_bytes(params)
     pool = h.pool.view(n_pool, pb)
@@ -410,7 +413,7 @@ def main():
     types = KV_TYPES[args.kv_types]
     default_types = args.kv_types == "q8_0-q4_0"
     h, qs, outs, kind, rows, hist = build(w, args.width, n_layers, torch, kv, inputs, types, args.split_pages,
-                                          args.deterministic)
+                                          args.deterministic, args.chunk_slots)
     log(f"bench: inputs ready in {time.perf_counter() - t0:.1f} s; {kind} rows={rows}")
     stream = h.compute_stream
 
@@ -436,7 +439,7 @@ def main():
     torch.cuda.synchronize()
     log(f"bench: warmup {args.warmup} done; timing {args.steps} steps")
 
-    chunks = -(-(w.n_pages - w.n_resident) // 16) if streamed else 0
+    chunks = -(-(w.n_pages - w.n_resident) // (args.chunk_slots or 16)) if streamed else 0
     launches_per_pass = n_layers * (chunks + 3)
     if graph is None:
         h.profile(max(1, args.steps) * launches_per_pass)
@@ -511,7 +514,8 @@ def main():
                    "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": 128, "rows": rows,
                    "kv_types": types[2], "mode": mode, "split_pages": args.split_pages or "auto",
                    "chunk_order": "static" if args.deterministic else "claimed in splits of >= 96 chunks, else static",
-                   "resident_fraction": w.resident_fraction, "ring_slots": w.ring_slots},
+                   "resident_fraction": w.resident_fraction, "ring_slots": w.ring_slots,
+                   "chunk_slots": (args.chunk_slots or 16) if streamed else None},
         "gpu": gpu_info(torch),
         "layers_per_s": round(n_layers / (ms_per_step / 1e3), 1),
         "kv_gbps": round(kv_gbps, 1),
