@@ -182,3 +182,42 @@ def test_pair_full_size_prefill_rows(pair):
     say(f"  rows {rows}: max-abs err {err:.3e}")
     assert err <= TOL
     h.destroy()
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=IDS)
+@pytest.mark.parametrize("T", [32, 64])
+def test_pair_small_pages(pair, T):
+    """Pages of 32 and 64 tokens per pair: decode, 6-row verify, a 70-row
+    prefill chunk and an append across page boundaries, all against the
+    oracle reading the same pages."""
+    N, Hq, Hkv = 1000, 16, 2
+    say(f"case types k={pair[0]} v={pair[1]} page_tokens={T}")
+    kvl = inputs.draw_layer(N, Hkv, 0, 71, pad="garbage", page_tokens=T, k_type=pair[0], v_type=pair[1])
+    n = kvl.pages.shape[0]
+    extra = 3
+    h = handle(Hq, Hkv, n + extra + 2, n + extra, 80, page_tokens=T, k_type=pair[0], v_type=pair[1])
+    table = np.random.default_rng(T).permutation(n + 2)[:n].astype(np.uint32)
+    place(h, 0, kvl, table, page_tokens=T)
+    for W, kind in [(1, "decode"), (6, "verify"), (70, "prefill")]:
+        q = inputs.draw_queries(W, Hq, W, 71)
+        got = run(h, 0, q, W, kind)
+        err = np.max(np.abs(got - oracle_out(kvl, q, Hq, Hkv, page_tokens=T)))
+        say(f"  {kind} W={W}: max-abs err {err:.3e}")
+        assert err <= TOL
+    # grow by 2 pages' worth of rows into fresh pool pages, then decode
+    R = 2 * T - 7
+    free = np.setdiff1d(np.arange(n + extra + 2), table)[: -(-(N + R) // T) - n].astype(np.uint32)
+    g = torch.Generator().manual_seed(T)
+    k = torch.randn(R, Hkv, 128, generator=g)
+    v = torch.randn(R, Hkv, 128, generator=g)
+    h.append(0, k.cuda(), v.cuda(), R, free)
+    n1 = -(-(N + R) // T)
+    pages = np.stack([h.debug_read_page(0, P) for P in range(n1)])
+    q = inputs.draw_queries(1, Hq, 9, 71)
+    got = run(h, 0, q, 1, "decode")
+    ref, _ = oracle.attend_paged(np.arange(n1, dtype=np.uint32), N + R, T, Hq, Hkv, q.numpy(), inputs.scale_for(),
+                                 pool=pages, k_type=pair[0], v_type=pair[1])
+    err = np.max(np.abs(got - ref))
+    say(f"  decode after append of {R} rows: max-abs err {err:.3e}")
+    assert err <= TOL
+    h.destroy()
