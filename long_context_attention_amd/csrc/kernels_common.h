@@ -77,6 +77,46 @@ __device__ __forceinline__ half8 q4_to_half8(uint32_t w) {
     return half8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
+// 8 int8 codes -> 8 f16 of c + 1152 (exact, byte i -> element i), without
+// the bias subtraction: the split kernel starts each block's Q . K^T sum at
+// -1152 * sum(q) instead, which removes it exactly up to fp32 rounding of
+// that one term.
+__device__ __forceinline__ half8 q8_biased_half8(uint32_t w0, uint32_t w1) {
+    const uint32_t k64 = 0x64646464u;
+    const uint32_t u0 = w0 ^ 0x80808080u, u1 = w1 ^ 0x80808080u;
+    const uint4 r{__builtin_amdgcn_perm(k64, u0, 0x04010400u), __builtin_amdgcn_perm(k64, u0, 0x04030402u),
+                  __builtin_amdgcn_perm(k64, u1, 0x04010400u), __builtin_amdgcn_perm(k64, u1, 0x04030402u)};
+    return __builtin_bit_cast(half8, r);
+}
+
+// 8 Q4_0 codes in one dword -> 8 exact f16 (n - 8) in the order of
+// q4_swizzle: (w & 0x000F000F) | 0x64006400 is the f16 pair 1024 + n of the
+// low nibbles of bytes 0 and 2, the mask 0x00F000F0 gives 1024 + 16 n for
+// their high nibbles (scaled back by a packed fma), and the same on w >> 8
+// covers bytes 1 and 3: nine instructions where the byte-permute form takes
+// eleven.
+// (w & mask) | bits in one v_and_or_b32 (the compiler splits it in two when
+// both constants are literals)
+__device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t mask, uint32_t bits) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(mask), "v"(bits));
+    return r;
+}
+
+__device__ __forceinline__ half8 q4_swz_half8(uint32_t w) {
+    const uint32_t k64 = 0x64006400u, w8 = w >> 8;
+    const half2v bias_lo = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const half2v sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f}, bias_hi = {(_Float16)-72.0f, (_Float16)-72.0f};
+    const half2v a = bits_h2(and_or(w, 0x000F000Fu, k64)) - bias_lo;   // elements 0, 2
+    const half2v b = bits_h2(and_or(w8, 0x000F000Fu, k64)) - bias_lo;  // 1, 3
+    const half2v c = __builtin_elementwise_fma(bits_h2(and_or(w, 0x00F000F0u, k64)), sixteenth, bias_hi);   // 4, 6
+    const half2v d = __builtin_elementwise_fma(bits_h2(and_or(w8, 0x00F000F0u, k64)), sixteenth, bias_hi);  // 5, 7
+    return half8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+// element e of q4_swz_half8 holds code q4_swizzle(e) of the dword (an
+// involution: 0 2 1 3 4 6 5 7)
+__host__ __device__ constexpr int q4_swizzle(int e) { return (e & 4) | ((e & 1) << 1) | ((e >> 1) & 1); }
+
 __device__ __forceinline__ float h2f_lo(uint32_t u) { return (float)bits_h2(u).x; }
 __device__ __forceinline__ float h2f_hi(uint32_t u) { return (float)bits_h2(u).y; }
 
@@ -246,14 +286,18 @@ __device__ __forceinline__ void read_kcodes(const uint8_t *stg, int lane, uint32
 }
 
 // The lane's K operand (8 f16: key 16 tt + c16, dims 32 b + 8 g .. +8) of
-// key tile tt and block b, exact: Q8_0 c, Q4_0 n - 8, F16 the value.
-template <int KT>
+// key tile tt and block b: Q8_0 c, or c + 1152 when BIASED (the bias then
+// leaves through the accumulator start, RowState::kcorr), Q4_0 n - 8 in
+// q4_swizzle order of the dims (the query fragment follows it), F16 the
+// value.
+template <int KT, bool BIASED>
 __device__ __forceinline__ half8 k_frag(const uint32_t *kq, int tt, int b) {
     if constexpr (KT == kTypeQ8_0) {
         const uint32_t *w = kq + 8 * tt + 4 * (b >> 1) + 2 * (b & 1);
+        if constexpr (BIASED) return q8_biased_half8(w[0], w[1]);
         return q8_to_half8(w[0], w[1]);
     } else if constexpr (KT == kTypeQ4_0) {
-        return q4_to_half8(kq[4 * tt + b]);
+        return q4_swz_half8(kq[4 * tt + b]);
     } else {
         const uint32_t *w = kq + 16 * tt + 4 * b;
         return __builtin_bit_cast(half8, uint4{w[0], w[1], w[2], w[3]});
@@ -289,11 +333,12 @@ __device__ __forceinline__ void read_vcodes(const uint8_t *stg, int lane, uint32
 }
 
 // The lane's V^T operand of 16-dim tile n (8 f16 over the lane's key slots),
-// exact: Q4_0 n - 8, Q8_0 c, F16 the value.
+// exact: Q4_0 n - 8 (slots in q4_swizzle order; the P' operand follows it),
+// Q8_0 c, F16 the value.
 template <int VT>
 __device__ __forceinline__ half8 v_frag(const uint32_t *vq, int n) {
     if constexpr (VT == kTypeQ4_0) {
-        return q4_to_half8(vq[n]);
+        return q4_swz_half8(vq[n]);
     } else if constexpr (VT == kTypeQ8_0) {
         return q8_to_half8(vq[2 * n], vq[2 * n + 1]);
     } else {
@@ -329,6 +374,7 @@ constexpr float kRescale = 8.0f;
 // Per-wave state of one tile of 16 query rows (the lane's row is c16).
 struct RowState {
     half8 qf[4];     // B operand of S^T = K Q^T, block b
+    floatx4 kcorr[4];  // biased Q8_0 keys: start of block b's sum, -1152 * (sum of the row's qf over it)
     int row_pos;     // position of the lane's row; -1 = padding row
     float m_ref;     // softmax reference (log2 units), uniform per row
     float l_run;     // lane's share of the softmax denominator
@@ -338,6 +384,12 @@ struct RowState {
 // The softmax reference a tile's scores are taken relative to: the row's
 // lazy reference, or 0 before the first key.
 __device__ __forceinline__ float score_ref(const RowState &st) { return st.m_ref == kNegInf ? 0.f : st.m_ref; }
+
+// Q8_0 keys enter the matrix cores biased (c + 1152, no subtraction) in
+// single-tile blocks; two-tile blocks keep the subtraction, whose 32 packed
+// subtracts per chunk serve both tiles, instead of 32 more live registers.
+template <int NT, int KT>
+constexpr bool kBiasedK = KT == kTypeQ8_0 && NT == 1;
 
 // Scores of one chunk for NT row tiles, relative to the tile's reference:
 // s[t][4tt + v] = score(key 16tt + 4g + v of the chunk) - score_ref(tile t),
@@ -360,7 +412,7 @@ __device__ __forceinline__ void chunk_scores(const RowState (&st)[NT], const uin
             for (int t = 0; t < NT; t++) d[t] = floatx4{-ref[t], -ref[t], -ref[t], -ref[t]};
 #pragma unroll
             for (int b = 0; b < 4; b++) {
-                const half8 kf = k_frag<KT>(kq, tt, b);
+                const half8 kf = k_frag<KT, kBiasedK<NT, KT>>(kq, tt, b);
 #pragma unroll
                 for (int t = 0; t < NT; t++) d[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, st[t].qf[b], d[t], 0, 0, 0);
             }
@@ -373,10 +425,12 @@ __device__ __forceinline__ void chunk_scores(const RowState (&st)[NT], const uin
             floatx4 d[4][NT];
 #pragma unroll
             for (int b = 0; b < 4; b++) {
-                const half8 kf = k_frag<KT>(kq, tt, b);
+                const half8 kf = k_frag<KT, kBiasedK<NT, KT>>(kq, tt, b);
 #pragma unroll
-                for (int t = 0; t < NT; t++)
-                    d[b][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, st[t].qf[b], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                for (int t = 0; t < NT; t++) {
+                    const floatx4 c0 = kBiasedK<NT, KT> ? st[t].kcorr[b] : floatx4{0.f, 0.f, 0.f, 0.f};
+                    d[b][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, st[t].qf[b], c0, 0, 0, 0);
+                }
             }
 #pragma unroll
             for (int t = 0; t < NT; t++)
@@ -446,6 +500,35 @@ __device__ __forceinline__ void sanitize_vscales(uint8_t *stg, int lane, uint32_
     *w = v;
 }
 
+// binary16 of p * (half H of the binary16 pair s), written into the low
+// (mix_lo) or high (mix_hi) half of a dword: one v_fma_mix per element.
+template <int H>
+__device__ __forceinline__ uint32_t mix_lo(float p, uint32_t s) {
+    uint32_t r;
+    if constexpr (H)
+        asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "=v"(r) : "v"(p), "v"(s));
+    else
+        asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "=v"(r) : "v"(p), "v"(s));
+    return r;
+}
+template <int H>
+__device__ __forceinline__ uint32_t mix_hi(uint32_t r, float p, uint32_t s) {
+    if constexpr (H)
+        asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "+v"(r) : "v"(p), "v"(s));
+    else
+        asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "+v"(r) : "v"(p), "v"(s));
+    return r;
+}
+
+// Dword k of the P' operand of one value block: slots 2k, 2k + 1 of the
+// operand (key slots in q4_swizzle order for Q4_0 values), P * d_V each.
+template <int VT, int K>
+__device__ __forceinline__ uint32_t pv_pair(const float (&p)[8], const uint32_t *vdb) {
+    constexpr int i0 = VT == kTypeQ4_0 ? q4_swizzle(2 * K) : 2 * K;
+    constexpr int i1 = VT == kTypeQ4_0 ? q4_swizzle(2 * K + 1) : 2 * K + 1;
+    return mix_hi<i1 & 1>(mix_lo<i0 & 1>(p[i0], vdb[i0 >> 1]), p[i1], vdb[i1 >> 1]);
+}
+
 // Softmax step of one chunk for one row tile from its relative scores: lazy
 // reference update, probabilities P = 2^s, the denominator, and the P'
 // operands: P * d_V per value block for block V types, P itself for F16
@@ -468,11 +551,12 @@ __device__ __forceinline__ void chunk_probs(RowState &st, float (&s)[8], const u
     } else {
 #pragma unroll
         for (int b = 0; b < 4; b++) {
-            float e[8];
-#pragma unroll
-            for (int i = 0; i < 8; i++) e[i] = __builtin_fmaf(p[i], half_of(vd + 4 * b, i), 0.0f);
-            pf[b] = half8{(_Float16)e[0], (_Float16)e[1], (_Float16)e[2], (_Float16)e[3],
-                          (_Float16)e[4], (_Float16)e[5], (_Float16)e[6], (_Float16)e[7]};
+            uint4 w;
+            w.x = pv_pair<VT, 0>(p, vd + 4 * b);
+            w.y = pv_pair<VT, 1>(p, vd + 4 * b);
+            w.z = pv_pair<VT, 2>(p, vd + 4 * b);
+            w.w = pv_pair<VT, 3>(p, vd + 4 * b);
+            pf[b] = __builtin_bit_cast(half8, w);
         }
     }
 }

@@ -142,15 +142,30 @@ __global__ __launch_bounds__((64 * SplitCfg<NT, KT, VT>::waves), 1) void split_k
     if (pend != kNone) pend_entry = table_at(a.page_table, pend / cpp);
 
     // ---- query fragments: lane (row c16, group g) holds dims 32b + 8g .. +8
-    // of block b, pre-scaled by softmax_scale * log2(e)
+    // of block b (in q4_swizzle order for Q4_0 keys, matching their operand),
+    // pre-scaled by softmax_scale * log2(e).  Biased Q8_0 keys enter the
+    // matrix cores as c + 1152, so each block's sum starts at -1152 times the
+    // sum of the row's rounded query over the block (the four groups' shares
+    // added across lanes in a fixed order).
 #pragma unroll
     for (int t = 0; t < NT; t++)
 #pragma unroll
         for (int b = 0; b < 4; b++) {
             const float4 x = qraw[t][2 * b], y = qraw[t][2 * b + 1];
-            st[t].qf[b] = half8{(_Float16)(x.x * a.qscale), (_Float16)(x.y * a.qscale), (_Float16)(x.z * a.qscale),
-                                (_Float16)(x.w * a.qscale), (_Float16)(y.x * a.qscale), (_Float16)(y.y * a.qscale),
-                                (_Float16)(y.z * a.qscale), (_Float16)(y.w * a.qscale)};
+            const float v[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+            half8 h;
+#pragma unroll
+            for (int e = 0; e < 8; e++) h[e] = (_Float16)(v[KT == kTypeQ4_0 ? q4_swizzle(e) : e] * a.qscale);
+            st[t].qf[b] = h;
+            if constexpr (kBiasedK<NT, KT>) {
+                float sum = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; e++) sum += (float)h[e];
+                sum += __shfl_xor(sum, 16);
+                sum += __shfl_xor(sum, 32);
+                const float c0 = -1152.0f * sum;
+                st[t].kcorr[b] = floatx4{c0, c0, c0, c0};
+            }
         }
 
     // the fragments exist before the first ring load is issued
