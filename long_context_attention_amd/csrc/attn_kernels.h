@@ -4,6 +4,11 @@
 #include <stddef.h>
 #include <stdint.h>
 
+// Page entries that travel with the launch: the first kPrePages entries of
+// each of the first kPreSplits splits, so a workgroup's first loads need no
+// page-table read (one dependent memory round trip less at the start).
+constexpr uint32_t kPreSplits = 64, kPrePages = 4;
+
 struct SplitArgs {
     const uint8_t *pool;          // resident pool pages
     const uint8_t *ring;          // ring slots
@@ -26,6 +31,11 @@ struct SplitArgs {
     const float *q;               // [W][Hq][128]
     float *part_o;                // [splits][W*Hq][128]
     float *part_ml;               // [splits][W*Hq][2]
+    // split kernel, range splits s < n_pre_splits: pre_entries[s * kPrePages
+    // + k] is the device entry of logical page (s * split_chunks * 32) / T + k
+    // (0 past the last page); page-list and wide launches set n_pre_splits = 0
+    uint32_t n_pre_splits;
+    uint32_t pre_entries[kPreSplits * kPrePages];
 };
 
 struct MergeArgs {

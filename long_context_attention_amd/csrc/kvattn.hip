@@ -177,6 +177,7 @@ struct LayerState {
     std::vector<uint32_t> resident;   // logical pages, ascending
     std::vector<uint32_t> streamed;   // logical pages, ascending (ordinal order)
     std::vector<uint32_t> table;      // the caller's entries, per logical page
+    std::vector<uint32_t> dev;        // the device entries, per logical page
 };
 
 }  // namespace
@@ -384,6 +385,15 @@ int attend_resident(kvattn_t h, uint32_t layer, const float *q, uint32_t W, floa
     Plan pl = plan_resident(h->p, L.n_tokens, L.n_pages, W, h->n_cus);
     SplitArgs a = base_args(h, layer, W, q);
     a.split_chunks = pl.split_chunks;
+    // split kernel: the first page entries of the first splits travel with
+    // the launch
+    const uint32_t cpp = h->p.page_tokens / 32;
+    a.n_pre_splits = pl.wide ? 0u : std::min<uint32_t>(pl.n_splits, kPreSplits);
+    for (uint32_t s = 0; s < a.n_pre_splits; s++) {
+        const uint32_t p0 = (uint32_t)((uint64_t)s * pl.split_chunks / cpp);
+        for (uint32_t k = 0; k < kPrePages; k++)
+            a.pre_entries[s * kPrePages + k] = p0 + k < L.n_pages ? L.dev[p0 + k] : 0u;
+    }
     // long splits let waves claim chunks (balances them, measured faster);
     // short ones keep the static order, which was as fast or faster there
     a.dynamic_order = (!h->p.deterministic && pl.split_chunks >= kClaimMinChunks) ? 1u : 0u;
@@ -746,6 +756,7 @@ int install_layer(kvattn_t h, uint32_t layer, const uint32_t *page_table, uint32
     }
     L.n_resident = (uint32_t)L.resident.size();
     L.n_streamed = (uint32_t)L.streamed.size();
+    L.dev = dev;
     std::vector<uint32_t> list(L.resident);
     list.insert(list.end(), L.streamed.begin(), L.streamed.end());
     HIP_TRY(h, hipMemcpy(h->d_table(layer), dev.data(), n_pages * sizeof(uint32_t), hipMemcpyHostToDevice));

@@ -43,6 +43,19 @@ __global__ __launch_bounds__((64 * SplitCfg<NT, KT, VT>::waves), 1) void split_k
     constexpr int kWaveRingBytes = SplitCfg<NT, KT, VT>::ring_bytes;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // rings; reused by the combine
 
+    // ---- every argument the prologue reads, in one round trip: the split's
+    // launch-carried page entries (index clamped into the array) and the
+    // scalar fields, all loaded before the first wait (left to itself the
+    // compiler loads them in dependent batches, one round trip each)
+    const uint32_t pre_base = min((uint32_t)blockIdx.x, kPreSplits - 1) * kPrePages;
+    const uint4 pre{a.pre_entries[pre_base], a.pre_entries[pre_base + 1], a.pre_entries[pre_base + 2],
+                    a.pre_entries[pre_base + 3]};
+    asm volatile("" ::"s"(a.page_list), "s"(a.list_offset), "s"(a.n_tokens), "s"(a.T), "s"(a.W), "s"(a.G), "s"(a.Hq),
+                 "s"(a.split_chunks), "s"(a.dynamic_order), "s"(a.q), "s"(a.qscale), "s"(a.n_pre_splits),
+                 "s"(a.page_table), "s"(a.pool), "s"(a.ring), "s"(a.page_bytes), "s"(a.sec_kd), "s"(a.sec_vc),
+                 "s"(a.sec_vd), "s"(a.ring_base), "s"(a.n_ring_slots), "s"(pre.x), "s"(pre.y), "s"(pre.z),
+                 "s"(pre.w));
+
     const int lane = threadIdx.x & 63;
     // wave index, made visibly uniform so chunk bookkeeping stays scalar
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -65,6 +78,8 @@ __global__ __launch_bounds__((64 * SplitCfg<NT, KT, VT>::waves), 1) void split_k
         c_begin = blockIdx.x * a.split_chunks;
         c_end = min(c_begin + a.split_chunks, n_chunks_all);
     }
+    const uint32_t p0 = c_begin / cpp;  // first page of the split
+    const bool pre_ok = !a.page_list && blockIdx.x < a.n_pre_splits;
     // chunks whose keys every row sees (keys <= n_tokens - W) need no mask
     const uint32_t clean_end = (a.n_tokens - a.W + 1) >> 5;
     // Chunk order.  A wave's first kStages - 1 chunks are first + kSplitWaves
@@ -76,10 +91,6 @@ __global__ __launch_bounds__((64 * SplitCfg<NT, KT, VT>::waves), 1) void split_k
     const uint32_t first = c_begin + wave;
     __shared__ uint32_t next_claim;
     const bool dynamic = a.dynamic_order != 0;
-    if (dynamic) {
-        if (threadIdx.x == 0) next_claim = c_begin + kSplitWaves * (kStages - 1);
-        __syncthreads();
-    }
     uint32_t static_k = 0;  // the wave's next index in the static sequence
     auto next_chunk = [&]() -> uint32_t {
         uint32_t c;
@@ -96,14 +107,20 @@ __global__ __launch_bounds__((64 * SplitCfg<NT, KT, VT>::waves), 1) void split_k
 
     uint8_t *ring = smem + wave * kWaveRingBytes;
     const uint32_t ring_lds = lds_addr(ring);
+    // the pool and ring bases as loaded above (opaque, so the choice between
+    // them is not turned back into a load of one of the two arguments)
+    const uint8_t *pool_base = a.pool, *ring_base = a.ring;
+    asm volatile("" : "+s"(pool_base), "+s"(ring_base));
     auto issue = [&](uint32_t chunk, uint32_t entry, uint32_t stage) {
         const uint32_t jj0 = (chunk - (chunk / cpp) * cpp) << 5;
-        issue_chunk<KT, VT>(a, page_base(a, entry), kvh, jj0, lane, ring_lds + stage * C::bytes);
+        issue_chunk<KT, VT, true>(a, page_base(a, pool_base, ring_base, entry), kvh, jj0, lane, ring_lds + stage * C::bytes);
     };
 
-    // ---- query loads and the first page entries, one round trip together;
-    // the queries are converted before the ring prologue, so no wait on them
-    // (the compiler's vmcnt counts only its own loads) covers the ring loads
+    // ---- query loads, then the ring prologue: the first kStages - 1 chunks
+    // of every wave go out without waiting for the queries.  Loads return in
+    // issue order, so the compiler's wait before the query conversion (it
+    // counts only its own loads) also waits for those chunks, which the first
+    // compute needs anyway.
     RowState st[NT];
     float4 qraw[NT][8];
 #pragma unroll
@@ -135,11 +152,19 @@ __global__ __launch_bounds__((64 * SplitCfg<NT, KT, VT>::waves), 1) void split_k
 #pragma unroll
     for (int i = 0; i < kStages - 1; i++) {
         q[i] = next_chunk();
-        entry0[i] = q[i] != kNone ? table_at(a.page_table, q[i] / cpp) : 0u;
+        entry0[i] = q[i] != kNone ? split_entry(a, pre_ok, pre, p0, q[i] / cpp) : 0u;
     }
     q[kStages - 1] = kNone;
+#pragma unroll
+    for (int i = 0; i < kStages - 1; i++)
+        if (q[i] != kNone) issue(q[i], entry0[i], i);
+    // dynamic order: the counter is set before the first claim
+    if (dynamic) {
+        if (threadIdx.x == 0) next_claim = c_begin + kSplitWaves * (kStages - 1);
+        __syncthreads();
+    }
     pend = next_chunk();
-    if (pend != kNone) pend_entry = table_at(a.page_table, pend / cpp);
+    if (pend != kNone) pend_entry = split_entry(a, pre_ok, pre, p0, pend / cpp);
 
     // ---- query fragments: lane (row c16, group g) holds dims 32b + 8g .. +8
     // of block b (in q4_swizzle order for Q4_0 keys, matching their operand),
@@ -168,17 +193,6 @@ __global__ __launch_bounds__((64 * SplitCfg<NT, KT, VT>::waves), 1) void split_k
             }
         }
 
-    // the fragments exist before the first ring load is issued
-#pragma unroll
-    for (int t = 0; t < NT; t++)
-#pragma unroll
-        for (int b = 0; b < 4; b++) asm volatile("" ::"v"(st[t].qf[b]) : "memory");
-
-    // ---- ring prologue: the first kStages - 1 chunks in flight; page
-    // entries (scalar loads) run one chunk ahead of their use
-#pragma unroll
-    for (int i = 0; i < kStages - 1; i++)
-        if (q[i] != kNone) issue(q[i], entry0[i], i);
 
     if (q[0] != kNone) {
         uint32_t pv_vq[C::vw];
@@ -192,7 +206,7 @@ __global__ __launch_bounds__((64 * SplitCfg<NT, KT, VT>::waves), 1) void split_k
                 issue(pend, pend_entry, stage == 0 ? kStages - 1 : stage - 1);
                 q[kStages - 1] = pend;
                 pend = next_chunk();
-                if (pend != kNone) pend_entry = table_at(a.page_table, pend / cpp);
+                if (pend != kNone) pend_entry = split_entry(a, pre_ok, pre, p0, pend / cpp);
             }
             uint32_t newer = 0;  // chunks issued after this one
 #pragma unroll

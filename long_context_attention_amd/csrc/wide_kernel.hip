@@ -200,7 +200,7 @@ __global__ __launch_bounds__((64 * WAVES), 1) void wide_kernel(const SplitArgs a
         const uint32_t dst = lds_addr(raw_ring[p & 3]);
 #pragma unroll
         for (int i = 0; i < kLoadsMax; i++)
-            if (wave + WAVES * i < C::dma) issue_chunk_part<KT, VT>(a, base, kvh, jj0, lane, dst, wave + WAVES * i);
+            if (wave + WAVES * i < C::dma) issue_chunk_part<KT, VT, false>(a, base, kvh, jj0, lane, dst, wave + WAVES * i);
     };
     static_assert(2 * kLoadsMax <= 8, "wait_vmcnt_upto range");
     auto n_valid_of = [&](uint32_t p) {
