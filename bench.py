@@ -75,6 +75,9 @@ def parse():
                          "same device-page budget and time its final split")
     ap.add_argument("--kv-types", choices=sorted(KV_TYPES), default="q8_0-q4_0",
                     help="K/V element-type pair of the cache (default: the workloads' Q8_0 K / Q4_0 V)")
+    ap.add_argument("--hbm-ceiling", action="store_true",
+                    help="only measure the plain-read ceiling of the device for the workload's quantised-KV bytes "
+                         "per layer (64 buffers, libkvattn_probe) and print it as JSON")
     ap.add_argument("--h2d-ceiling", action="store_true",
                     help="only measure the host-to-device ceiling (pinned copies) and print it as JSON")
     return ap.parse_args()
@@ -228,6 +231,34 @@ def h2d_ceiling(torch, mb=436, reps=3):
     return {"contiguous_gbps": round(best, 2), "page_pieces_gbps": round(piece_rate, 2), "bytes": n}
 
 
+def hbm_read_ceiling(bytes_per_launch, n_buffers=64, reps=5):
+    """Plain-read ceiling for one launch reading `bytes_per_launch` (rounded
+    up to 16 B) from one of n_buffers distinct device buffers in turn:
+    microseconds per launch and GB/s for each load policy and grid size of
+    kvattn_probe_read_ceiling (libkvattn_probe.so, a measurement helper
+    beside the attention library)."""
+    import ctypes
+    from long_context_attention_amd import build as hipbuild
+    if not os.path.exists(hipbuild.PROBE_LIB):
+        raise RuntimeError(f"{hipbuild.PROBE_LIB} is missing: run __graft_entry__.build() first")
+    lib = ctypes.CDLL(hipbuild.PROBE_LIB)
+    lib.kvattn_probe_read_ceiling.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32,
+                                              ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+    lib.kvattn_probe_read_ceiling.restype = ctypes.c_int
+    nbytes = -(-int(bytes_per_launch) // 16) * 16
+    us = (ctypes.c_double * 8)()
+    best = ctypes.c_double(0.0)
+    rc = lib.kvattn_probe_read_ceiling(nbytes, n_buffers, reps, us, ctypes.byref(best))
+    if rc != 0:
+        raise RuntimeError(f"kvattn_probe_read_ceiling returned {rc}")
+    grids = [256, 512, 1024, 2048]
+    table = {pol: {str(g): {"us": round(us[i * 4 + j], 3), "gbps": round(nbytes / us[i * 4 + j] / 1e3, 1)}
+                   for j, g in enumerate(grids)} for i, pol in enumerate(["default", "nontemporal"])}
+    return {"bytes_per_launch": nbytes, "buffers": n_buffers, "reps": reps, "best_gbps": round(best.value, 1),
+            "best_frac_hbm_peak": round(best.value / HBM_PEAK_GBPS, 4), "by_policy_and_grid": table,
+            "kernel": "workgroup-contiguous slices, 512 threads, eight 16-byte loads in flight per thread"}
+
+
 # --------------------------------------------------------------------------- adaptive partition
 def adaptive_run(h, w, hist, qs, outs, kind, rows, n_layers, steps, torch, kv, max_iters=8):
     """Closed loop of kvattn_policy_step on the streamed workload: the device
@@ -312,6 +343,10 @@ def gpu_info(torch):
     effort: absent when the tool is not there)."""
     props = torch.cuda.get_device_properties(0)
     info = {"name": props.name, "arch": getattr(props, "gcnArchName", ""), "compute_units": props.multi_processor_count}
+    # under a profiler the child would inherit its preloaded library, which
+    # initialises the GPU before rocm-smi's interpreter replaces the launcher
+    if "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ):
+        return info
     try:
         import subprocess
         out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=10).stdout
@@ -402,6 +437,10 @@ def main():
         print(json.dumps({"h2d_ceiling": h2d_ceiling(torch)}), flush=True)
         return
     w = inputs.WORKLOADS[args.workload]
+    if args.hbm_ceiling:
+        layer_bytes = w.n_tokens * w.n_kv_heads * KV_TYPES[args.kv_types][3]
+        print(json.dumps({"workload": w.name, "hbm_read_ceiling": hbm_read_ceiling(layer_bytes)}), flush=True)
+        return
     n_layers = args.layers or w.n_layers
     streamed = w.resident_fraction < 1.0
     mode = args.mode or ("eager" if streamed else "graph")

@@ -1,4 +1,6 @@
-"""Build the HIP library in-tree: long_context_attention_amd/libkvattn.so (gfx950)."""
+"""Build the HIP libraries in-tree (gfx950): long_context_attention_amd/libkvattn.so
+and the measurement helper libkvattn_probe.so (plain-read ceiling, used by the
+benchmark only)."""
 from __future__ import annotations
 
 import os
@@ -10,6 +12,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvattn.so")
 SOURCES = ["kvattn.hip", "split_kernel.hip", "wide_kernel.hip", "writer_kernel.hip", "copy_kernels.hip"]
 HEADERS = ["attn_kernels.h", "kernels_common.h", "sched.h"]
+PROBE_LIB = os.path.join(HERE, "libkvattn_probe.so")
+PROBE_SOURCES = ["read_probe.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -25,8 +29,14 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
+    _compile(SOURCES, LIB, verbose)
+    _compile(PROBE_SOURCES, PROBE_LIB, verbose)
+    return LIB
+
+
+def _compile(sources, lib, verbose):
+    srcs = [os.path.join(CSRC, s) for s in sources]
+    tmp = lib + ".tmp"
     cmd = [hipcc(), *FLAGS, "-I", os.path.join(os.path.dirname(HERE), "include"), "-o", tmp, *srcs]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -37,16 +47,15 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{errs}")
     if verbose and errs.strip():
         print(errs, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
 
 
 def is_stale() -> bool:
-    if not os.path.exists(LIB):
+    if not os.path.exists(LIB) or not os.path.exists(PROBE_LIB):
         return True
-    t = os.path.getmtime(LIB)
-    deps = [os.path.join(CSRC, f) for f in SOURCES + HEADERS]
-    deps.append(os.path.join(os.path.dirname(HERE), "include", "kvattn.h"))
+    t = min(os.path.getmtime(LIB), os.path.getmtime(PROBE_LIB))
+    deps = [os.path.join(CSRC, f) for f in SOURCES + HEADERS + PROBE_SOURCES]
+    deps += [os.path.join(os.path.dirname(HERE), "include", h) for h in ("kvattn.h", "kvattn_probe.h")]
     return any(os.path.getmtime(d) > t for d in deps)
 
 

@@ -20,9 +20,11 @@
 //
 // Arithmetic (per KV head, 16 keys x 16 query rows per matrix-core tile,
 // v_mfma_f32_16x16x32_f16, fp32 accumulation).  Split kernel:
-//   S^T = K . Q^T     A = K codes (int8 -> exact f16 by a byte permute), one
-//                     MFMA per 32-dim block, each block's fp32 dot scaled by
-//                     its own binary16 d_K before the blocks are summed;
+//   S^T = K . Q^T     A = K codes (int8 -> exact f16 by a byte permute; with
+//                     one row tile left biased by +1152, the bias removed by
+//                     the accumulator's start value), one MFMA per 32-dim
+//                     block, each block's fp32 dot scaled by its own binary16
+//                     d_K before the blocks are summed;
 //                     B = Q * softmax_scale * log2(e), rounded to f16.
 //   O^T += V^T . P'^T A = V codes (n - 8, exact f16), B = P * d_V per (row,
 //                     key, 32-dim block), rounded to f16 once.

@@ -7,8 +7,8 @@
 namespace kvattn_dev {
 
 // ---------------------------------------------------------------------------
-// Split kernel.  A workgroup of 8 waves handles one split (a range of 32-key
-// chunks) of one KV head for a block of 16 * NT query rows; the waves take
+// Split kernel.  A workgroup (12, 8 or 4 waves, SplitCfg) handles one split (a
+// range of 32-key chunks) of one KV head for a block of 16 * NT query rows; the waves take
 // the split's chunks round robin and each computes every row of the block,
 // so a chunk is loaded and dequantised once per block.  Rows of a KV head
 // are ordered (w, hh): r = w * G + hh, hh < G.

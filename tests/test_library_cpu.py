@@ -29,6 +29,27 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(kv.kvattn.EXPORTS)
 
 
+def test_probe_library_exports_and_rejects_bad_arguments():
+    # the plain-read ceiling helper beside the attention library (benchmark only)
+    from long_context_attention_amd import build as hipbuild
+    src = open(os.path.join(ROOT, "include", "kvattn_probe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = sorted(set(re.findall(r"\b(kvattn_[a-z_]+)\s*\(", src)))
+    assert names == ["kvattn_probe_read_ceiling"]
+    P = ctypes.CDLL(hipbuild.PROBE_LIB)
+    fn = P.kvattn_probe_read_ceiling
+    fn.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32, ctypes.POINTER(ctypes.c_double),
+                   ctypes.POINTER(ctypes.c_double)]
+    fn.restype = ctypes.c_int
+    us = (ctypes.c_double * 8)()
+    best = ctypes.c_double()
+    # argument checks come before any device call
+    assert fn(15, 1, 1, us, ctypes.byref(best)) == -1      # not a multiple of 16
+    assert fn(1024, 0, 1, us, ctypes.byref(best)) == -1    # no buffer
+    assert fn(1024, 1, 0, us, ctypes.byref(best)) == -1    # no pass
+    assert fn(1024, 1, 1, None, ctypes.byref(best)) == -1  # no output
+
+
 def test_supported_and_sizes():
     assert kv.supported()
     for pair in [(kv.TYPE_Q8_0, kv.TYPE_Q8_0), (kv.TYPE_Q4_0, kv.TYPE_Q4_0), (kv.TYPE_F16, kv.TYPE_F16)]:
