@@ -28,9 +28,9 @@ struct SplitCfg {
     static constexpr int waves = C::bytes > 12288 ? 4 : (NT == 1 && !big) ? 12 : 8;
     static constexpr int stages = (NT == 1 || big) ? 2 : 3;
     static constexpr int ring_bytes = stages * C::bytes;
-    // the combine after the loop reuses the rings: per wave and row m, l and
-    // a padded 132-float accumulator row
-    static constexpr int combine_bytes = waves * 16 * NT * (2 + 132) * 4;
+    // the combine after the loop reuses the rings: per wave and row of one
+    // 16-row tile, m, l and a padded 132-float accumulator row
+    static constexpr int combine_bytes = waves * 16 * (2 + 132) * 4;
     static constexpr int lds_bytes = waves * ring_bytes > combine_bytes ? waves * ring_bytes : combine_bytes;
     static_assert(lds_bytes <= 163840, "LDS budget");
 };
@@ -219,9 +219,12 @@ __global__ __launch_bounds__((64 * SplitCfg<NT, KT, VT>::waves), 1) void split_k
             float s[NT][8];
             read_kcodes<KT, VT>(stg, lane, kq);
             if constexpr (C::kblk) read_kscales<KT, VT>(stg, grp, kd);
+            // the previous chunk's P.V first: its operands die before this
+            // chunk's scores need registers (measured 0.5 % faster than after
+            // the scores, and about 25 fewer registers)
+            if (have_pv) chunk_pv<NT, VT>(st, pv_vq, pv_pf);
             chunk_scores<NT, KT>(st, kq, kd, s);
             if (c >= clean_end) mask_scores<NT>(st, 32 * c, grp, s);
-            if (have_pv) chunk_pv<NT, VT>(st, pv_vq, pv_pf);
             if constexpr (C::vblk) {
                 if (tail) sanitize_vscales<KT, VT>(stg, lane, a.n_tokens - 32 * c);
                 read_vscales<KT, VT>(stg, grp, vd);
@@ -240,57 +243,56 @@ __global__ __launch_bounds__((64 * SplitCfg<NT, KT, VT>::waves), 1) void split_k
         chunk_pv<NT, VT>(st, pv_vq, pv_pf);
     }
 
-    // ---- combine the waves (fixed wave order) and write the partials; the
-    // rings are reused once every wave is done with its own
+    // ---- combine the waves (fixed wave order) and write the partials, one
+    // 16-row tile at a time; the rings are reused once every wave is done
+    // with its own
     wait_vmcnt<0>();
-    __syncthreads();
-    constexpr int R = 16 * NT;  // rows per block
-    constexpr int OS = 132;     // padded row stride
+    constexpr int OS = 132;  // padded row stride
     float *sm_m = reinterpret_cast<float *>(smem);
-    float *sm_l = sm_m + kSplitWaves * R;
-    float *sm_o = sm_l + kSplitWaves * R;
+    float *sm_l = sm_m + kSplitWaves * 16;
+    float *sm_o = sm_l + kSplitWaves * 16;
+    const uint32_t units = a.W * a.Hq;
 #pragma unroll
     for (int t = 0; t < NT; t++) {
+        __syncthreads();  // rings (first tile) or the previous tile's reads are done
         float l = st[t].l_run;
         l += __shfl_xor(l, 16);
         l += __shfl_xor(l, 32);
-        const int row = 16 * t + c16;
         if (grp == 0) {
-            sm_m[wave * R + row] = st[t].m_ref;
-            sm_l[wave * R + row] = l;
+            sm_m[wave * 16 + c16] = st[t].m_ref;
+            sm_l[wave * 16 + c16] = l;
         }
 #pragma unroll
         for (int n = 0; n < 8; n++)
-            *reinterpret_cast<floatx4 *>(&sm_o[(wave * R + row) * OS + 16 * n + 4 * grp]) = st[t].acc[n];
-    }
-    __syncthreads();
-
-    const uint32_t units = a.W * a.Hq;
-    const uint32_t rows_here = min((uint32_t)R, rows_kv - block_row0);
-    for (uint32_t idx = threadIdx.x; idx < rows_here * 128; idx += blockDim.x) {
-        const uint32_t r = idx >> 7, t = idx & 127;
-        float M = kNegInf;
+            *reinterpret_cast<floatx4 *>(&sm_o[(wave * 16 + c16) * OS + 16 * n + 4 * grp]) = st[t].acc[n];
+        __syncthreads();
+        const uint32_t row0 = block_row0 + 16 * t;
+        const uint32_t rows_here = row0 < rows_kv ? min(16u, rows_kv - row0) : 0u;
+        for (uint32_t idx = threadIdx.x; idx < rows_here * 128; idx += blockDim.x) {
+            const uint32_t r = idx >> 7, d = idx & 127;
+            float M = kNegInf;
 #pragma unroll
-        for (int w = 0; w < kSplitWaves; w++) M = fmaxf(M, sm_m[w * R + r]);
-        float L = 0.f, A = 0.f;
-        if (M != kNegInf) {
+            for (int w = 0; w < kSplitWaves; w++) M = fmaxf(M, sm_m[w * 16 + r]);
+            float L = 0.f, A = 0.f;
+            if (M != kNegInf) {
 #pragma unroll
-            for (int w = 0; w < kSplitWaves; w++) {
-                const float mw = sm_m[w * R + r];
-                if (mw == kNegInf) continue;
-                const float f = fast_exp2(mw - M);
-                L += f * sm_l[w * R + r];
-                A += f * sm_o[(w * R + r) * OS + t];
+                for (int w = 0; w < kSplitWaves; w++) {
+                    const float mw = sm_m[w * 16 + r];
+                    if (mw == kNegInf) continue;
+                    const float f = fast_exp2(mw - M);
+                    L += f * sm_l[w * 16 + r];
+                    A += f * sm_o[(w * 16 + r) * OS + d];
+                }
             }
-        }
-        const uint32_t rk = block_row0 + r;
-        const uint32_t wq = rk / a.G, hh = rk - wq * a.G;
-        const uint32_t unit = wq * a.Hq + kvh * a.G + hh;
-        const size_t pu = (size_t)split * units + unit;
-        a.part_o[pu * 128 + t] = A;
-        if (t == 0) {
-            a.part_ml[pu * 2] = M;
-            a.part_ml[pu * 2 + 1] = L;
+            const uint32_t rk = row0 + r;
+            const uint32_t wq = rk / a.G, hh = rk - wq * a.G;
+            const uint32_t unit = wq * a.Hq + kvh * a.G + hh;
+            const size_t pu = (size_t)split * units + unit;
+            a.part_o[pu * 128 + d] = A;
+            if (d == 0) {
+                a.part_ml[pu * 2] = M;
+                a.part_ml[pu * 2 + 1] = L;
+            }
         }
     }
 }
