@@ -43,6 +43,7 @@ struct MergeArgs {
     const float *part_ml;
     uint32_t n_splits;
     uint32_t units;               // W * Hq
+    uint32_t Hkv, G;              // KV heads, query heads per KV head
     float *out;                   // [W][Hq][128]
 };
 

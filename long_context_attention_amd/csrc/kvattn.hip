@@ -364,6 +364,8 @@ int run_merge(kvattn_t h, uint32_t W, uint32_t n_splits, float *out) {
     m.part_ml = h->part_ml();
     m.n_splits = n_splits;
     m.units = W * h->p.n_q_heads;
+    m.Hkv = h->p.n_kv_heads;
+    m.G = h->p.n_q_heads / h->p.n_kv_heads;
     m.out = out;
     hipEvent_t e0, e1;
     prof_slot(h, 1, &e0, &e1);

@@ -47,7 +47,12 @@ __global__ __launch_bounds__((64 * SplitCfg<NT, KT, VT>::waves), 1) void split_k
     // launch-carried page entries (index clamped into the array) and the
     // scalar fields, all loaded before the first wait (left to itself the
     // compiler loads them in dependent batches, one round trip each)
-    const uint32_t pre_base = min((uint32_t)blockIdx.x, kPreSplits - 1) * kPrePages;
+    // workgroup (KV head, item, row block): consecutive workgroups take
+    // different KV heads, so with the round-robin placement of workgroups on
+    // the 8 XCDs all splits of a KV head (8 heads) share one XCD's L2 with the
+    // merge workgroups of its query heads (merge_unit)
+    const uint32_t item = blockIdx.y;
+    const uint32_t pre_base = min(item, kPreSplits - 1) * kPrePages;
     const uint4 pre{a.pre_entries[pre_base], a.pre_entries[pre_base + 1], a.pre_entries[pre_base + 2],
                     a.pre_entries[pre_base + 3]};
     asm volatile("" ::"s"(a.page_list), "s"(a.list_offset), "s"(a.n_tokens), "s"(a.T), "s"(a.W), "s"(a.G), "s"(a.Hq),
@@ -61,7 +66,7 @@ __global__ __launch_bounds__((64 * SplitCfg<NT, KT, VT>::waves), 1) void split_k
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int grp = lane >> 4;  // 16-lane group
     const int c16 = lane & 15;
-    const uint32_t kvh = blockIdx.y;
+    const uint32_t kvh = blockIdx.x;
     const uint32_t block_row0 = blockIdx.z * (16 * NT);
     const uint32_t rows_kv = a.W * a.G;
     const uint32_t n_chunks_all = (a.n_tokens + 31) >> 5;
@@ -70,16 +75,16 @@ __global__ __launch_bounds__((64 * SplitCfg<NT, KT, VT>::waves), 1) void split_k
     // ---- split -> chunk range
     uint32_t split, c_begin, c_end;
     if (a.page_list) {
-        split = table_at(a.page_list, a.list_offset + blockIdx.x);
+        split = table_at(a.page_list, a.list_offset + item);
         c_begin = split * cpp;
         c_end = min(c_begin + cpp, n_chunks_all);
     } else {
-        split = blockIdx.x;
-        c_begin = blockIdx.x * a.split_chunks;
+        split = item;
+        c_begin = item * a.split_chunks;
         c_end = min(c_begin + a.split_chunks, n_chunks_all);
     }
     const uint32_t p0 = c_begin / cpp;  // first page of the split
-    const bool pre_ok = !a.page_list && blockIdx.x < a.n_pre_splits;
+    const bool pre_ok = !a.page_list && item < a.n_pre_splits;
     // chunks whose keys every row sees (keys <= n_tokens - W) need no mask
     const uint32_t clean_end = (a.n_tokens - a.W + 1) >> 5;
     // Chunk order.  A wave's first kStages - 1 chunks are first + kSplitWaves
@@ -408,12 +413,22 @@ __device__ __forceinline__ void merge_rows(const float *part_ml, const float *pa
 constexpr int kMergeMaxSplits = 4096;
 constexpr int kMergeWideUnits = 4, kMergeWideSplits = 512;
 
+// Unit merged by workgroup b of a one-unit-per-workgroup merge: KV head
+// b mod Hkv first, so that workgroup b runs on the XCD that held the split
+// workgroups of that KV head (the split kernel's grid puts the KV head
+// innermost).  A bijection of [0, units): b = (w * G + hh) * Hkv + kvh.
+__device__ __forceinline__ uint32_t merge_unit(const MergeArgs &a, uint32_t b) {
+    const uint32_t r = b / a.Hkv, kvh = b - r * a.Hkv;
+    const uint32_t w = r / a.G, hh = r - w * a.G;
+    return (w * a.Hkv + kvh) * a.G + hh;
+}
+
 template <int U>
 __global__ __launch_bounds__(128 * U) void merge_kernel(const MergeArgs a) {
     constexpr int kSplits = U == 1 ? kMergeMaxSplits : kMergeWideSplits;
     __shared__ float2 wl[U * kSplits];
     __shared__ float2 row_ml[U];
-    const uint32_t unit0 = blockIdx.x * U;
+    const uint32_t unit0 = U == 1 ? merge_unit(a, blockIdx.x) : blockIdx.x * U;
     const uint32_t nrows = min((uint32_t)U, a.units - unit0);
     merge_rows(a.part_ml, a.part_o, a.out, a.n_splits, a.units, nrows, [=](uint32_t r) { return unit0 + r; }, wl,
                row_ml);
@@ -432,7 +447,7 @@ __global__ __launch_bounds__(128 * kManyParts) void merge_many_kernel(const Merg
     __shared__ float2 wl[kMergeMaxSplits];
     __shared__ float part_sum[kManyParts][128];
     __shared__ float wave_red[2 * kManyParts];
-    const uint32_t unit = blockIdx.x, tid = threadIdx.x, nt = blockDim.x, ns = a.n_splits;
+    const uint32_t unit = merge_unit(a, blockIdx.x), tid = threadIdx.x, nt = blockDim.x, ns = a.n_splits;
     const uint32_t lane = tid & 63, wave = tid >> 6;
     const size_t mls = (size_t)a.units * 2, pos = (size_t)a.units * 128;
     const uint32_t d = tid & 127, q = tid >> 7;
@@ -550,7 +565,7 @@ hipError_t kvattn_split_setup() {
 hipError_t kvattn_launch_split(const SplitArgs &a, uint32_t n_items, uint32_t n_row_blocks, int rt, hipStream_t s,
                                hipEvent_t ev_start, hipEvent_t ev_stop) {
     (void)hipGetLastError();  // clear a stale error so the check below reports this launch
-    const dim3 grid(n_items, a.Hkv, n_row_blocks);
+    const dim3 grid(a.Hkv, n_items, n_row_blocks);  // n_items <= 4096 pages
     const bool ok = with_split_kernel(rt, a.k_type, a.v_type, [&](auto kern, int waves, uint32_t lds) {
         if (ev_start)
             hipExtLaunchKernelGGL(kern, grid, dim3(64 * waves), lds, s, ev_start, ev_stop, 0, a);
