@@ -348,10 +348,13 @@ __device__ __forceinline__ void merge_rows(const float *part_ml, const float *pa
     const float *po0 = po_of(min(tid, n_items - 1)), *po1 = po_of(min(tid + nt, n_items - 1));
     float o0[kMergeBatch], o1[kMergeBatch];
 #pragma unroll
-    for (int k = 0; k < kMergeBatch; k++) {
-        const size_t off = (size_t)min((uint32_t)k, n_splits - 1) * pos;
-        o0[k] = po0[off];
-        o1[k] = po1[off];
+    for (int k = 0; k < kMergeBatch; k++) o0[k] = po0[(size_t)min((uint32_t)k, n_splits - 1) * pos];
+    if (nt < n_items) {  // a second dimension per thread (workgroup-uniform)
+#pragma unroll
+        for (int k = 0; k < kMergeBatch; k++) o1[k] = po1[(size_t)min((uint32_t)k, n_splits - 1) * pos];
+    } else {
+#pragma unroll
+        for (int k = 0; k < kMergeBatch; k++) o1[k] = 0.f;
     }
     if (tid < n_ml) wl[tid] = ml0;
     for (uint32_t i = tid + nt; i < n_ml; i += nt) wl[i] = ml_at(i);
