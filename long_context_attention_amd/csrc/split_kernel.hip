@@ -437,6 +437,34 @@ __global__ __launch_bounds__(128 * U) void merge_kernel(const MergeArgs a) {
                row_ml);
 }
 
+// Merge of calls with few splits (decode, verify: n_splits <= KMAX): one
+// unit per 128-thread workgroup, thread d owns dimension d.  No LDS and no
+// barrier: lane s of each wave loads split s's (m, l); M, the weights w_s and
+// L come from wave reductions, and w_s reaches every lane by v_readlane, so
+// the only wait is the one memory round trip of the loads, all issued first.
+// The arithmetic and its order are those of merge_rows.
+template <int KMAX>
+__global__ __launch_bounds__(128) void merge_small_kernel(const MergeArgs a) {
+    const uint32_t unit = merge_unit(a, blockIdx.x);
+    const uint32_t d = threadIdx.x, lane = threadIdx.x & 63, ns = a.n_splits;
+    const size_t mls = (size_t)a.units * 2, pos = (size_t)a.units * 128;
+    const float *po = a.part_o + (size_t)unit * 128 + d;
+    float o[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; k++) o[k] = po[(size_t)min((uint32_t)k, ns - 1) * pos];
+    const float2 ml = *reinterpret_cast<const float2 *>(a.part_ml + (size_t)min(lane, ns - 1) * mls + (size_t)unit * 2);
+    asm volatile("" ::: "memory");  // every load above is issued before any result is used
+    const bool live = lane < ns && ml.y > 0.f;  // splits with l = 0 (no visible key) are skipped
+    const float M = wave_max(live ? ml.x : kNegInf);
+    const float w = live ? fast_exp2(ml.x - M) : 0.f;
+    const float L = wave_sum(w * ml.y);
+    float A = 0.f;
+#pragma unroll
+    for (int k = 0; k < KMAX; k++)
+        if ((uint32_t)k < ns) A += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k)) * o[k];
+    a.out[(size_t)unit * 128 + d] = A / L;
+}
+
 // Merge of calls with many splits (streamed layers and resident layers split
 // one page per split: one split per page): one unit per workgroup of 512
 // threads.  M, the weights w_s and L as in merge_rows, reduced over the
@@ -597,6 +625,18 @@ hipError_t kvattn_launch_merge(const MergeArgs &a, hipStream_t s, hipEvent_t ev_
             hipExtLaunchKernelGGL(kvattn_dev::merge_kernel<U>, grid, block, 0, s, ev_start, ev_stop, 0, a);
         else
             hipLaunchKernelGGL(kvattn_dev::merge_kernel<U>, grid, block, 0, s, a);
+    } else if (a.n_splits <= 64) {
+        dim3 grid(a.units), block(128);
+        auto go = [&](auto kern) {
+            if (ev_start)
+                hipExtLaunchKernelGGL(kern, grid, block, 0, s, ev_start, ev_stop, 0, a);
+            else
+                hipLaunchKernelGGL(kern, grid, block, 0, s, a);
+        };
+        if (a.n_splits <= 32)
+            go(kvattn_dev::merge_small_kernel<32>);
+        else
+            go(kvattn_dev::merge_small_kernel<64>);
     } else {
         dim3 grid(a.units), block(128);
         if (ev_start)
