@@ -609,16 +609,17 @@ hipError_t kvattn_launch_split(const SplitArgs &a, uint32_t n_items, uint32_t n_
 
 hipError_t kvattn_launch_merge(const MergeArgs &a, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
     (void)hipGetLastError();
-    // many splits (one per page): one unit per 512-thread workgroup; few
-    // units (decode, verify): one per workgroup, the most parallel latency;
-    // thousands (prefill chunks): four per workgroup
+    // many splits (one per page): one unit per 512-thread workgroup; up to
+    // 64 splits (decode, verify, prefill chunks): one unit per 128-thread
+    // workgroup without barriers; otherwise 65..512 splits over thousands of
+    // units four per workgroup, or one per workgroup
     if (a.n_splits >= kvattn_dev::kManyMinSplits) {
         dim3 grid(a.units), block(128 * kvattn_dev::kManyParts);
         if (ev_start)
             hipExtLaunchKernelGGL(kvattn_dev::merge_many_kernel, grid, block, 0, s, ev_start, ev_stop, 0, a);
         else
             hipLaunchKernelGGL(kvattn_dev::merge_many_kernel, grid, block, 0, s, a);
-    } else if (a.units >= 1024 && a.n_splits <= kvattn_dev::kMergeWideSplits) {
+    } else if (a.units >= 1024 && a.n_splits > 64 && a.n_splits <= kvattn_dev::kMergeWideSplits) {
         constexpr int U = kvattn_dev::kMergeWideUnits;
         dim3 grid((a.units + U - 1) / U), block(128 * U);
         if (ev_start)
@@ -633,7 +634,11 @@ hipError_t kvattn_launch_merge(const MergeArgs &a, hipStream_t s, hipEvent_t ev_
             else
                 hipLaunchKernelGGL(kern, grid, block, 0, s, a);
         };
-        if (a.n_splits <= 32)
+        if (a.n_splits <= 8)
+            go(kvattn_dev::merge_small_kernel<8>);
+        else if (a.n_splits <= 16)
+            go(kvattn_dev::merge_small_kernel<16>);
+        else if (a.n_splits <= 32)
             go(kvattn_dev::merge_small_kernel<32>);
         else
             go(kvattn_dev::merge_small_kernel<64>);
