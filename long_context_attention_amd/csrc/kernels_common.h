@@ -312,16 +312,14 @@ __device__ __forceinline__ void read_kcodes(const uint8_t *stg, int lane, uint32
 }
 
 // The lane's K operand (8 f16: key 16 tt + c16, dims 32 b + 8 g .. +8) of
-// key tile tt and block b: Q8_0 c, or c + 1152 when BIASED (the bias then
-// leaves through the accumulator start, RowState::kcorr), Q4_0 n - 8 in
-// q4_swizzle order of the dims (the query fragment follows it), F16 the
-// value.
-template <int KT, bool BIASED>
+// key tile tt and block b: Q8_0 c + 1152 (the bias leaves through the
+// accumulator start, RowState::kcorr), Q4_0 n - 8 in q4_swizzle order of the
+// dims (the query fragment follows it), F16 the value.
+template <int KT>
 __device__ __forceinline__ half8 k_frag(const uint32_t *kq, int tt, int b) {
     if constexpr (KT == kTypeQ8_0) {
         const uint32_t *w = kq + 8 * tt + 4 * (b >> 1) + 2 * (b & 1);
-        if constexpr (BIASED) return q8_biased_half8(w[0], w[1]);
-        return q8_to_half8(w[0], w[1]);
+        return q8_biased_half8(w[0], w[1]);
     } else if constexpr (KT == kTypeQ4_0) {
         return q4_swz_half8(kq[4 * tt + b]);
     } else {
@@ -400,7 +398,7 @@ constexpr float kRescale = 8.0f;
 // Per-wave state of one tile of 16 query rows (the lane's row is c16).
 struct RowState {
     half8 qf[4];     // B operand of S^T = K Q^T, block b
-    floatx4 kcorr[4];  // biased Q8_0 keys: start of block b's sum, -1152 * (sum of the row's qf over it)
+    floatx4 kcorr[4];  // Q8_0 keys: start of block b's sum, -1152 * (sum of the row's qf over it)
     int row_pos;     // position of the lane's row; -1 = padding row
     float m_ref;     // softmax reference (log2 units), uniform per row
     float l_run;     // lane's share of the softmax denominator
@@ -414,8 +412,6 @@ __device__ __forceinline__ float score_ref(const RowState &st) { return st.m_ref
 // Q8_0 keys enter the matrix cores biased (c + 1152, no subtraction); the
 // start values cost 16 registers per row tile (measured +1 to +4 % on the
 // two-tile verify widths, +1.3 % with one tile, against the subtraction).
-template <int NT, int KT>
-constexpr bool kBiasedK = KT == kTypeQ8_0;
 
 // Scores of one chunk for NT row tiles, relative to the tile's reference:
 // s[t][4tt + v] = score(key 16tt + 4g + v of the chunk) - score_ref(tile t),
@@ -438,7 +434,7 @@ __device__ __forceinline__ void chunk_scores(const RowState (&st)[NT], const uin
             for (int t = 0; t < NT; t++) d[t] = floatx4{-ref[t], -ref[t], -ref[t], -ref[t]};
 #pragma unroll
             for (int b = 0; b < 4; b++) {
-                const half8 kf = k_frag<KT, kBiasedK<NT, KT>>(kq, tt, b);
+                const half8 kf = k_frag<KT>(kq, tt, b);
 #pragma unroll
                 for (int t = 0; t < NT; t++) d[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, st[t].qf[b], d[t], 0, 0, 0);
             }
@@ -451,10 +447,10 @@ __device__ __forceinline__ void chunk_scores(const RowState (&st)[NT], const uin
             floatx4 d[4][NT];
 #pragma unroll
             for (int b = 0; b < 4; b++) {
-                const half8 kf = k_frag<KT, kBiasedK<NT, KT>>(kq, tt, b);
+                const half8 kf = k_frag<KT>(kq, tt, b);
 #pragma unroll
                 for (int t = 0; t < NT; t++) {
-                    const floatx4 c0 = kBiasedK<NT, KT> ? st[t].kcorr[b] : floatx4{0.f, 0.f, 0.f, 0.f};
+                    const floatx4 c0 = KT == kTypeQ8_0 ? st[t].kcorr[b] : floatx4{0.f, 0.f, 0.f, 0.f};
                     d[b][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, st[t].qf[b], c0, 0, 0, 0);
                 }
             }

@@ -173,10 +173,10 @@ __global__ __launch_bounds__((64 * SplitCfg<NT, KT, VT>::waves), 1) void split_k
 
     // ---- query fragments: lane (row c16, group g) holds dims 32b + 8g .. +8
     // of block b (in q4_swizzle order for Q4_0 keys, matching their operand),
-    // pre-scaled by softmax_scale * log2(e).  Biased Q8_0 keys enter the
-    // matrix cores as c + 1152, so each block's sum starts at -1152 times the
-    // sum of the row's rounded query over the block (the four groups' shares
-    // added across lanes in a fixed order).
+    // pre-scaled by softmax_scale * log2(e).  Q8_0 keys enter the matrix
+    // cores as c + 1152, so each block's sum starts at -1152 times the sum of
+    // the row's rounded query over the block (the four groups' shares added
+    // across lanes in a fixed order).
 #pragma unroll
     for (int t = 0; t < NT; t++)
 #pragma unroll
@@ -187,7 +187,7 @@ __global__ __launch_bounds__((64 * SplitCfg<NT, KT, VT>::waves), 1) void split_k
 #pragma unroll
             for (int e = 0; e < 8; e++) h[e] = (_Float16)(v[KT == kTypeQ4_0 ? q4_swizzle(e) : e] * a.qscale);
             st[t].qf[b] = h;
-            if constexpr (kBiasedK<NT, KT>) {
+            if constexpr (KT == kTypeQ8_0) {
                 float sum = 0.f;
 #pragma unroll
                 for (int e = 0; e < 8; e++) sum += (float)h[e];
