@@ -274,19 +274,27 @@ __global__ __launch_bounds__((64 * SplitCfg<NT, KT, VT>::waves), 1) void split_k
         const uint32_t row0 = block_row0 + 16 * t;
         const uint32_t rows_here = row0 < rows_kv ? min(16u, rows_kv - row0) : 0u;
         for (uint32_t idx = threadIdx.x; idx < rows_here * 128; idx += blockDim.x) {
-            const uint32_t r = idx >> 7, d = idx & 127;
+            const uint32_t r = idx >> 7, d = idx & 127;  // a wave's 64 threads share row r
+            // all reads first, no branch between them: a wave with no visible
+            // key has m = -inf, l = 0 and a zero accumulator, and
+            // 2^(-inf - M) = 0 adds nothing
+            float mv[kSplitWaves], lv[kSplitWaves], ov[kSplitWaves];
+#pragma unroll
+            for (int w = 0; w < kSplitWaves; w++) {
+                mv[w] = sm_m[w * 16 + r];
+                lv[w] = sm_l[w * 16 + r];
+                ov[w] = sm_o[(w * 16 + r) * OS + d];
+            }
             float M = kNegInf;
 #pragma unroll
-            for (int w = 0; w < kSplitWaves; w++) M = fmaxf(M, sm_m[w * 16 + r]);
+            for (int w = 0; w < kSplitWaves; w++) M = fmaxf(M, mv[w]);
             float L = 0.f, A = 0.f;
             if (M != kNegInf) {
 #pragma unroll
                 for (int w = 0; w < kSplitWaves; w++) {
-                    const float mw = sm_m[w * 16 + r];
-                    if (mw == kNegInf) continue;
-                    const float f = fast_exp2(mw - M);
-                    L += f * sm_l[w * 16 + r];
-                    A += f * sm_o[(w * 16 + r) * OS + d];
+                    const float f = fast_exp2(mv[w] - M);
+                    L += f * lv[w];
+                    A += f * ov[w];
                 }
             }
             const uint32_t rk = row0 + r;
