@@ -263,13 +263,16 @@ __global__ __launch_bounds__((64 * SplitCfg<NT, KT, VT>::waves), 1) void split_k
         float l = st[t].l_run;
         l += __shfl_xor(l, 16);
         l += __shfl_xor(l, 32);
-        if (grp == 0) {
-            sm_m[wave * 16 + c16] = st[t].m_ref;
-            sm_l[wave * 16 + c16] = l;
-        }
+        // only rows that exist are combined, so only they are staged
+        if (block_row0 + 16 * t + c16 < rows_kv) {
+            if (grp == 0) {
+                sm_m[wave * 16 + c16] = st[t].m_ref;
+                sm_l[wave * 16 + c16] = l;
+            }
 #pragma unroll
-        for (int n = 0; n < 8; n++)
-            *reinterpret_cast<floatx4 *>(&sm_o[(wave * 16 + c16) * OS + 16 * n + 4 * grp]) = st[t].acc[n];
+            for (int n = 0; n < 8; n++)
+                *reinterpret_cast<floatx4 *>(&sm_o[(wave * 16 + c16) * OS + 16 * n + 4 * grp]) = st[t].acc[n];
+        }
         __syncthreads();
         const uint32_t row0 = block_row0 + 16 * t;
         const uint32_t rows_here = row0 < rows_kv ? min(16u, rows_kv - row0) : 0u;
