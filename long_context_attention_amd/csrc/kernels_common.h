@@ -9,7 +9,8 @@
 //   wide_kernel   calls with more rows (prefill chunks): one workgroup per
 //                 (split, KV head, 256-row block); each chunk is turned into
 //                 an f16 view of K and V once and shared by all 256 rows.
-//   merge_kernel  log-sum-exp merge of the split partials in split order;
+//   merge_small_kernel, merge_many_kernel
+//                 log-sum-exp merge of the split partials in split order;
 //                 splits with l = 0 are skipped (the zero guard the review
 //                 finds missing in the chunk normaliser).
 // Both attention kernels write one un-normalised partial (m, l, acc[128]) per

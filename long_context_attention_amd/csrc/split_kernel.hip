@@ -329,123 +329,21 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
-// Block-wide log-sum-exp merge (Flash-Decoding's reduction step) of nrows
-// (row, query head) units over n_splits >= 1 split partials (m, l, acc[128]).
-// For row r (unit unit_of(r)): M = max m_s over splits with l_s > 0,
-// w_s = 2^(m_s - M) (0 for empty splits), L = sum w_s l_s, out[t] =
-// (sum_s w_s acc_s[t]) / L.  One wave per row computes M, w and L (lane j
-// sums splits j, j + 64, ... then a butterfly); dimension t sums splits in
-// order.
-// Latency: each thread issues its first (m, l) and the first 32 splits of
-// its first two dimensions before anything waits, so up to 32 splits and
-// 2 x blockDim dimensions take one memory round trip.
-// wl: LDS for nrows * n_splits float2; row_ml: LDS for nrows float2.
-constexpr int kMergeBatch = 32;
+// Log-sum-exp merge (Flash-Decoding's reduction step) of the split partials
+// (m, l, acc[128]) of each (row, query head) unit: M = max m_s over splits
+// with l_s > 0, w_s = 2^(m_s - M) (0 for empty splits), L = sum w_s l_s,
+// out[t] = (sum_s w_s acc_s[t]) / L, dimension t summed in split order.
+constexpr int kMergeMaxSplits = 4096;  // splits per unit (one per page at most)
+constexpr uint32_t kMergeSmallMax = 64;  // up to this many splits take merge_small_kernel
 
-template <class UnitOf>
-__device__ __forceinline__ void merge_rows(const float *part_ml, const float *part_o, float *out, uint32_t n_splits,
-                                           uint32_t units, uint32_t nrows, UnitOf unit_of, float2 *wl,
-                                           float2 *row_ml) {
-    const uint32_t nt = blockDim.x, tid = threadIdx.x;
-    const size_t mls = (size_t)units * 2, pos = (size_t)units * 128;
-    const uint32_t n_ml = nrows * n_splits, n_items = nrows * 128;
-    auto ml_at = [&](uint32_t i) {
-        const uint32_t r = i / n_splits, s = i - r * n_splits;
-        return *reinterpret_cast<const float2 *>(part_ml + s * mls + (size_t)unit_of(r) * 2);
-    };
-    auto po_of = [&](uint32_t i) { return part_o + (size_t)unit_of(i >> 7) * 128 + (i & 127); };
-    // clamped addresses keep every early load unconditional
-    const float2 ml0 = ml_at(min(tid, n_ml - 1));
-    const float *po0 = po_of(min(tid, n_items - 1)), *po1 = po_of(min(tid + nt, n_items - 1));
-    float o0[kMergeBatch], o1[kMergeBatch];
-#pragma unroll
-    for (int k = 0; k < kMergeBatch; k++) o0[k] = po0[(size_t)min((uint32_t)k, n_splits - 1) * pos];
-    if (nt < n_items) {  // a second dimension per thread (workgroup-uniform)
-#pragma unroll
-        for (int k = 0; k < kMergeBatch; k++) o1[k] = po1[(size_t)min((uint32_t)k, n_splits - 1) * pos];
-    } else {
-#pragma unroll
-        for (int k = 0; k < kMergeBatch; k++) o1[k] = 0.f;
-    }
-    if (tid < n_ml) wl[tid] = ml0;
-    for (uint32_t i = tid + nt; i < n_ml; i += nt) wl[i] = ml_at(i);
-    __syncthreads();
-    const uint32_t lane = tid & 63, nw = nt >> 6;
-    for (uint32_t r = __builtin_amdgcn_readfirstlane(tid >> 6); r < nrows; r += nw) {
-        float2 *row = wl + r * n_splits;
-        float M = kNegInf;
-        for (uint32_t s = lane; s < n_splits; s += 64) {
-            const float2 v = row[s];
-            if (v.y > 0.f) M = fmaxf(M, v.x);
-        }
-        M = wave_max(M);
-        float L = 0.f;
-        for (uint32_t s = lane; s < n_splits; s += 64) {
-            const float2 v = row[s];
-            const float w = v.y > 0.f ? fast_exp2(v.x - M) : 0.f;
-            row[s].x = w;
-            L += w * v.y;
-        }
-        L = wave_sum(L);
-        if (lane == 0) row_ml[r] = make_float2(M, L);
-    }
-    __syncthreads();
-    const uint32_t nb0 = min(n_splits, (uint32_t)kMergeBatch);
-    // dimension i: splits [0, 32) from `first`, the rest loaded here
-    auto finish = [&](uint32_t i, const float(&first)[kMergeBatch]) {
-        const uint32_t r = i >> 7;
-        const float2 *row = wl + r * n_splits;
-        const float *po = po_of(i);
-        float A = 0.f;
-#pragma unroll
-        for (int k = 0; k < kMergeBatch; k++)
-            if ((uint32_t)k < nb0) A += row[k].x * first[k];
-        for (uint32_t s0 = kMergeBatch; s0 < n_splits; s0 += kMergeBatch) {
-            float ob[kMergeBatch];
-#pragma unroll
-            for (int k = 0; k < kMergeBatch; k++) ob[k] = po[(size_t)min(s0 + k, n_splits - 1) * pos];
-#pragma unroll
-            for (int k = 0; k < kMergeBatch; k++)
-                if (s0 + k < n_splits) A += row[s0 + k].x * ob[k];
-        }
-        out[(size_t)unit_of(r) * 128 + (i & 127)] = A / row_ml[r].y;
-    };
-    if (tid < n_items) finish(tid, o0);
-    if (tid + nt < n_items) finish(tid + nt, o1);
-    for (uint32_t i = tid + 2 * nt; i < n_items; i += nt) {
-        const float *po = po_of(i);
-        float ob[kMergeBatch];
-#pragma unroll
-        for (int k = 0; k < kMergeBatch; k++) ob[k] = po[(size_t)min((uint32_t)k, n_splits - 1) * pos];
-        finish(i, ob);
-    }
-}
-
-// U (row, query head) units per workgroup of 128 U threads: U = 4 for calls
-// with thousands of units (prefill chunks) while the splits fit 512 per unit
-// in LDS, else one unit per workgroup for up to 4096 splits.
-constexpr int kMergeMaxSplits = 4096;
-constexpr int kMergeWideUnits = 4, kMergeWideSplits = 512;
-
-// Unit merged by workgroup b of a one-unit-per-workgroup merge: KV head
-// b mod Hkv first, so that workgroup b runs on the XCD that held the split
-// workgroups of that KV head (the split kernel's grid puts the KV head
-// innermost).  A bijection of [0, units): b = (w * G + hh) * Hkv + kvh.
+// Unit merged by workgroup b: KV head b mod Hkv first, so that workgroup b
+// runs on the XCD that held the split workgroups of that KV head (the split
+// kernel's grid puts the KV head innermost).  A bijection of [0, units):
+// b = (w * G + hh) * Hkv + kvh.
 __device__ __forceinline__ uint32_t merge_unit(const MergeArgs &a, uint32_t b) {
     const uint32_t r = b / a.Hkv, kvh = b - r * a.Hkv;
     const uint32_t w = r / a.G, hh = r - w * a.G;
     return (w * a.Hkv + kvh) * a.G + hh;
-}
-
-template <int U>
-__global__ __launch_bounds__(128 * U) void merge_kernel(const MergeArgs a) {
-    constexpr int kSplits = U == 1 ? kMergeMaxSplits : kMergeWideSplits;
-    __shared__ float2 wl[U * kSplits];
-    __shared__ float2 row_ml[U];
-    const uint32_t unit0 = U == 1 ? merge_unit(a, blockIdx.x) : blockIdx.x * U;
-    const uint32_t nrows = min((uint32_t)U, a.units - unit0);
-    merge_rows(a.part_ml, a.part_o, a.out, a.n_splits, a.units, nrows, [=](uint32_t r) { return unit0 + r; }, wl,
-               row_ml);
 }
 
 // Merge of calls with few splits (decode, verify: n_splits <= KMAX): one
@@ -453,7 +351,6 @@ __global__ __launch_bounds__(128 * U) void merge_kernel(const MergeArgs a) {
 // barrier: lane s of each wave loads split s's (m, l); M, the weights w_s and
 // L come from wave reductions, and w_s reaches every lane by v_readlane, so
 // the only wait is the one memory round trip of the loads, all issued first.
-// The arithmetic and its order are those of merge_rows.
 template <int KMAX>
 __global__ __launch_bounds__(128) void merge_small_kernel(const MergeArgs a) {
     const uint32_t unit = merge_unit(a, blockIdx.x);
@@ -476,14 +373,14 @@ __global__ __launch_bounds__(128) void merge_small_kernel(const MergeArgs a) {
     a.out[(size_t)unit * 128 + d] = A / L;
 }
 
-// Merge of calls with many splits (streamed layers and resident layers split
-// one page per split: one split per page): one unit per workgroup of 512
-// threads.  M, the weights w_s and L as in merge_rows, reduced over the
+// Merge of calls with more than 64 splits (streamed layers and resident
+// layers split one page per split: one split per page): one unit per
+// workgroup of 512 threads.  M, the weights w_s and L reduced over the
 // threads in a fixed order; dimension d is summed in four parts (splits
 // congruent to q mod 4, in split order), which then add in part order, so
 // each thread waits for a quarter of the batches of 32 loads.
 constexpr int kManyParts = 4;
-constexpr uint32_t kManyMinSplits = 65;  // more splits than this take merge_many_kernel
+constexpr int kMergeBatch = 32;
 
 __global__ __launch_bounds__(128 * kManyParts) void merge_many_kernel(const MergeArgs a) {
     __shared__ float2 wl[kMergeMaxSplits];
@@ -620,45 +517,26 @@ hipError_t kvattn_launch_split(const SplitArgs &a, uint32_t n_items, uint32_t n_
 
 hipError_t kvattn_launch_merge(const MergeArgs &a, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
     (void)hipGetLastError();
-    // many splits (one per page): one unit per 512-thread workgroup; up to
-    // 64 splits (decode, verify, prefill chunks): one unit per 128-thread
-    // workgroup without barriers; otherwise 65..512 splits over thousands of
-    // units four per workgroup, or one per workgroup
-    if (a.n_splits >= kvattn_dev::kManyMinSplits) {
-        dim3 grid(a.units), block(128 * kvattn_dev::kManyParts);
+    auto go = [&](auto kern, dim3 grid, dim3 block) {
         if (ev_start)
-            hipExtLaunchKernelGGL(kvattn_dev::merge_many_kernel, grid, block, 0, s, ev_start, ev_stop, 0, a);
+            hipExtLaunchKernelGGL(kern, grid, block, 0, s, ev_start, ev_stop, 0, a);
         else
-            hipLaunchKernelGGL(kvattn_dev::merge_many_kernel, grid, block, 0, s, a);
-    } else if (a.units >= 1024 && a.n_splits > 64 && a.n_splits <= kvattn_dev::kMergeWideSplits) {
-        constexpr int U = kvattn_dev::kMergeWideUnits;
-        dim3 grid((a.units + U - 1) / U), block(128 * U);
-        if (ev_start)
-            hipExtLaunchKernelGGL(kvattn_dev::merge_kernel<U>, grid, block, 0, s, ev_start, ev_stop, 0, a);
-        else
-            hipLaunchKernelGGL(kvattn_dev::merge_kernel<U>, grid, block, 0, s, a);
-    } else if (a.n_splits <= 64) {
-        dim3 grid(a.units), block(128);
-        auto go = [&](auto kern) {
-            if (ev_start)
-                hipExtLaunchKernelGGL(kern, grid, block, 0, s, ev_start, ev_stop, 0, a);
-            else
-                hipLaunchKernelGGL(kern, grid, block, 0, s, a);
-        };
-        if (a.n_splits <= 8)
-            go(kvattn_dev::merge_small_kernel<8>);
-        else if (a.n_splits <= 16)
-            go(kvattn_dev::merge_small_kernel<16>);
-        else if (a.n_splits <= 32)
-            go(kvattn_dev::merge_small_kernel<32>);
-        else
-            go(kvattn_dev::merge_small_kernel<64>);
-    } else {
-        dim3 grid(a.units), block(128);
-        if (ev_start)
-            hipExtLaunchKernelGGL(kvattn_dev::merge_kernel<1>, grid, block, 0, s, ev_start, ev_stop, 0, a);
-        else
-            hipLaunchKernelGGL(kvattn_dev::merge_kernel<1>, grid, block, 0, s, a);
-    }
+            hipLaunchKernelGGL(kern, grid, block, 0, s, a);
+    };
+    // up to 64 splits (decode, verify, prefill chunks): one unit per
+    // 128-thread workgroup without LDS or barriers; more (streamed layers and
+    // resident layers split one page per split): one unit per 512-thread
+    // workgroup
+    const dim3 grid(a.units);
+    if (a.n_splits > kvattn_dev::kMergeSmallMax)
+        go(kvattn_dev::merge_many_kernel, grid, dim3(128 * kvattn_dev::kManyParts));
+    else if (a.n_splits <= 8)
+        go(kvattn_dev::merge_small_kernel<8>, grid, dim3(128));
+    else if (a.n_splits <= 16)
+        go(kvattn_dev::merge_small_kernel<16>, grid, dim3(128));
+    else if (a.n_splits <= 32)
+        go(kvattn_dev::merge_small_kernel<32>, grid, dim3(128));
+    else
+        go(kvattn_dev::merge_small_kernel<64>, grid, dim3(128));
     return hipGetLastError();
 }
