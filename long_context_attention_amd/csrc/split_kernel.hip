@@ -7,18 +7,19 @@
 namespace kvattn_dev {
 
 // ---------------------------------------------------------------------------
-// Split kernel.  A workgroup (12, 8 or 4 waves, SplitCfg) handles one split (a
-// range of 32-key chunks) of one KV head for a block of 16 * NT query rows; the waves take
-// the split's chunks round robin and each computes every row of the block,
-// so a chunk is loaded and dequantised once per block.  Rows of a KV head
+// Split kernel.  A workgroup (12, 8 or 4 waves, SplitCfg) handles one split
+// (a range of 32-key chunks) of one KV head for a block of 16 * NT query
+// rows; the waves take the split's chunks round robin and each computes every
+// row of the block, so a chunk is loaded and dequantised once per block.  Rows of a KV head
 // are ordered (w, hh): r = w * G + hh, hh < G.
-// Each wave streams its chunks through its own LDS ring and overlaps chunk
-// i's Q.K^T with chunk i-1's P.V, whose operands it carries over.
+// Each wave streams its chunks through its own LDS ring; chunk i-1's P.V,
+// whose operands the wave carries over in registers, runs at the start of
+// chunk i, just before chunk i's Q.K^T.
 // ---------------------------------------------------------------------------
 // Shape per row-tile count and element-type pair, each filling most of the
 // 160 KiB of LDS with chunk rings: Q8_0 K / Q4_0 V and Q4_0 / Q4_0 with one
 // tile (<= 16 rows per KV head) need few registers, so 12 waves (three per
-// SIMD) with two-stage rings; two tiles need about 250 registers, so 8 waves
+// SIMD) with two-stage rings; two tiles need about 220 registers, so 8 waves
 // with three-stage rings.  The larger Q8_0 / Q8_0 chunks take 8 waves with
 // two stages, F16 / F16 chunks (16 KiB) 4 waves with two stages.
 template <int NT, int KT, int VT>
@@ -346,11 +347,12 @@ __device__ __forceinline__ uint32_t merge_unit(const MergeArgs &a, uint32_t b) {
     return (w * a.Hkv + kvh) * a.G + hh;
 }
 
-// Merge of calls with few splits (decode, verify: n_splits <= KMAX): one
-// unit per 128-thread workgroup, thread d owns dimension d.  No LDS and no
-// barrier: lane s of each wave loads split s's (m, l); M, the weights w_s and
-// L come from wave reductions, and w_s reaches every lane by v_readlane, so
-// the only wait is the one memory round trip of the loads, all issued first.
+// Merge of calls with few splits (decode, verify, prefill chunks: n_splits
+// <= KMAX <= 64): one unit per 128-thread workgroup, thread d owns dimension
+// d.  No LDS and no barrier: lane s of each wave loads split s's (m, l); M,
+// the weights w_s and L come from wave reductions, and w_s reaches every lane
+// by v_readlane, so the only wait is the one memory round trip of the loads,
+// all issued first.
 template <int KMAX>
 __global__ __launch_bounds__(128) void merge_small_kernel(const MergeArgs a) {
     const uint32_t unit = merge_unit(a, blockIdx.x);

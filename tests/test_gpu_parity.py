@@ -133,6 +133,25 @@ def test_split_count_sweep():
         h.destroy()
 
 
+@pytest.mark.parametrize("n_splits", [8, 9, 17, 33, 64, 65, 100])
+def test_merge_split_ranges(n_splits):
+    # one page per split: the merge instances for up to 8, 16, 32 and 64
+    # splits and the many-split merge, each at its boundaries, ragged tail
+    N, Hq, Hkv, W = n_splits * 256 - 13, 40, 8, 3
+    say(f"case merge splits={n_splits} N={N} W={W}")
+    kvl = layer_kv(N, Hkv, wid=62 + n_splits)
+    q = inputs.draw_queries(W, Hq, 0, 62 + n_splits)
+    n = kvl.pages.shape[0]
+    assert n == n_splits
+    ref = oracle_out(kvl, q, Hq, Hkv)
+    h = handle(Hq, Hkv, n, n, 8, split_pages=1)
+    place(h, 0, kvl, perm_table(n, n_splits))
+    err = np.max(np.abs(run(h, 0, q, W, "verify") - ref))
+    say(f"  max-abs err {err:.3e}")
+    assert err <= TOL
+    h.destroy()
+
+
 @pytest.mark.parametrize("W", [1, 6])
 def test_chunk_order_modes(W):
     """Deterministic mode repeats its bits exactly; the default (waves claim
