@@ -21,11 +21,11 @@ def say(*a):
 
 
 def handle(Hq, Hkv, n_pool, max_pages, max_rows, n_ring=0, split_pages=0, chunk_slots=0, n_layers=1,
-           page_tokens=256, k_type=kv.TYPE_Q8_0, v_type=kv.TYPE_Q4_0, deterministic=0):
+           page_tokens=256, k_type=kv.TYPE_Q8_0, v_type=kv.TYPE_Q4_0, deterministic=0, compute_stream=None):
     p = kv.make_params(n_layers, Hq, Hkv, n_pool, max_pages, max_rows, n_ring_slots=n_ring,
                        split_pages=split_pages, chunk_slots=chunk_slots, page_tokens=page_tokens,
                        k_type=k_type, v_type=v_type, deterministic=deterministic)
-    return kv.allocate(p)
+    return kv.allocate(p, compute_stream=compute_stream)
 
 
 def place(h, layer, kvl, table, history=None, page_tokens=256):
