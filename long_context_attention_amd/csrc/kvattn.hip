@@ -29,7 +29,7 @@ namespace {
 
 constexpr uint32_t kHeadDim = 128;
 constexpr uint32_t kNarrowRows = 32;      // rows per KV head handled with the verify split plan
-constexpr uint32_t kPrefillMaxSplits = 16;
+constexpr uint32_t kWideMaxWorkgroups = 256;  // wide calls: workgroups one launch fills (one per compute unit)
 constexpr uint32_t kClaimMinChunks = 96;  // splits at least this long use the claimed chunk order
 constexpr uint32_t kEntryStream = 0xC0000000u;  // device entry tag: streamed ordinal
 constexpr size_t kAlign = 256;
@@ -118,7 +118,13 @@ size_t partial_units(const kvattn_params &p) {
     const uint32_t G = p.n_q_heads / p.n_kv_heads;
     const uint64_t narrow_w = std::min<uint64_t>(p.max_rows, std::max<uint32_t>(1, kNarrowRows / G));
     const uint64_t narrow = (uint64_t)p.max_pages_per_layer * narrow_w * p.n_q_heads;
-    const uint64_t wide = (uint64_t)std::min(kPrefillMaxSplits, p.max_pages_per_layer) * p.max_rows * p.n_q_heads;
+    // wide calls: splits x row blocks x KV heads <= kWideMaxWorkgroups (or one
+    // split), and a row block holds at most 12 waves' rows, so splits x W x Hq
+    // stays within kWideMaxWorkgroups such blocks, or W x Hq with one split
+    const uint64_t block = 12ull * kvattn_wide_rows_per_wave();
+    const uint64_t wide = std::min<uint64_t>((uint64_t)p.max_pages_per_layer * p.max_rows * p.n_q_heads,
+                                             std::max<uint64_t>(kWideMaxWorkgroups * block,
+                                                                (uint64_t)p.max_rows * p.n_q_heads));
     return (size_t)std::max(narrow, wide);
 }
 
@@ -274,8 +280,9 @@ SplitArgs base_args(kvattn_t h, uint32_t layer, uint32_t W, const float *q) {
 // Split plan of a call on an all-resident layer.  A split is a range of
 // 32-key chunks of one KV head.  Narrow calls (rows per KV head <= 32) run
 // the split kernel and aim at one workgroup per compute unit (or honour
-// split_pages); wide calls (prefill chunks) run the wide kernel on 256-row
-// blocks with as many splits as fill the compute units once, at most 16.
+// split_pages); wide calls (prefill chunks, wide verify) run the wide kernel
+// on 256- or 384-row blocks with as many splits as fill the compute units
+// once (at most kWideMaxWorkgroups workgroups).
 // The split count never exceeds the page count, which bounds the partial
 // buffer.
 struct Plan {
@@ -314,7 +321,8 @@ Plan plan_resident(const kvattn_params &p, uint32_t n_tokens, uint32_t n_pages, 
         pl.wide_waves = b12 * 12 * 100 < b8 * 8 * 137 ? 12 : 8;
         pl.n_row_blocks = (uint32_t)(pl.wide_waves == 12 ? b12 : b8);
         const uint64_t per = (uint64_t)p.n_kv_heads * pl.n_row_blocks;
-        uint32_t splits = (uint32_t)std::min<uint64_t>(kPrefillMaxSplits, std::max<uint64_t>(1, cus / per));
+        const uint64_t slots = std::min<uint64_t>(cus, kWideMaxWorkgroups);
+        uint32_t splits = (uint32_t)std::max<uint64_t>(1, slots / per);
         splits = std::min(splits, n_pages);
         pl.split_chunks = (n_chunks + splits - 1) / splits;
     }
@@ -776,10 +784,9 @@ int install_layer(kvattn_t h, uint32_t layer, const uint32_t *page_table, uint32
     return KVATTN_OK;
 }
 
-std::vector<uint32_t> streamed_counts(kvattn_t h) {
-    std::vector<uint32_t> counts(h->p.n_layers, 0);
+void streamed_counts(kvattn_t h, std::vector<uint32_t> &counts) {
+    counts.assign(h->p.n_layers, 0);
     for (uint32_t l = 0; l < h->p.n_layers; l++) counts[l] = h->layers[l].set ? h->layers[l].n_streamed : 0;
-    return counts;
 }
 }  // namespace
 
@@ -1051,7 +1058,9 @@ int kvattn_set_ring_slots(kvattn_t h, uint32_t n_slots) {
     const uint32_t chunk = h->p.chunk_slots ? h->p.chunk_slots : 16;
     h->sched.destroy();
     if (!h->sched.init(h->p.n_layers, n_slots, std::min(chunk, n_slots))) return fail(h, KVATTN_E_HIP, "ring event setup failed");
-    h->sched.set_layer_counts(streamed_counts(h));
+    std::vector<uint32_t> counts;
+    streamed_counts(h, counts);
+    h->sched.set_layer_counts(counts);
     h->ring_slots = n_slots;
     h->obs_of.clear();  // chunk keys of the old schedule
     h->obs_used = 0;
