@@ -28,7 +28,8 @@
 namespace {
 
 constexpr uint32_t kHeadDim = 128;
-constexpr uint32_t kNarrowRows = 32;      // rows per KV head handled with the verify split plan
+constexpr uint32_t kNarrowRows = 32;      // rows per KV head of one split-kernel workgroup
+constexpr uint32_t kNarrowMaxBlocks = 2;  // split-kernel row blocks before the wide kernel takes over
 constexpr uint32_t kWideMaxWorkgroups = 256;  // wide calls: workgroups one launch fills (one per compute unit)
 constexpr uint32_t kClaimMinChunks = 96;  // splits at least this long use the claimed chunk order
 constexpr uint32_t kEntryStream = 0xC0000000u;  // device entry tag: streamed ordinal
@@ -280,11 +281,12 @@ SplitArgs base_args(kvattn_t h, uint32_t layer, uint32_t W, const float *q) {
 // Split plan of a call on an all-resident layer.  A split is a range of
 // 32-key chunks of one KV head.  Narrow calls (rows per KV head <= 32) run
 // the split kernel and aim at one workgroup per compute unit (or honour
-// split_pages); wide calls (prefill chunks, wide verify) run the wide kernel
-// on 256- or 384-row blocks with as many splits as fill the compute units
-// once (at most kWideMaxWorkgroups workgroups).
-// The split count never exceeds the page count, which bounds the partial
-// buffer.
+// split_pages); calls of up to kNarrowMaxBlocks x 32 rows run the split
+// kernel on that many 32-row blocks; wider calls (prefill chunks, wide
+// verify) run the wide kernel on 256- or 384-row blocks.  Both multi-block
+// plans take as many splits as fill the compute units once (at most
+// kWideMaxWorkgroups workgroups).  The split count never exceeds the page
+// count, which bounds the partial buffer.
 struct Plan {
     uint32_t split_chunks, n_splits, n_row_blocks;
     int nrt;         // split kernel: 16-row tiles per workgroup
@@ -300,14 +302,20 @@ Plan plan_resident(const kvattn_params &p, uint32_t n_tokens, uint32_t n_pages, 
     const uint64_t cus = (uint64_t)std::max(n_cus, 1);
     Plan pl;
     pl.wide_waves = 8;
-    pl.wide = rows > kNarrowRows;
+    pl.wide = rows > kNarrowRows * kNarrowMaxBlocks;
     if (!pl.wide) {
         pl.nrt = rows <= 16 ? 1 : 2;
-        pl.n_row_blocks = 1;
-        if (p.split_pages) {
+        pl.n_row_blocks = (rows + kNarrowRows - 1) / kNarrowRows;
+        if (p.split_pages && pl.n_row_blocks == 1) {
             pl.split_chunks = p.split_pages * cpp;
         } else {
-            uint32_t splits = (uint32_t)std::max<uint64_t>(1, (cus + p.n_kv_heads - 1) / p.n_kv_heads);
+            // one row block: ceil(CUs / KV heads) splits; more: the row blocks
+            // of a split share its keys, and splits x row blocks x KV heads
+            // stays within kWideMaxWorkgroups (which bounds the partials)
+            uint32_t splits = pl.n_row_blocks == 1
+                                  ? (uint32_t)std::max<uint64_t>(1, (cus + p.n_kv_heads - 1) / p.n_kv_heads)
+                                  : (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(cus, kWideMaxWorkgroups) /
+                                                                        ((uint64_t)p.n_kv_heads * pl.n_row_blocks));
             splits = std::min(splits, n_pages);
             pl.split_chunks = std::max<uint32_t>((n_chunks + splits - 1) / splits, std::min<uint32_t>(8, n_chunks));
         }

@@ -66,6 +66,13 @@ CASES = [
     (1000, 8, 1, 100, "prefill", 0),
     (256, 16, 2, 256, "prefill", 0),     # row 0 sees one key
     (3000, 40, 8, 37, "prefill", 0),
+    (5000, 40, 8, 7, "verify", 0),      # 35 rows per KV head: two 32-row blocks of the split kernel
+    (5000, 40, 8, 12, "verify", 0),     # 60 rows, two blocks
+    (3000, 8, 1, 5, "verify", 0),       # 40 rows, one KV head
+    (1500, 8, 8, 40, "verify", 0),      # G = 1: 40 rows of distinct positions
+    (2000, 16, 2, 8, "prefill", 0),     # 64 rows as a prefill chunk
+    (700, 40, 8, 7, "verify", 1),       # two blocks: split_pages applies to one-block calls only
+    (5000, 40, 8, 13, "verify", 0),     # 65 rows: the wide kernel
     (100 * 256 - 17, 40, 8, 4, "verify", 1),   # 100 splits: the many-split merge
     (300 * 256, 8, 1, 1, "decode", 1),         # 300 splits
 ]
