@@ -2,13 +2,15 @@
 // Q8_0-K / Q4_0-V attention (split_kernel.hip, wide_kernel.hip,
 // writer_kernel.hip, copy_kernels.hip).
 //
-//   split_kernel  calls with up to 32 rows per KV head (decode, verify): one
-//                 workgroup per (split of 32-key chunks, KV head); every wave
-//                 streams its own chunks into an LDS ring with direct-to-LDS
-//                 loads and computes all rows of the block.
-//   wide_kernel   calls with more rows (prefill chunks): one workgroup per
-//                 (split, KV head, 256-row block); each chunk is turned into
-//                 an f16 view of K and V once and shared by all 256 rows.
+//   split_kernel  calls with up to 64 rows per KV head (decode, verify): one
+//                 workgroup per (split of 32-key chunks, KV head, block of up
+//                 to 32 rows); every wave streams its own chunks into an LDS
+//                 ring with direct-to-LDS loads and computes all rows of the
+//                 block.
+//   wide_kernel   calls with more rows (prefill chunks, wide verify): one
+//                 workgroup per (split, KV head, 256- or 384-row block); each
+//                 chunk is turned into an f16 view of K and V once and shared
+//                 by all rows of the block.
 //   merge_small_kernel, merge_many_kernel
 //                 log-sum-exp merge of the split partials in split order;
 //                 splits with l = 0 are skipped (the zero guard the review

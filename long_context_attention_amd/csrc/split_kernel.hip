@@ -1,5 +1,6 @@
-// split_kernel.hip -- the split-KV kernel for calls with up to 32 rows per KV
-// head (decode, verify) and the log-sum-exp merge of the split partials.
+// split_kernel.hip -- the split-KV kernel (decode, verify: up to 32 rows per
+// KV head in a workgroup, calls of up to 64 rows as two row blocks) and the
+// log-sum-exp merge of the split partials.
 #include <type_traits>
 
 #include "kernels_common.h"
