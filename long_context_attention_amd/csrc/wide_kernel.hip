@@ -26,8 +26,9 @@ namespace kvattn_dev {
 constexpr int kWideRowsPerWave = 32;
 // Two chunks per barrier halve the barriers and let a wave's matrix-core work
 // on one chunk overlap its vector work on the other (measured +7 % on the
-// prefill chunk against one; three were faster for Q8_0/Q4_0 but slower for
-// Q8_0/Q8_0 and do not fit the LDS for F16).
+// prefill chunk against one; three per barrier, with rings of six, ran 4 %
+// slower for Q8_0/Q4_0 and 1-2 % slower for Q4_0/Q4_0 and do not fit the LDS
+// for F16).
 constexpr int kViewBytes = 16384;  // K' [tt][b][lane] x 16 B, then V' [n][lane] x 16 B
 
 // Scores for NT row tiles from the f16 view, relative to each tile's
