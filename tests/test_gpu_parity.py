@@ -97,8 +97,11 @@ def test_parity_sweep(N, Hq, Hkv, W, kind, sp):
 
 
 # ------------------------------------------------------------------ placement, bitwise
-def test_placement_bitwise_invariance():
-    N, Hq, Hkv, W = 3000, 40, 8, 4
+@pytest.mark.parametrize("W", [4, 10, 20], ids=["one-block", "two-blocks", "wide"])
+def test_placement_bitwise_invariance(W):
+    # 20, 50 and 100 rows per KV head: the split kernel on one and on two row
+    # blocks, and the wide kernel; each plan is fixed by the shapes alone
+    N, Hq, Hkv = 3000, 40, 8
     say(f"case placement N={N} Hq={Hq} Hkv={Hkv} W={W}, 6 placements, split_pages=2")
     kvl = layer_kv(N, Hkv, wid=60)
     q = inputs.draw_queries(W, Hq, 0, 60)
@@ -106,7 +109,7 @@ def test_placement_bitwise_invariance():
     outs = []
     for seed in range(6):
         rng = np.random.default_rng(seed)
-        h = handle(Hq, Hkv, 2 * n, n, 8, n_ring=n + 2, split_pages=2, deterministic=1)
+        h = handle(Hq, Hkv, 2 * n, n, max(8, W), n_ring=n + 2, split_pages=2, deterministic=1)
         table = np.empty(n, dtype=np.uint32)
         pool_ids = rng.permutation(2 * n)[:n]
         ring_ids = rng.permutation(n + 2)[:n]
