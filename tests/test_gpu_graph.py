@@ -28,7 +28,8 @@ def _queries(rows, Hq, seed):
 def _calls(h, layer, qs, outs):
     h.decode(layer, qs[0], outs[0])
     h.verify(layer, qs[1], qs[1].shape[0], outs[1])
-    h.prefill_chunk(layer, qs[2], qs[2].shape[0], outs[2])
+    h.verify(layer, qs[2], qs[2].shape[0], outs[2])
+    h.prefill_chunk(layer, qs[3], qs[3].shape[0], outs[3])
 
 
 @pytest.mark.parametrize("deterministic", [1, 0], ids=["fixed-order", "claimed-order"])
@@ -42,7 +43,8 @@ def test_graph_replay_attention(deterministic):
     table = np.random.default_rng(5).permutation(n).astype(np.uint32)
     h = handle(Hq, Hkv, n, n, 64, split_pages=sp, deterministic=deterministic, compute_stream=torch.cuda.Stream())
     place(h, 0, kvl, table)
-    qs = [_queries(1, Hq, 0), _queries(3, Hq, 1), _queries(64, Hq, 2)]
+    # 4, 12, 40 (two 32-row blocks) and 256 (wide kernel) rows per KV head
+    qs = [_queries(1, Hq, 0), _queries(3, Hq, 1), _queries(10, Hq, 4), _queries(64, Hq, 2)]
     refs = [oracle_out(kvl, q.cpu(), Hq, Hkv) for q in qs]
 
     stream = h.compute_stream
