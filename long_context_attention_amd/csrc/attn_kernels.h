@@ -81,7 +81,7 @@ uint32_t kvattn_merge_max_splits();
 // rt: row tiles of 16 rows per workgroup (1 or 2); n_row_blocks blocks of 16 * rt rows
 hipError_t kvattn_launch_split(const SplitArgs &a, uint32_t n_items, uint32_t n_row_blocks, int rt, hipStream_t s,
                                hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
-// Wide calls (> 64 rows per KV head): workgroups of `waves` (8 or 12) waves,
+// Wide calls (> 96 rows per KV head): workgroups of `waves` (8 or 12) waves,
 // n_row_blocks blocks of waves * kvattn_wide_rows_per_wave() rows, n_splits
 // ranges of split_chunks chunks.
 hipError_t kvattn_launch_wide(const SplitArgs &a, uint32_t n_splits, uint32_t n_row_blocks, int waves, hipStream_t s,

@@ -2,7 +2,7 @@
 // Q8_0-K / Q4_0-V attention (split_kernel.hip, wide_kernel.hip,
 // writer_kernel.hip, copy_kernels.hip).
 //
-//   split_kernel  calls with up to 64 rows per KV head (decode, verify): one
+//   split_kernel  calls with up to 96 rows per KV head (decode, verify): one
 //                 workgroup per (split of 32-key chunks, KV head, block of up
 //                 to 32 rows); every wave streams its own chunks into an LDS
 //                 ring with direct-to-LDS loads and computes all rows of the

@@ -29,7 +29,7 @@ namespace {
 
 constexpr uint32_t kHeadDim = 128;
 constexpr uint32_t kNarrowRows = 32;      // rows per KV head of one split-kernel workgroup
-constexpr uint32_t kNarrowMaxBlocks = 2;  // split-kernel row blocks before the wide kernel takes over
+constexpr uint32_t kNarrowMaxBlocks = 3;  // split-kernel row blocks before the wide kernel takes over
 constexpr uint32_t kWideMaxWorkgroups = 256;  // wide calls: workgroups one launch fills (one per compute unit)
 constexpr uint32_t kClaimMinChunks = 96;  // splits at least this long use the claimed chunk order
 constexpr uint32_t kEntryStream = 0xC0000000u;  // device entry tag: streamed ordinal

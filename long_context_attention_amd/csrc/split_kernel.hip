@@ -1,6 +1,6 @@
 // split_kernel.hip -- the split-KV kernel (decode, verify: up to 32 rows per
-// KV head in a workgroup, calls of up to 64 rows as two row blocks) and the
-// log-sum-exp merge of the split partials.
+// KV head in a workgroup, calls of up to 96 rows as two or three row blocks)
+// and the log-sum-exp merge of the split partials.
 #include <type_traits>
 
 #include "kernels_common.h"

@@ -1,11 +1,11 @@
-// wide_kernel.hip -- the kernel for calls with more than 64 rows per KV head
+// wide_kernel.hip -- the kernel for calls with more than 96 rows per KV head
 // (prefill chunks, wide verify).
 #include "kernels_common.h"
 
 namespace kvattn_dev {
 
 // ---------------------------------------------------------------------------
-// Wide kernel (prefill chunks, and any call with more than 64 rows per KV
+// Wide kernel (prefill chunks, and any call with more than 96 rows per KV
 // head).  A workgroup of 8 or 12 waves handles one split of one KV head for a
 // block of 256 or 384 rows; wave w owns rows 32w .. 32w + 31 (two 16-row
 // tiles) over every chunk of the split, so no combine across waves is needed.

@@ -72,7 +72,9 @@ CASES = [
     (1500, 8, 8, 40, "verify", 0),      # G = 1: 40 rows of distinct positions
     (2000, 16, 2, 8, "prefill", 0),     # 64 rows as a prefill chunk
     (700, 40, 8, 7, "verify", 1),       # two blocks: split_pages applies to one-block calls only
-    (5000, 40, 8, 13, "verify", 0),     # 65 rows: the wide kernel
+    (5000, 40, 8, 13, "verify", 0),     # 65 rows: three blocks
+    (5000, 40, 8, 19, "verify", 0),     # 95 rows: three blocks
+    (5000, 40, 8, 20, "verify", 0),     # 100 rows: the wide kernel
     (100 * 256 - 17, 40, 8, 4, "verify", 1),   # 100 splits: the many-split merge
     (300 * 256, 8, 1, 1, "decode", 1),         # 300 splits
 ]
