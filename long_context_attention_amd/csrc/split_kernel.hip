@@ -37,7 +37,10 @@ struct SplitCfg {
     static_assert(lds_bytes <= 163840, "LDS budget");
 };
 
-template <int NT, int KT, int VT>
+// STREAM: chunk loads carry the non-temporal hint (each chunk is read by one
+// workgroup); calls of several row blocks, whose blocks read the same chunks,
+// load without it.
+template <int NT, int KT, int VT, bool STREAM>
 __global__ __launch_bounds__((64 * SplitCfg<NT, KT, VT>::waves), 1) void split_kernel(const SplitArgs a) {
     using C = Chunk<KT, VT>;
     constexpr int kSplitWaves = SplitCfg<NT, KT, VT>::waves;
@@ -120,7 +123,7 @@ __global__ __launch_bounds__((64 * SplitCfg<NT, KT, VT>::waves), 1) void split_k
     asm volatile("" : "+s"(pool_base), "+s"(ring_base));
     auto issue = [&](uint32_t chunk, uint32_t entry, uint32_t stage) {
         const uint32_t jj0 = (chunk - (chunk / cpp) * cpp) << 5;
-        issue_chunk<KT, VT, true>(a, page_base(a, pool_base, ring_base, entry), kvh, jj0, lane, ring_lds + stage * C::bytes);
+        issue_chunk<KT, VT, STREAM>(a, page_base(a, pool_base, ring_base, entry), kvh, jj0, lane, ring_lds + stage * C::bytes);
     };
 
     // ---- query loads, then the ring prologue: the first kStages - 1 chunks
@@ -453,14 +456,21 @@ __global__ __launch_bounds__(128 * kManyParts) void merge_many_kernel(const Merg
 namespace {
 
 // Calls f(kernel, waves, lds bytes) with the split kernel of row tiles rt and
-// the element-type pair; false for an unsupported pair.
+// the element-type pair (without the non-temporal hint when `blocks`: several
+// row blocks, which have two row tiles); false for an unsupported pair.
 template <class F>
-bool with_split_kernel(int rt, uint32_t kt, uint32_t vt, F f) {
+bool with_split_kernel(int rt, uint32_t kt, uint32_t vt, bool blocks, F f) {
     using namespace kvattn_dev;
     auto pick = [&](auto nt, auto ktc, auto vtc) {
         constexpr int NT = decltype(nt)::value, KT = decltype(ktc)::value, VT = decltype(vtc)::value;
         using Cfg = SplitCfg<NT, KT, VT>;
-        f(&split_kernel<NT, KT, VT>, Cfg::waves, (uint32_t)Cfg::lds_bytes);
+        if constexpr (NT == 2) {
+            if (blocks) {
+                f(&split_kernel<NT, KT, VT, false>, Cfg::waves, (uint32_t)Cfg::lds_bytes);
+                return true;
+            }
+        }
+        f(&split_kernel<NT, KT, VT, true>, Cfg::waves, (uint32_t)Cfg::lds_bytes);
         return true;
     };
     using I1 = std::integral_constant<int, 1>;
@@ -479,7 +489,7 @@ bool with_split_kernel(int rt, uint32_t kt, uint32_t vt, F f) {
 
 size_t kvattn_split_smem_bytes(int rt, uint32_t k_type, uint32_t v_type) {
     size_t bytes = 0;
-    with_split_kernel(rt, k_type, v_type, [&](auto, int, uint32_t lds) { bytes = lds; });
+    with_split_kernel(rt, k_type, v_type, false, [&](auto, int, uint32_t lds) { bytes = lds; });
     return bytes;
 }
 
@@ -493,11 +503,12 @@ hipError_t kvattn_split_setup() {
     hipError_t err = hipSuccess;
     for (const auto &pr : pairs)
         for (int rt = 1; rt <= 2; rt++)
-            with_split_kernel(rt, pr[0], pr[1], [&](auto kern, int, uint32_t lds) {
-                if (err == hipSuccess)
-                    err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-            });
+            for (int blocks = 0; blocks <= 1; blocks++)
+                with_split_kernel(rt, pr[0], pr[1], blocks != 0, [&](auto kern, int, uint32_t lds) {
+                    if (err == hipSuccess)
+                        err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                });
     return err;
 }
 
@@ -508,7 +519,7 @@ hipError_t kvattn_launch_split(const SplitArgs &a, uint32_t n_items, uint32_t n_
                                hipEvent_t ev_start, hipEvent_t ev_stop) {
     (void)hipGetLastError();  // clear a stale error so the check below reports this launch
     const dim3 grid(a.Hkv, n_items, n_row_blocks);  // n_items <= 4096 pages
-    const bool ok = with_split_kernel(rt, a.k_type, a.v_type, [&](auto kern, int waves, uint32_t lds) {
+    const bool ok = with_split_kernel(rt, a.k_type, a.v_type, n_row_blocks > 1, [&](auto kern, int waves, uint32_t lds) {
         if (ev_start)
             hipExtLaunchKernelGGL(kern, grid, dim3(64 * waves), lds, s, ev_start, ev_stop, 0, a);
         else
