@@ -155,8 +155,10 @@ int kvattn_create(const kvattn_params *params, void *d_pool, size_t pool_bytes, 
 /*
  * Copy n pages from host memory h_pages (n * page_bytes, pinned for an
  * asynchronous copy) to the pool pages or ring slots named by dst[i]
- * (pool id, or KVATTN_PT_RING(slot)).  The copy runs on the copy stream;
- * later compute on the compute stream waits for it.  h_pages must stay
+ * (pool id, or KVATTN_PT_RING(slot)).  The copy runs on the copy stream,
+ * after the compute stream has passed every call enqueued before it (so a
+ * page that an earlier call still reads is never overwritten under it);
+ * later compute on the compute stream waits for the copy.  h_pages must stay
  * valid until the compute stream has passed the next call.
  */
 int kvattn_upload_pages(kvattn_t h, const void *h_pages, const uint32_t *dst, uint32_t n);
@@ -240,6 +242,17 @@ int kvattn_synchronize(kvattn_t h);
  * ring slot.
  */
 int kvattn_debug_read_page(kvattn_t h, uint32_t layer, uint32_t logical_page, void *h_out);
+
+/*
+ * Test aid: while d_counter is non-NULL (a caller-owned device uint32, zeroed
+ * by the caller), the attention kernels of later calls add one to it per
+ * softmax re-reference event: a 16-row tile whose running reference exists
+ * meets a score more than 8 (log2 units) above it, rescales its accumulators
+ * and moves the reference (the online-softmax step that keeps the walk over
+ * the ordered history exact, "troed's fork ...", section "Keep the stock
+ * attention order").  NULL stops counting.  KVATTN_E_ARG if misaligned.
+ */
+int kvattn_debug_count_rescales(kvattn_t h, uint32_t *d_counter);
 
 /*
  * Host only (no GPU work): the page-table checks kvattn_set_layer applies

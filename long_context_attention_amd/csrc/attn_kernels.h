@@ -36,6 +36,9 @@ struct SplitArgs {
     // (0 past the last page); page-list and wide launches set n_pre_splits = 0
     uint32_t n_pre_splits;
     uint32_t pre_entries[kPreSplits * kPrePages];
+    // test aid: when non-null, the kernels add one per softmax re-reference
+    // event (a row tile moving a reference it already had)
+    uint32_t *rescale_count;
 };
 
 struct MergeArgs {

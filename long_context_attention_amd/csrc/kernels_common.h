@@ -476,12 +476,16 @@ __device__ __forceinline__ void chunk_scores(const RowState (&st)[NT], const uin
 // before the first key) the reference moves to the row maximum, the
 // accumulators and the denominator are rescaled, and s is shifted to the new
 // reference.
-__device__ __forceinline__ void update_reference(RowState &st, float (&s)[8]) {
+// counter (test aid, normally null): one is added per event in which a row
+// tile that already had a reference moves it, so a test can show that its
+// inputs reach this branch.
+__device__ __forceinline__ void update_reference(RowState &st, float (&s)[8], uint32_t *counter) {
     float m = s[0];
 #pragma unroll
     for (int i = 1; i < 8; i++) m = fmaxf(m, s[i]);
     const float thr = st.m_ref == kNegInf ? kNegInf : kRescale;
     if (__any(m > thr)) {
+        if (counter && __any(st.m_ref != kNegInf) && (threadIdx.x & 63) == 0) atomicAdd(counter, 1u);
         m = fmaxf(m, __shfl_xor(m, 16));
         m = fmaxf(m, __shfl_xor(m, 32));
         const float ref = score_ref(st);
@@ -560,8 +564,8 @@ __device__ __forceinline__ uint32_t pv_pair(const float (&p)[8], const uint32_t 
 // values.
 template <int VT>
 __device__ __forceinline__ void chunk_probs(RowState &st, float (&s)[8], const uint32_t vd[16],
-                                            half8 (&pf)[VT == kTypeF16 ? 1 : 4]) {
-    update_reference(st, s);
+                                            half8 (&pf)[VT == kTypeF16 ? 1 : 4], uint32_t *counter) {
+    update_reference(st, s, counter);
     float p[8];
     float lsum = 0.f;
 #pragma unroll

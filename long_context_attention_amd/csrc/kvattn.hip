@@ -199,6 +199,8 @@ struct kvattn {
     int device = 0;
     int n_cus = 256;
     hipEvent_t upload_done = nullptr;
+    hipEvent_t compute_mark = nullptr;  // compute-stream position uploads wait for
+    uint32_t *dbg_rescales = nullptr;   // test aid: re-reference event counter (device)
     std::vector<LayerState> layers;
     StreamScheduler sched;
     bool any_streamed = false, any_ring_slots = false;
@@ -275,6 +277,7 @@ SplitArgs base_args(kvattn_t h, uint32_t layer, uint32_t W, const float *q) {
     a.q = q;
     a.part_o = h->part_o();
     a.part_ml = h->part_ml();
+    a.rescale_count = h->dbg_rescales;
     return a;
 }
 
@@ -691,6 +694,7 @@ int kvattn_create(const kvattn_params *params, void *d_pool, size_t pool_bytes, 
     h->layers.resize(p.n_layers);
     hipError_t e = hipGetDevice(&h->device);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&h->upload_done, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&h->compute_mark, hipEventDisableTiming);
     if (e == hipSuccess) h->n_cus = n_cus_of(h->device);
     if (e == hipSuccess) e = kvattn_split_setup();
     if (e != hipSuccess) {
@@ -703,6 +707,7 @@ int kvattn_create(const kvattn_params *params, void *d_pool, size_t pool_bytes, 
     if (p.n_ring_slots) {
         if (!h->sched.init(p.n_layers, p.n_ring_slots, std::min(chunk, p.n_ring_slots))) {
             (void)hipEventDestroy(h->upload_done);
+            (void)hipEventDestroy(h->compute_mark);
             delete h;
             return fail(nullptr, KVATTN_E_HIP, "ring event setup failed");
         }
@@ -727,6 +732,13 @@ int kvattn_upload_pages(kvattn_t h, const void *h_pages, const uint32_t *dst, ui
     }
     const size_t pb = h->lay.page_bytes;
     const uint8_t *src = static_cast<const uint8_t *>(h_pages);
+    // the copies overwrite pages that kernels already enqueued on the compute
+    // stream may still read: they start once the compute stream has passed
+    // everything enqueued before this call
+    if (h->copy != h->compute) {
+        HIP_TRY(h, hipEventRecord(h->compute_mark, h->compute));
+        HIP_TRY(h, hipStreamWaitEvent(h->copy, h->compute_mark, 0));
+    }
     for (uint32_t i = 0; i < n; i++) {
         uint32_t e = dst[i];
         uint8_t *d = (e & KVATTN_PT_RING_FLAG) ? h->ring + (size_t)(e & ~KVATTN_PT_RING_FLAG) * pb : h->pool + (size_t)e * pb;
@@ -916,6 +928,13 @@ int kvattn_debug_read_page(kvattn_t h, uint32_t layer, uint32_t logical_page, vo
     return KVATTN_OK;
 }
 
+int kvattn_debug_count_rescales(kvattn_t h, uint32_t *d_counter) {
+    if (!h) return fail(nullptr, KVATTN_E_ARG, "null handle");
+    if (reinterpret_cast<uintptr_t>(d_counter) & 3) return fail(h, KVATTN_E_ARG, "counter must be 4-byte aligned");
+    h->dbg_rescales = d_counter;
+    return KVATTN_OK;
+}
+
 int kvattn_profile(kvattn_t h, uint32_t max_launches) {
     if (!h) return fail(nullptr, KVATTN_E_ARG, "null handle");
     if (max_launches == 0) {
@@ -1082,6 +1101,7 @@ int kvattn_destroy(kvattn_t h) {
     if (hipStreamSynchronize(h->compute) != hipSuccess) rc = KVATTN_E_HIP;
     h->sched.destroy();
     if (h->upload_done) (void)hipEventDestroy(h->upload_done);
+    if (h->compute_mark) (void)hipEventDestroy(h->compute_mark);
     for (hipEvent_t e : h->prof_ev)
         if (e) (void)hipEventDestroy(e);
     for (hipEvent_t e : h->obs_ev)

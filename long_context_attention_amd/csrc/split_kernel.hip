@@ -240,7 +240,7 @@ __global__ __launch_bounds__((64 * SplitCfg<NT, KT, VT>::waves), 1) void split_k
                 read_vscales<KT, VT>(stg, grp, vd);
             }
 #pragma unroll
-            for (int t = 0; t < NT; t++) chunk_probs<VT>(st[t], s[t], vd, pv_pf[t]);
+            for (int t = 0; t < NT; t++) chunk_probs<VT>(st[t], s[t], vd, pv_pf[t], a.rescale_count);
             read_vcodes<KT, VT>(stg, lane, pv_vq);
             if constexpr (!C::vblk)
                 if (tail) clear_padding_vcodes<KT, VT>(pv_vq, grp, a.n_tokens - 32 * c);

@@ -60,8 +60,8 @@ __device__ __forceinline__ void view_scores(const RowState (&st)[NT], const uint
 
 // Softmax step of one chunk for one row tile from its relative scores (lazy
 // reference as in chunk_probs); P rounded to binary16 once.
-__device__ __forceinline__ void view_probs(RowState &st, float (&s)[8], half8 &pf) {
-    update_reference(st, s);
+__device__ __forceinline__ void view_probs(RowState &st, float (&s)[8], half8 &pf, uint32_t *counter) {
+    update_reference(st, s, counter);
     float p[8];
     float lsum = 0.f;
 #pragma unroll
@@ -262,7 +262,7 @@ __global__ __launch_bounds__((64 * WAVES), 1) void wide_kernel(const SplitArgs a
         view_scores<NT>(st, view, lane, s);
         if (c >= clean_end) mask_scores<NT>(st, 32 * c, grp, s);
 #pragma unroll
-        for (int t = 0; t < NT; t++) view_probs(st[t], s[t], pf[t]);
+        for (int t = 0; t < NT; t++) view_probs(st[t], s[t], pf[t], a.rescale_count);
         view_pv<NT>(st, view, lane, pf);
     };
     // step of two chunks: p and p + 1 are computed from their views while

@@ -91,7 +91,7 @@ _lib = None
 EXPORTS = ["kvattn_supported", "kvattn_page_bytes", "kvattn_workspace_bytes", "kvattn_create",
            "kvattn_upload_pages", "kvattn_set_layer", "kvattn_decode", "kvattn_verify", "kvattn_prefill_chunk",
            "kvattn_append",
-           "kvattn_synchronize", "kvattn_debug_read_page", "kvattn_validate_page_table", "kvattn_sched_simulate",
+           "kvattn_synchronize", "kvattn_debug_read_page", "kvattn_debug_count_rescales", "kvattn_validate_page_table", "kvattn_sched_simulate",
            "kvattn_profile", "kvattn_profile_read", "kvattn_policy_step", "kvattn_observe", "kvattn_observe_read",
            "kvattn_set_ring_slots", "kvattn_destroy",
            "kvattn_last_error", "kvattn_global_error"]
@@ -132,6 +132,8 @@ def lib():
     L.kvattn_synchronize.restype = I
     L.kvattn_debug_read_page.argtypes = [P, U, U, P]
     L.kvattn_debug_read_page.restype = I
+    L.kvattn_debug_count_rescales.argtypes = [P, P]
+    L.kvattn_debug_count_rescales.restype = I
     L.kvattn_validate_page_table.argtypes = [PP, P, U, I]
     L.kvattn_validate_page_table.restype = I
     L.kvattn_sched_simulate.argtypes = [U, U, U, P, P, U, P, U, ctypes.POINTER(U)]
@@ -283,6 +285,11 @@ class Handle:
         out = np.empty(page_bytes(self.params), dtype=np.uint8)
         _check(lib().kvattn_debug_read_page(self.h, layer, logical_page, out.ctypes.data), self.h)
         return out
+
+    def count_rescales(self, counter):
+        """Test aid: counter is a device uint32 tensor (zeroed by the caller)
+        that later calls increment per softmax re-reference event; None stops."""
+        _check(lib().kvattn_debug_count_rescales(self.h, None if counter is None else _addr(counter)), self.h)
 
     def profile(self, max_launches):
         _check(lib().kvattn_profile(self.h, max_launches), self.h)

@@ -11,6 +11,7 @@ import torch
 
 import inputs
 import long_context_attention_amd as kv
+import oracle
 from gpu_util import TOL, handle, oracle_out, place, run, say
 
 pytestmark = pytest.mark.gpu
@@ -259,11 +260,12 @@ def test_full_size_decode_sampled_layers():
     h.destroy()
 
 
-@pytest.mark.parametrize("W,layer", [(6, 5), (1, 6)])
+@pytest.mark.parametrize("W,layer", [(6, 5), (1, 6), (2, 7), (3, 8), (4, 9), (5, 10)])
 def test_full_size_verify(W, layer):
     """The all-resident verify workload at full size (163,840 tokens, causal
-    tail) with the automatic split plan the benchmark uses; two seeded layers
-    (W = 6 and W = 1), every output element against the oracle."""
+    tail) with the automatic split plan the benchmark uses (160-chunk splits:
+    the claimed chunk order); one seeded layer per width 1-6, every output
+    element against the oracle."""
     w = inputs.WORKLOADS["verify-160k"]
     say(f"case full-size {w.name} W={W}: layer {layer}")
     n = w.n_pages
@@ -322,17 +324,21 @@ def test_full_size_prefill_sampled_rows():
     h.destroy()
 
 
-def test_full_size_streamed_layer():
+@pytest.mark.parametrize("W", [1, 4])
+def test_full_size_streamed_layer(W):
     """The streamed workload at full size: 262,144 tokens, 410 resident pages,
     614 streamed from a pinned history through a 64-slot ring (default chunk
-    size), W = 4, two layers called in order; every output element against the
-    oracle reading the same bytes."""
+    size), two layers.  Both layers are set before the first call, so the
+    ring copies of layer 1 start while layer 0 computes (one layer ahead) and
+    the ring wraps across the layer boundary; every output element of both
+    layers against the oracle reading the same bytes."""
     w = inputs.WORKLOADS["stream-256k"]
-    W, L = 4, 2
-    say(f"case full-size {w.name} W={W}: {L} layers")
+    L = 2
+    say(f"case full-size {w.name} W={W}: {L} layers, both set before the first call")
     n = w.n_pages
     h = handle(w.n_q_heads, w.n_kv_heads, L * w.n_resident, n, 8, n_ring=w.ring_slots, n_layers=L)
     pb = kv.page_bytes(h.params)
+    hosts, qs = [], []
     for l in range(L):
         kvl = inputs.draw_layer(w.n_tokens, w.n_kv_heads, l, w.wid, device="cuda")
         res = inputs.resident_subset(n, w.n_resident, l, w.wid)
@@ -341,11 +347,51 @@ def test_full_size_streamed_layer():
         host = torch.empty((n, pb), dtype=torch.uint8, pin_memory=True)
         host.copy_(kvl.pages)
         place(h, l, kvl, table, history=host)
-        q = inputs.draw_queries(W, w.n_q_heads, l, w.wid, device="cuda")
-        got = run(h, l, q, W, "verify")
-        ref = oracle_out(kvl, q, w.n_q_heads, w.n_kv_heads)
-        err = np.max(np.abs(got - ref))
+        hosts.append(host)
+        qs.append(inputs.draw_queries(W, w.n_q_heads, l, w.wid, device="cuda"))
+        del kvl
+    outs = []
+    for l in range(L):
+        o = torch.full_like(qs[l], float("nan"))
+        h.verify(l, qs[l], W, o)
+        outs.append(o)
+    h.synchronize()
+    for l in range(L):
+        ref, _ = oracle.attend_paged(np.arange(n, dtype=np.uint32), w.n_tokens, 256, w.n_q_heads, w.n_kv_heads,
+                                     qs[l].cpu().numpy(), inputs.scale_for(), pool=hosts[l].numpy())
+        err = np.max(np.abs(outs[l].cpu().double().numpy() - ref))
         say(f"  layer {l}: max-abs err {err:.3e}")
         assert err <= TOL
-        del kvl, host
+    h.destroy()
+
+
+def test_upload_waits_for_compute():
+    """kvattn_upload_pages into ring slots that calls already enqueued on the
+    compute stream still read: the copies start only after those calls, so
+    every earlier output sees the old pages and the next call the new ones
+    (no synchronisation between the calls and the upload)."""
+    N, Hq, Hkv, W, calls = 64 * 256, 40, 8, 4, 24
+    say(f"case upload ordering N={N} W={W}: {calls} calls, then a re-upload of every slot, then one call")
+    a, b = layer_kv(N, Hkv, wid=90), layer_kv(N, Hkv, wid=91)
+    n = a.pages.shape[0]
+    q = inputs.draw_queries(W, Hq, 0, 90)
+    h = handle(Hq, Hkv, 1, n, 8, n_ring=n)
+    assert h.copy_stream is not None and h.copy_stream != h.compute_stream
+    slots = np.arange(n, dtype=np.uint32)
+    ha, hb = a.pages.contiguous().pin_memory(), b.pages.contiguous().pin_memory()
+    h.upload_pages(ha, kv.PT_RING_FLAG | slots)
+    h.set_layer(0, kv.PT_RING_FLAG | slots, N)
+    h.synchronize()
+    qd = q.cuda()
+    outs = [torch.empty_like(qd) for _ in range(calls + 1)]
+    for i in range(calls):
+        h.verify(0, qd, W, outs[i])
+    h.upload_pages(hb, kv.PT_RING_FLAG | slots)
+    h.verify(0, qd, W, outs[calls])
+    h.synchronize()
+    ref_a, ref_b = oracle_out(a, q, Hq, Hkv), oracle_out(b, q, Hq, Hkv)
+    errs = [float(np.max(np.abs(o.cpu().double().numpy() - ref_a))) for o in outs[:calls]]
+    err_b = float(np.max(np.abs(outs[calls].cpu().double().numpy() - ref_b)))
+    say(f"  before the upload: worst max-abs err {max(errs):.3e}; after: {err_b:.3e}")
+    assert max(errs) <= TOL and err_b <= TOL
     h.destroy()
