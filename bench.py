@@ -338,25 +338,42 @@ def adaptive_run(h, w, hist, qs, outs, kind, rows, n_layers, steps, torch, kv, m
 
 
 # --------------------------------------------------------------------------- machine
+def _sysfs_clock(dev_dir, name):
+    """Current level of a pp_dpm_* table ("<i>: <f>Mhz *" marks it), in MHz."""
+    try:
+        with open(os.path.join(dev_dir, name)) as f:
+            for line in f:
+                if line.rstrip().endswith("*"):
+                    return line.split(":", 1)[1].strip().rstrip("*").strip().lower().replace("mhz", "").strip()
+    except OSError:
+        pass
+    return None
+
+
 def gpu_info(torch):
-    """Device name and CU count, plus the current clocks rocm-smi reports (best
-    effort: absent when the tool is not there)."""
+    """Device name and CU count, plus the current shader and memory clocks read
+    from the device's sysfs tables (pp_dpm_sclk / pp_dpm_mclk; absent when
+    they are not readable).  No child process is started."""
     props = torch.cuda.get_device_properties(0)
     info = {"name": props.name, "arch": getattr(props, "gcnArchName", ""), "compute_units": props.multi_processor_count}
-    # under a profiler the child would inherit its preloaded library, which
-    # initialises the GPU before rocm-smi's interpreter replaces the launcher
-    if "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ):
-        return info
+    dirs = []
+    bus = getattr(props, "pci_bus_id", None)
+    if bus is not None:
+        dom, dev = getattr(props, "pci_domain_id", 0), getattr(props, "pci_device_id", 0)
+        dirs.append(f"/sys/bus/pci/devices/{dom:04x}:{bus:02x}:{dev:02x}.0")
     try:
-        import subprocess
-        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=10).stdout
-        for line in out.splitlines():
-            low = line.lower()
-            for key in ("sclk", "mclk", "fclk"):
-                if f"{key} clock level" in low and "mhz" in low:
-                    info.setdefault(f"{key}_mhz", line.split("(")[-1].split("Mhz")[0].split("MHz")[0].strip())
-    except Exception:
+        cards = sorted(d for d in os.listdir("/sys/class/drm") if d.startswith("card") and "-" not in d)
+        found = [f"/sys/class/drm/{c}/device" for c in cards if os.path.exists(f"/sys/class/drm/{c}/device/pp_dpm_sclk")]
+        if len(found) == 1:
+            dirs.append(found[0])
+    except OSError:
         pass
+    for d in dirs:
+        sclk, mclk = _sysfs_clock(d, "pp_dpm_sclk"), _sysfs_clock(d, "pp_dpm_mclk")
+        if sclk or mclk:
+            info.update({k: v for k, v in (("sclk_mhz", sclk), ("mclk_mhz", mclk)) if v})
+            info["clock_source"] = os.path.join(d, "pp_dpm_*")
+            break
     return info
 
 

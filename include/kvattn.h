@@ -130,29 +130,60 @@ typedef struct kvattn_params {
 } kvattn_params;
 
 /* 1 if the K/V type pair and head_dim are implemented (the four pairs above,
- * head_dim 128), else 0. */
+ * head_dim 128), else 0: the capability a backend must advertise truthfully
+ * before any attention runs ("troed's fork ...", section "Backend-neutral
+ * memory and streaming contracts": the attention operations advertise the
+ * supported K/V pairs, and a port advertises only real support). */
 int kvattn_supported(uint32_t k_type, uint32_t v_type, uint32_t head_dim);
 
-/* Bytes of one page (0 if the parameters are invalid). */
+/* Bytes of one page (0 if the parameters are invalid), computed from the
+ * actual K and V types and the geometry ("troed's fork ...", section
+ * "Backend-neutral memory and streaming contracts": page offsets follow the
+ * quant types; section "KV data movement and attention": 256-position
+ * pages).  No allocation, no GPU work. */
 size_t kvattn_page_bytes(const kvattn_params *params);
 
 /* Bytes the caller must provide as d_workspace (0 if the parameters are
  * invalid): device page tables, page lists, one staging page and the split
- * partials (m, l, acc[128] per split, row and query head, fp32). */
+ * partials (m, l, acc[128] per split, row and query head, fp32).  The
+ * attention operations expose their workspace size beside the span call so
+ * the caller can budget it ("troed's fork ...", section "Backend-neutral
+ * memory and streaming contracts"; "Adaptive KV Streaming for llama.cpp",
+ * section "Batch and micro-batch sizes": a bounded query workspace). */
 size_t kvattn_workspace_bytes(const kvattn_params *params);
 
 /*
- * Create a handle.  d_pool: n_pool_pages pages (pool_bytes >= that);
- * d_ring: n_ring_slots pages or NULL when n_ring_slots is 0; d_workspace:
- * kvattn_workspace_bytes bytes.  compute_stream runs the kernels;
- * copy_stream runs host-to-device page copies (it may equal compute_stream).
- * The current HIP device must be the one that owns the buffers.
+ * Create a handle: the backend side of the pages' streaming contract, which
+ * owns no memory.  It names regions of allocations the caller already made
+ * (pool, ring, workspace) without copying them, and supplies what the
+ * contract leaves to the backend -- asynchronous host-to-device copies,
+ * ready / consumed fences between a copy stream and a compute stream, KV
+ * writes and attention over the history ("troed's fork ...", section
+ * "Backend-neutral memory and streaming contracts": views of existing
+ * allocations, and the backend adapter's copy, fence, write and attention
+ * operations).
+ * d_pool: n_pool_pages pages (pool_bytes >= that); d_ring: n_ring_slots pages
+ * or NULL when n_ring_slots is 0; d_workspace: kvattn_workspace_bytes bytes;
+ * all 16-byte aligned device memory, owned by the caller, outliving the
+ * handle.  compute_stream runs the kernels; copy_stream runs host-to-device
+ * page copies (it may equal compute_stream).  The current HIP device must be
+ * the one that owns the buffers.  Errors: KVATTN_E_ARG (null or misaligned
+ * buffer, null out), KVATTN_E_UNSUPPORTED / KVATTN_E_RANGE (parameters),
+ * KVATTN_E_NOSPACE (a buffer smaller than the parameters need),
+ * KVATTN_E_HIP; the message is in kvattn_global_error().  On error *out is
+ * NULL and nothing was enqueued.
  */
 int kvattn_create(const kvattn_params *params, void *d_pool, size_t pool_bytes, void *d_ring,
                   size_t ring_bytes, void *d_workspace, size_t workspace_bytes, void *compute_stream,
                   void *copy_stream, kvattn_t *out);
 
 /*
+ * Place pages: the span copy of the pages' copy-operations table, which
+ * enqueues a host-to-device copy of K/V bytes into device slots and fences
+ * it for the consumer ("troed's fork ...", section "Backend-neutral memory
+ * and streaming contracts": the copy operations and ready / consumed fences;
+ * section "KV data movement and attention": a ready fence before a read, a
+ * consumed fence before a slot is reused).
  * Copy n pages from host memory h_pages (n * page_bytes, pinned for an
  * asynchronous copy) to the pool pages or ring slots named by dst[i]
  * (pool id, or KVATTN_PT_RING(slot)).  The copy runs on the copy stream,
@@ -164,9 +195,17 @@ int kvattn_create(const kvattn_params *params, void *d_pool, size_t pool_bytes, 
 int kvattn_upload_pages(kvattn_t h, const void *h_pages, const uint32_t *dst, uint32_t n);
 
 /*
- * Set layer `layer`'s history: n_tokens positions in ceil(n_tokens /
- * page_tokens) logical pages, page_table[P] naming where logical page P
- * lives.  Rejects (KVATTN_E_PLAN) a table that names one physical page
+ * Set layer `layer`'s history, the pages' span plan: one attention history
+ * as logical pages in order, each placed in the pool, a ring slot or the
+ * host history, validated so that no physical page serves two logical ones
+ * and every logical page up to n_tokens is covered once ("troed's fork ...",
+ * section "Backend-neutral memory and streaming contracts": the plan rejects
+ * gaps, overlaps and insufficient coverage; a table with one entry per
+ * logical page cannot have gaps, and an overlap is a physical page named
+ * twice).
+ * n_tokens positions in ceil(n_tokens / page_tokens) logical pages,
+ * page_table[P] (host memory, read during the call) naming where logical
+ * page P lives.  Rejects (KVATTN_E_PLAN) a table that names one physical page
  * twice, names KVATTN_PT_HOST without a host history, or mixes
  * caller-placed ring slots with streamed pages on one handle (the scheduler
  * owns the ring once any page streams).  h_history: the layer's pages in
@@ -232,14 +271,22 @@ int kvattn_prefill_chunk(kvattn_t h, uint32_t layer, const float *d_q, uint32_t 
 int kvattn_append(kvattn_t h, uint32_t layer, const float *d_k, const float *d_v, uint32_t R,
                   const uint32_t *new_pages, uint32_t n_new, void *h_publish);
 
-/* Block the host until both streams have finished the handle's work. */
+/* Completion fence: block the host until both streams have finished the
+ * handle's work, so every buffer the handle's calls used may be reused or
+ * freed.  Holding a buffer does not prove that queued GPU work stopped using
+ * it; only such a fence does ("troed's fork ...", sections "Phase arena" and
+ * "Backend-neutral memory and streaming contracts").  KVATTN_E_ARG for a null
+ * handle, KVATTN_E_HIP if a stream reports an error. */
 int kvattn_synchronize(kvattn_t h);
 
 /*
  * Test aid: copy the bytes of `layer`'s logical page through the kernels'
  * own device-side page resolver into h_out (page_bytes of host memory).
  * Synchronous.  Streamed pages resolve to their most recently assigned
- * ring slot.
+ * ring slot.  It shows the resolver returns the bytes of the logical page
+ * wherever the page lives, which is what keeps placement out of the result
+ * ("Adaptive KV Streaming for llama.cpp", section "Adaptive KV streaming").
+ * Errors: KVATTN_E_RANGE, KVATTN_E_STATE (layer not set), KVATTN_E_ARG.
  */
 int kvattn_debug_read_page(kvattn_t h, uint32_t layer, uint32_t logical_page, void *h_out);
 
@@ -258,14 +305,19 @@ int kvattn_debug_count_rescales(kvattn_t h, uint32_t *d_counter);
  * Host only (no GPU work): the page-table checks kvattn_set_layer applies
  * that need no handle state -- range of pool ids and ring slots, no physical
  * page named twice, streamed pages need a host history (has_history != 0)
- * and a ring, page count within max_pages_per_layer.  Returns the status
- * kvattn_set_layer would return; the message is in kvattn_global_error().
+ * and a ring, page count within max_pages_per_layer (the span-plan checks of
+ * "troed's fork ...", section "Backend-neutral memory and streaming
+ * contracts").  Returns the status kvattn_set_layer would return; the
+ * message is in kvattn_global_error().
  */
 int kvattn_validate_page_table(const kvattn_params *params, const uint32_t *page_table, uint32_t n_tokens,
                                int has_history);
 
 /*
- * Test aid, host only (no GPU work): run the streaming planner over a
+ * Test aid, host only (no GPU work): run the streaming planner (ring slots
+ * filled in logical order, a ready fence before compute reads a chunk, a
+ * consumed fence before its slots are refilled, prefetch one layer ahead:
+ * "troed's fork ...", section "KV data movement and attention") over a
  * sequence of layer calls (call_layers[0 .. n_calls), layers with no streamed
  * pages skipped) for layers whose streamed-page counts are
  * streamed_counts[0 .. n_layers), and log the enqueue sequence the HIP path
@@ -285,7 +337,10 @@ int kvattn_sched_simulate(uint32_t n_layers, uint32_t n_slots, uint32_t chunk_sl
                           uint32_t *n_ops);
 
 /*
- * Profiling aid.  kvattn_profile(h, n) with n > 0 brackets each of the next
+ * Profiling aid (device time per kernel, so a rate is measured rather than
+ * read from busy time: "troed's fork ...", section "KV data movement and
+ * attention", copy-busy is not bandwidth).  kvattn_profile(h, n) with n > 0
+ * brackets each of the next
  * n kernel launches (split or merge) with timing events on the compute
  * stream; n = 0 stops.  kvattn_profile_read waits for the compute stream and
  * returns the summed device time (ms) and launch counts of the split and the
@@ -386,16 +441,26 @@ int kvattn_policy_step(const kvattn_policy_config *config, const kvattn_policy_s
 int kvattn_observe(kvattn_t h, uint32_t max_chunks);
 int kvattn_observe_read(kvattn_t h, int reset, kvattn_policy_observation *out);
 
-/* Ring slots the scheduler uses from now on (1 .. params.n_ring_slots).
- * Drains both streams and restarts the streaming schedule; pages of caller-
- * placed ring slots must lie below the new count. */
+/* Ring slots the scheduler uses from now on (1 .. params.n_ring_slots): how
+ * the policy's ring size is applied ("troed's fork ...", section "KV data
+ * movement and attention": the resident/ring split is adjusted with
+ * hysteresis).  Drains both streams and restarts the streaming schedule;
+ * pages of caller-placed ring slots must lie below the new count
+ * (KVATTN_E_RANGE otherwise). */
 int kvattn_set_ring_slots(kvattn_t h, uint32_t n_slots);
 
-/* Drain both streams, release events, free the handle (NULL is a no-op). */
+/* Drain both streams (the completion fence above), release the handle's
+ * events and free it; the caller's buffers are not touched.  Ending a use of
+ * the memory follows the pages' order: drain the work first, then release
+ * what held the memory ("troed's fork ...", sections "Phase arena" and
+ * "Backend-neutral memory and streaming contracts").  NULL is a no-op;
+ * KVATTN_E_HIP if draining failed (the handle is freed anyway). */
 int kvattn_destroy(kvattn_t h);
 
 /* Message of the handle's last failed call ("" if none); static text for
- * NULL.  Valid until the next call on the handle. */
+ * NULL.  Valid until the next call on the handle.  Failures are reported,
+ * never turned into an abort ("Block KV cache streaming ...", maintainer
+ * review: a too-small arena must become an error return). */
 const char *kvattn_last_error(kvattn_t h);
 
 /* Message of the last failure of a call that had no handle to report on

@@ -237,3 +237,33 @@ class StreamPlanner {
     bool started_ = false;
 };
 
+// One streamed layer's enqueue sequence, shared by the HIP path, the CPU
+// simulator (kvattn_sched_simulate) and the host checks built with
+// sanitizers: resident pages first (no wait), then each ring chunk after its
+// ready fence, recording its consumed fence; the copies of later chunks and
+// of the next streamed layer are enqueued as soon as the fence each depends
+// on has been recorded.
+template <class Exec>
+int drive_streamed_layer(StreamPlanner &pl, uint32_t layer, Exec &x) {
+    int rc;
+    if (!pl.begin_layer(layer)) {
+        if ((rc = x.drain())) return rc;  // out-of-order call: restart the schedule here
+        pl.restart(layer);
+        if (!pl.begin_layer(layer)) return x.internal("schedule restart failed");
+    }
+    x.begin(layer);
+    ChunkRef c;
+    while (pl.next_copy(&c))
+        if ((rc = x.copy(c))) return rc;
+    if ((rc = x.resident(layer))) return rc;
+    while (pl.next_compute(layer, &c)) {
+        if ((rc = x.compute(c))) return rc;
+        pl.mark_consumed(c);
+        while (pl.next_copy(&c))
+            if ((rc = x.copy(c))) return rc;
+    }
+    pl.end_layer(layer);
+    while (pl.next_copy(&c))
+        if ((rc = x.copy(c))) return rc;
+    return x.merge(layer);
+}
