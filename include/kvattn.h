@@ -264,9 +264,11 @@ int kvattn_prefill_chunk(kvattn_t h, uint32_t layer, const float *d_q, uint32_t 
  * pages in logical order (typically the layer's host history): after the
  * write, every page the new rows landed in is copied there (device to host
  * on the compute stream), so a host history stays authoritative.
- * Asynchronous on the compute stream, except that a call adding pages first
- * drains both streams to install the grown page table.  On KVATTN_E_HIP the
- * layer's state is undefined: set it again.
+ * Asynchronous on the compute stream, with no host wait: a call that adds
+ * pages writes their device page-table and page-list entries from a launch
+ * on the compute stream whose arguments carry them, ahead of the writer, so
+ * a call may be captured in a graph (replays rewrite the same entries).  On
+ * KVATTN_E_HIP the layer's state is undefined: set it again.
  */
 int kvattn_append(kvattn_t h, uint32_t layer, const float *d_k, const float *d_v, uint32_t R,
                   const uint32_t *new_pages, uint32_t n_new, void *h_publish);

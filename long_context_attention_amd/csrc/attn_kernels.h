@@ -76,7 +76,19 @@ struct WriterArgs {
     uint32_t k_type, v_type;
 };
 
+// Device page-table and page-list entries written by a launch whose
+// arguments carry their values: no host buffer and no host wait, so it can
+// sit in a captured graph.  dst_a[i] = a[i] and, when dst_b is set,
+// dst_b[i] = b[i] for i < n <= kTableWriteMax.
+constexpr uint32_t kTableWriteMax = 64;
+struct TableWriteArgs {
+    uint32_t *dst_a, *dst_b;
+    uint32_t n;
+    uint32_t a[kTableWriteMax], b[kTableWriteMax];
+};
+
 size_t kvattn_split_smem_bytes(int rt, uint32_t k_type, uint32_t v_type);
+hipError_t kvattn_launch_table_write(const TableWriteArgs &a, hipStream_t s);
 hipError_t kvattn_launch_writer(const WriterArgs &a, hipStream_t s);
 hipError_t kvattn_launch_ring_copy(const RingCopyArgs &a, hipStream_t s);
 hipError_t kvattn_split_setup();

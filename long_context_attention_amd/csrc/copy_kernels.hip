@@ -41,6 +41,17 @@ __global__ void read_page_kernel(const SplitArgs a, uint32_t logical_page, uint8
         reinterpret_cast<uint4 *>(dst)[i] = reinterpret_cast<const uint4 *>(src)[i];
 }
 
+// ---------------------------------------------------------------------------
+// Table write: entries carried by the launch arguments (one wave).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void table_write_kernel(const TableWriteArgs a) {
+    const uint32_t i = threadIdx.x;
+    if (i < a.n) {
+        a.dst_a[i] = a.a[i];
+        if (a.dst_b) a.dst_b[i] = a.b[i];
+    }
+}
+
 }  // namespace kvattn_dev
 
 // ---------------------------------------------------------------------------
@@ -55,5 +66,12 @@ hipError_t kvattn_launch_ring_copy(const RingCopyArgs &a, hipStream_t s) {
 hipError_t kvattn_launch_read_page(const SplitArgs &a, uint32_t logical_page, uint8_t *dst, hipStream_t s) {
     (void)hipGetLastError();
     hipLaunchKernelGGL(kvattn_dev::read_page_kernel, dim3(64), dim3(256), 0, s, a, logical_page, dst);
+    return hipGetLastError();
+}
+
+hipError_t kvattn_launch_table_write(const TableWriteArgs &a, hipStream_t s) {
+    (void)hipGetLastError();
+    if (a.n > kTableWriteMax) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kvattn_dev::table_write_kernel, dim3(1), dim3(64), 0, s, a);
     return hipGetLastError();
 }

@@ -37,6 +37,7 @@ constexpr size_t kAlign = 256;
 
 thread_local std::string g_error;
 
+
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
@@ -130,7 +131,7 @@ size_t partial_units(const kvattn_params &p) {
 }
 
 struct WsLayout {
-    size_t tables, lists, staging, part_ml, part_o, total;
+    size_t tables, rlists, slists, staging, part_ml, part_o, total;
 };
 
 WsLayout workspace_layout(const kvattn_params &p) {
@@ -138,8 +139,9 @@ WsLayout workspace_layout(const kvattn_params &p) {
     const size_t ents = (size_t)p.n_layers * p.max_pages_per_layer * sizeof(uint32_t);
     const size_t units = partial_units(p);
     w.tables = 0;
-    w.lists = align_up(ents);
-    w.staging = w.lists + align_up(ents);
+    w.rlists = align_up(ents);
+    w.slists = w.rlists + align_up(ents);
+    w.staging = w.slists + align_up(ents);
     w.part_ml = w.staging + align_up(page_layout(p).page_bytes);
     w.part_o = w.part_ml + align_up(units * 2 * sizeof(float));
     w.total = w.part_o + align_up(units * kHeadDim * sizeof(float));
@@ -222,7 +224,11 @@ struct kvattn {
     size_t prof_used = 0;
 
     uint32_t *d_table(uint32_t layer) { return reinterpret_cast<uint32_t *>(wsp + ws.tables) + (size_t)layer * p.max_pages_per_layer; }
-    uint32_t *d_list(uint32_t layer) { return reinterpret_cast<uint32_t *>(wsp + ws.lists) + (size_t)layer * p.max_pages_per_layer; }
+    // per layer: resident logical pages (ascending) and streamed logical
+    // pages (ascending, ordinal order), in separate lists so that a grown
+    // history appends resident pages without moving the streamed ones
+    uint32_t *d_rlist(uint32_t layer) { return reinterpret_cast<uint32_t *>(wsp + ws.rlists) + (size_t)layer * p.max_pages_per_layer; }
+    uint32_t *d_slist(uint32_t layer) { return reinterpret_cast<uint32_t *>(wsp + ws.slists) + (size_t)layer * p.max_pages_per_layer; }
     float *part_ml() { return reinterpret_cast<float *>(wsp + ws.part_ml); }
     float *part_o() { return reinterpret_cast<float *>(wsp + ws.part_o); }
 };
@@ -377,10 +383,16 @@ int launch_wide(kvattn_t h, const SplitArgs &a, uint32_t n_splits, uint32_t n_ro
     return KVATTN_OK;
 }
 
-int run_merge(kvattn_t h, uint32_t W, uint32_t n_splits, float *out) {
+// Where a call's split partials live.
+struct Partials {
+    float *o, *ml;
+};
+Partials workspace_partials(kvattn_t h) { return Partials{h->part_o(), h->part_ml()}; }
+
+int run_merge(kvattn_t h, uint32_t W, uint32_t n_splits, float *out, Partials parts) {
     MergeArgs m;
-    m.part_o = h->part_o();
-    m.part_ml = h->part_ml();
+    m.part_o = parts.o;
+    m.part_ml = parts.ml;
     m.n_splits = n_splits;
     m.units = W * h->p.n_q_heads;
     m.Hkv = h->p.n_kv_heads;
@@ -401,10 +413,11 @@ int n_cus_of(int device) {
 // Attention on a layer without streamed pages: partials, then the merge (a
 // separate launch measured cheaper than a device-wide release / counter /
 // acquire handshake at the end of the split kernel).
-int attend_resident(kvattn_t h, uint32_t layer, const float *q, uint32_t W, float *out) {
+int attend_resident(kvattn_t h, uint32_t layer, const float *q, uint32_t W, float *out, const Plan &pl, Partials parts) {
     const LayerState &L = h->layers[layer];
-    Plan pl = plan_resident(h->p, L.n_tokens, L.n_pages, W, h->n_cus);
     SplitArgs a = base_args(h, layer, W, q);
+    a.part_o = parts.o;
+    a.part_ml = parts.ml;
     a.split_chunks = pl.split_chunks;
     // split kernel: the first page entries of the first splits travel with
     // the launch
@@ -420,7 +433,7 @@ int attend_resident(kvattn_t h, uint32_t layer, const float *q, uint32_t W, floa
     a.dynamic_order = (!h->p.deterministic && pl.split_chunks >= kClaimMinChunks) ? 1u : 0u;
     const int rc = pl.wide ? launch_wide(h, a, pl.n_splits, pl.n_row_blocks, pl.wide_waves)
                            : launch_split(h, a, pl.n_splits, pl.n_row_blocks, pl.nrt);
-    return rc != KVATTN_OK ? rc : run_merge(h, W, pl.n_splits, out);
+    return rc != KVATTN_OK ? rc : run_merge(h, W, pl.n_splits, out, parts);
 }
 
 struct HipExec {
@@ -478,7 +491,7 @@ struct HipExec {
         if (L.history_dev) {
             RingCopyArgs r;
             r.history = L.history_dev;
-            r.list = h->d_list(c.layer) + L.n_resident;
+            r.list = h->d_slist(c.layer);
             r.ring = h->ring;
             r.first = c.first;
             r.count = c.count;
@@ -502,23 +515,24 @@ struct HipExec {
     int resident(uint32_t layer) {
         const LayerState &L = h->layers[layer];
         if (!L.n_resident) return KVATTN_OK;
+        a.page_list = h->d_rlist(layer);
         a.list_offset = 0;
         return launch_split(h, a, L.n_resident, 1, nrt);
     }
     int compute(const ChunkRef &c) {
-        const LayerState &L = h->layers[c.layer];
         const long ob = obs_slot(c, false);
         int rc;
         if (ob >= 0 && (rc = obs_record(ob, 2, h->compute))) return rc;
         HIP_TRY(h, hipStreamWaitEvent(h->compute, h->sched.ready_event(c.event), 0));
-        a.list_offset = L.n_resident + c.first;
+        a.page_list = h->d_slist(c.layer);
+        a.list_offset = c.first;
         a.ring_base = (uint32_t)(c.ordinal_base % h->ring_slots);
         if ((rc = launch_split(h, a, c.count, 1, nrt))) return rc;
         if (ob >= 0 && (rc = obs_record(ob, 3, h->compute))) return rc;
         HIP_TRY(h, hipEventRecord(h->sched.consumed_event(c.event), h->compute));
         return KVATTN_OK;
     }
-    int merge(uint32_t layer) { return run_merge(h, W, h->layers[layer].n_pages, out); }
+    int merge(uint32_t layer) { return run_merge(h, W, h->layers[layer].n_pages, out, workspace_partials(h)); }
 };
 
 int attend_streamed(kvattn_t h, uint32_t layer, const float *q, uint32_t W, float *out) {
@@ -526,7 +540,7 @@ int attend_streamed(kvattn_t h, uint32_t layer, const float *q, uint32_t W, floa
     if (W * G > kNarrowRows)
         return fail(h, KVATTN_E_UNSUPPORTED, "streamed layers support at most %u rows per KV head (W*G = %u)", kNarrowRows, W * G);
     HipExec x{h, W, q, out, base_args(h, layer, W, q), W * G <= 16 ? 1 : 2};
-    x.a.page_list = h->d_list(layer);
+    x.a.page_list = h->d_rlist(layer);
     return drive_streamed_layer(h->sched, layer, x);
 }
 
@@ -595,7 +609,8 @@ int attend(kvattn_t h, uint32_t layer, const float *q, uint32_t W, float *out, b
         if (prefill) return fail(h, KVATTN_E_UNSUPPORTED, "prefill chunks need an all-resident layer (layer %u streams %u pages)", layer, L.n_streamed);
         return attend_streamed(h, layer, q, W, out);
     }
-    return attend_resident(h, layer, q, W, out);
+    const Plan pl = plan_resident(h->p, L.n_tokens, L.n_pages, W, h->n_cus);
+    return attend_resident(h, layer, q, W, out, pl, workspace_partials(h));
 }
 
 }  // namespace
@@ -757,10 +772,11 @@ int install_layer(kvattn_t h, uint32_t layer, const uint32_t *page_table, uint32
     L.n_resident = (uint32_t)L.resident.size();
     L.n_streamed = (uint32_t)L.streamed.size();
     L.dev = dev;
-    std::vector<uint32_t> list(L.resident);
-    list.insert(list.end(), L.streamed.begin(), L.streamed.end());
     HIP_TRY(h, hipMemcpy(h->d_table(layer), dev.data(), n_pages * sizeof(uint32_t), hipMemcpyHostToDevice));
-    HIP_TRY(h, hipMemcpy(h->d_list(layer), list.data(), n_pages * sizeof(uint32_t), hipMemcpyHostToDevice));
+    if (L.n_resident)
+        HIP_TRY(h, hipMemcpy(h->d_rlist(layer), L.resident.data(), L.n_resident * sizeof(uint32_t), hipMemcpyHostToDevice));
+    if (L.n_streamed)
+        HIP_TRY(h, hipMemcpy(h->d_slist(layer), L.streamed.data(), L.n_streamed * sizeof(uint32_t), hipMemcpyHostToDevice));
     L.set = true;
     h->any_streamed = false;
     h->any_ring_slots = false;
@@ -829,12 +845,32 @@ int kvattn_append(kvattn_t h, uint32_t layer, const float *d_k, const float *d_v
         uint32_t n_pages = 0;
         int rc = validate_table(h, h->p, table.data(), (uint32_t)n_after, L.history != nullptr, &chk, &n_pages);
         if (rc) return rc;
-        // the new pages enter the device tables before the writer runs
-        rc = install_layer(h, layer, table.data(), (uint32_t)n_after, n_pages, L.history, chk);
-        if (rc) return rc;
-    } else {
-        L.n_tokens = (uint32_t)n_after;
+        // the new pages enter the device table and the resident list from
+        // launches on the compute stream, ahead of the writer, whose
+        // arguments carry the entries: no drain, no host copy, capturable
+        const uint32_t old_pages = L.n_pages, old_res = L.n_resident;
+        for (uint32_t k = 0; k < need; k += kTableWriteMax) {
+            TableWriteArgs tw{};
+            tw.n = std::min<uint32_t>(kTableWriteMax, need - k);
+            tw.dst_a = h->d_table(layer) + old_pages + k;
+            tw.dst_b = h->d_rlist(layer) + old_res + k;
+            for (uint32_t i = 0; i < tw.n; i++) {
+                tw.a[i] = new_pages[k + i];
+                tw.b[i] = old_pages + k + i;
+            }
+            HIP_TRY(h, kvattn_launch_table_write(tw, h->compute));
+        }
+        // host mirror of the grown history (the streamed pages and the
+        // schedule do not change: the new pages are resident)
+        for (uint32_t i = 0; i < need; i++) {
+            L.table.push_back(new_pages[i]);
+            L.dev.push_back(new_pages[i]);
+            L.resident.push_back(old_pages + i);
+        }
+        L.n_pages = n_pages;
+        L.n_resident = (uint32_t)L.resident.size();
     }
+    L.n_tokens = (uint32_t)n_after;
     WriterArgs w;
     w.pool = h->pool;
     w.ring = h->ring;

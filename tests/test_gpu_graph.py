@@ -14,6 +14,7 @@ import torch
 
 import inputs
 import long_context_attention_amd as kv
+import oracle
 from gpu_util import TOL, handle, oracle_out, place, say
 
 pytestmark = pytest.mark.gpu
@@ -136,4 +137,67 @@ def test_graph_replay_append_then_decode():
             h.decode(0, q, side)
         torch.cuda.synchronize()
         assert torch.equal(side.cpu(), out_e)
+    h.destroy()
+
+
+def test_graph_replay_append_crossing_page():
+    """An append whose rows cross into a new page, captured with a decode:
+    the new page's device entries come from a launch on the compute stream
+    (no drain, no host copy: capture would reject either).  Before each
+    replay the pool is restored and the layer is set with a decoy page in
+    the new slot of the table, so a replay that did not write the entry
+    would read the decoy; every replay must equal the eager calls bit for
+    bit, and the eager result the oracle over the written pages."""
+    N, Hq, Hkv, R = 2 * 256 - 3, 8, 2, 5
+    say(f"case graph append across a page N={N} R={R} Hq={Hq} Hkv={Hkv}")
+    kvl = inputs.draw_layer(N, Hkv, 0, 63)
+    n = kvl.pages.shape[0]
+    table = np.array([1, 0], dtype=np.uint32)
+    new_page, decoy = 3, 2
+    h = handle(Hq, Hkv, 4, 4, 8, split_pages=1, deterministic=1, compute_stream=torch.cuda.Stream())
+    place(h, 0, kvl, table)
+    pb = kv.page_bytes(h.params)
+    h.pool[decoy * pb:(decoy + 1) * pb].copy_(inputs.draw_layer(256, Hkv, 1, 63).pages[0].cuda())
+    saved = h.pool.clone()
+    g = torch.Generator(device="cuda").manual_seed(63)
+    k = torch.randn(R, Hkv, 128, device="cuda", generator=g)
+    v = torch.randn(R, Hkv, 128, device="cuda", generator=g)
+    q = _queries(1, Hq, 7)
+    stream = h.compute_stream
+
+    out_e = torch.full_like(q, float("nan"))
+    with torch.cuda.stream(stream):
+        h.append(0, k, v, R, new_pages=[new_page])
+        h.decode(0, q, out_e)
+    torch.cuda.synchronize()
+    pages_e = np.stack([h.debug_read_page(0, P) for P in range(n + 1)])
+    out_e = out_e.cpu()
+    ref, _ = oracle.attend_paged(np.arange(n + 1, dtype=np.uint32), N + R, 256, Hq, Hkv, q.cpu().numpy(),
+                                 inputs.scale_for(), pool=pages_e)
+    err = float(np.max(np.abs(out_e.double().numpy() - ref)))
+    say(f"  eager append + decode vs oracle: max-abs err {err:.3e}")
+    assert err <= TOL
+
+    h.pool.copy_(saved)
+    h.set_layer(0, table, N)
+    torch.cuda.synchronize()
+    out_g = torch.full_like(q, float("nan"))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        h.append(0, k, v, R, new_pages=[new_page])
+        h.decode(0, q, out_g)
+    torch.cuda.synchronize()
+
+    for i in range(REPLAYS):
+        h.pool.copy_(saved)
+        h.set_layer(0, np.append(table, decoy).astype(np.uint32), N + R)
+        out_g.fill_(float("nan"))
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g.cpu(), out_e), f"replay {i}: decode after the append differs"
+        h.set_layer(0, np.append(table, new_page).astype(np.uint32), N + R)
+        for P in range(n + 1):
+            assert np.array_equal(h.debug_read_page(0, P), pages_e[P]), f"replay {i}: page {P} differs"
     h.destroy()
