@@ -231,6 +231,23 @@ int kvattn_decode(kvattn_t h, uint32_t layer, const float *d_q, float *d_out);
 int kvattn_verify(kvattn_t h, uint32_t layer, const float *d_q, uint32_t W, float *d_out);
 
 /*
+ * kvattn_verify without a workspace scratch region, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same arguments, result and
+ * errors as kvattn_verify, for layers with no streamed pages
+ * (KVATTN_E_UNSUPPORTED otherwise).  The split partials go to a static
+ * device array of 8 MiB inside the library, one per GPU, held until the
+ * process ends; a call whose split plan needs more (split count x W x
+ * n_q_heads x 520 bytes, plus alignment: e.g. more than 96 rows per KV head
+ * at the workloads' sizes) fails with KVATTN_E_NOSPACE before enqueuing
+ * anything.  The call allocates nothing.  Every call on one GPU, from any
+ * handle, uses the same array: calls that may run at the same time on one
+ * GPU (different streams, or handles on different threads) race and must be
+ * ordered by the caller.
+ */
+int kvattn_verify_noalloc(kvattn_t h, uint32_t layer, const float *d_q, uint32_t W, float *d_out);
+
+/*
  * Prefill chunk: R query rows whose own keys are already the last R
  * positions of the history (row r sees keys 0 .. n_tokens - R + r).  Uses
  * the matrix-core path with splits sized for many rows ("Adaptive KV

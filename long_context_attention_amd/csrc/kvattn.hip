@@ -15,6 +15,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <tuple>
 #include <new>
 #include <string>
@@ -37,6 +38,34 @@ constexpr size_t kAlign = 256;
 
 thread_local std::string g_error;
 
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free entry point (kvattn_verify_noalloc): the
+// split partials of its calls live in this file-scope device array, one copy
+// per GPU, held until the process ends.  Host code never uses the array's
+// name as an address: kvattn_create takes the address once per device, with
+// that device current, from hipGetSymbolAddress.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (`device`), looked up
+// on the device's first use.
+hipError_t scratch_address(int device, void **out) {
+    *out = nullptr;
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[device]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[device] = p;
+    }
+    *out = g_scratch_ptr[device];
+    return hipSuccess;
+}
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -203,6 +232,8 @@ struct kvattn {
     hipEvent_t upload_done = nullptr;
     hipEvent_t compute_mark = nullptr;  // compute-stream position uploads wait for
     uint32_t *dbg_rescales = nullptr;   // test aid: re-reference event counter (device)
+    void *scratch = nullptr;            // this device's static scratch (kvattn_verify_noalloc)
+    hipError_t scratch_err = hipSuccess;
     std::vector<LayerState> layers;
     StreamScheduler sched;
     bool any_streamed = false, any_ring_slots = false;
@@ -383,7 +414,8 @@ int launch_wide(kvattn_t h, const SplitArgs &a, uint32_t n_splits, uint32_t n_ro
     return KVATTN_OK;
 }
 
-// Where a call's split partials live.
+// Where a call's split partials live: the workspace, or the static scratch
+// of the allocation-free entry point.
 struct Partials {
     float *o, *ml;
 };
@@ -681,6 +713,12 @@ int kvattn_create(const kvattn_params *params, void *d_pool, size_t pool_bytes, 
     if (e == hipSuccess) e = hipEventCreateWithFlags(&h->upload_done, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&h->compute_mark, hipEventDisableTiming);
     if (e == hipSuccess) h->n_cus = n_cus_of(h->device);
+    // the allocation-free entry point's scratch on this device (a failure
+    // is reported by that entry point, not here)
+    if (e == hipSuccess) {
+        h->scratch_err = scratch_address(h->device, &h->scratch);
+        if (h->scratch_err != hipSuccess) (void)hipGetLastError();
+    }
     if (e == hipSuccess) e = kvattn_split_setup();
     if (e != hipSuccess) {
         int code = fail(nullptr, KVATTN_E_HIP, "device / event setup failed: %s", hipGetErrorString(e));
@@ -910,6 +948,29 @@ int kvattn_verify(kvattn_t h, uint32_t layer, const float *d_q, uint32_t W, floa
 
 int kvattn_prefill_chunk(kvattn_t h, uint32_t layer, const float *d_q, uint32_t R, float *d_out) {
     return attend(h, layer, d_q, R, d_out, true);
+}
+
+int kvattn_verify_noalloc(kvattn_t h, uint32_t layer, const float *d_q, uint32_t W, float *d_out) {
+    int rc = validate_call(h, layer, d_q, W, d_out);
+    if (rc) return rc;
+    const LayerState &L = h->layers[layer];
+    if (L.n_streamed)
+        return fail(h, KVATTN_E_UNSUPPORTED, "kvattn_verify_noalloc needs an all-resident layer (layer %u streams %u pages)",
+                    layer, L.n_streamed);
+    if (!h->scratch)
+        return fail(h, KVATTN_E_HIP, "static scratch address unavailable: %s", hipGetErrorString(h->scratch_err));
+    const Plan pl = plan_resident(h->p, L.n_tokens, L.n_pages, W, h->n_cus);
+    const size_t units = (size_t)pl.n_splits * W * h->p.n_q_heads;
+    const size_t ml_bytes = align_up(units * 2 * sizeof(float));
+    const size_t need = ml_bytes + units * kHeadDim * sizeof(float);
+    if (need > kScratchBytes)
+        return fail(h, KVATTN_E_NOSPACE,
+                    "the call's split partials need %zu bytes (%u splits x %u rows x %u query heads), more than the "
+                    "static scratch's %zu",
+                    need, pl.n_splits, W, h->p.n_q_heads, kScratchBytes);
+    uint8_t *base = static_cast<uint8_t *>(h->scratch);
+    const Partials parts{reinterpret_cast<float *>(base + ml_bytes), reinterpret_cast<float *>(base)};
+    return attend_resident(h, layer, d_q, W, d_out, pl, parts);
 }
 
 int kvattn_synchronize(kvattn_t h) {

@@ -89,7 +89,8 @@ def policy_config(n_layers, page_tokens, budget_pages, min_ring_slots=16, max_ri
 
 _lib = None
 EXPORTS = ["kvattn_supported", "kvattn_page_bytes", "kvattn_workspace_bytes", "kvattn_create",
-           "kvattn_upload_pages", "kvattn_set_layer", "kvattn_decode", "kvattn_verify", "kvattn_prefill_chunk",
+           "kvattn_upload_pages", "kvattn_set_layer", "kvattn_decode", "kvattn_verify", "kvattn_verify_noalloc",
+           "kvattn_prefill_chunk",
            "kvattn_append",
            "kvattn_synchronize", "kvattn_debug_read_page", "kvattn_debug_count_rescales", "kvattn_validate_page_table", "kvattn_sched_simulate",
            "kvattn_profile", "kvattn_profile_read", "kvattn_policy_step", "kvattn_observe", "kvattn_observe_read",
@@ -124,6 +125,8 @@ def lib():
     L.kvattn_decode.restype = I
     L.kvattn_verify.argtypes = [P, U, P, U, P]
     L.kvattn_verify.restype = I
+    L.kvattn_verify_noalloc.argtypes = [P, U, P, U, P]
+    L.kvattn_verify_noalloc.restype = I
     L.kvattn_prefill_chunk.argtypes = [P, U, P, U, P]
     L.kvattn_prefill_chunk.restype = I
     L.kvattn_append.argtypes = [P, U, P, P, U, P, U, P]
@@ -263,6 +266,9 @@ class Handle:
 
     def verify(self, layer, q, W, out):
         _check(lib().kvattn_verify(self.h, layer, _addr(q), W, _addr(out)), self.h)
+
+    def verify_noalloc(self, layer, q, W, out):
+        _check(lib().kvattn_verify_noalloc(self.h, layer, _addr(q), W, _addr(out)), self.h)
 
     def prefill_chunk(self, layer, q, R, out):
         _check(lib().kvattn_prefill_chunk(self.h, layer, _addr(q), R, _addr(out)), self.h)
