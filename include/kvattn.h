@@ -225,7 +225,12 @@ int kvattn_set_layer(kvattn_t h, uint32_t layer, const uint32_t *page_table, uin
  * 0 .. n_tokens - W + r).  d_q: fp32 [W][n_q_heads][128]; d_out: fp32
  * [W][n_q_heads][128].  Both device memory.  Decode is W = 1
  * (TG1); verify is 1 + the draft length ("troed's fork ...", footnote 1).
- * 1 <= W <= min(max_rows, n_tokens).
+ * 1 <= W <= min(max_rows, n_tokens).  On a layer with streamed pages every
+ * width runs: each staged span of ring slots is consumed by all row tiles
+ * of the call before its slots are released, so a wider call moves no more
+ * host-to-device bytes than W = 1 ("Adaptive KV Streaming for llama.cpp",
+ * section "Batch and micro-batch sizes"; the second mirror of "troed's fork
+ * ...", footnotes: wide verify as consecutive row tiles over one KV span).
  */
 int kvattn_decode(kvattn_t h, uint32_t layer, const float *d_q, float *d_out);
 int kvattn_verify(kvattn_t h, uint32_t layer, const float *d_q, uint32_t W, float *d_out);
@@ -251,8 +256,10 @@ int kvattn_verify_noalloc(kvattn_t h, uint32_t layer, const float *d_q, uint32_t
  * Prefill chunk: R query rows whose own keys are already the last R
  * positions of the history (row r sees keys 0 .. n_tokens - R + r).  Uses
  * the matrix-core path with splits sized for many rows ("Adaptive KV
- * Streaming for llama.cpp", section "Batch and micro-batch sizes").  The
- * layer must have no streamed (KVATTN_PT_HOST) pages.
+ * Streaming for llama.cpp", section "Batch and micro-batch sizes").  Layers
+ * with streamed pages run it as above: all row tiles consume each staged
+ * span before it is released, with the split partials accumulated into a
+ * fixed set of slots (the bounded query workspace of that section).
  * 1 <= R <= min(max_rows, n_tokens).
  */
 int kvattn_prefill_chunk(kvattn_t h, uint32_t layer, const float *d_q, uint32_t R, float *d_out);

@@ -39,6 +39,12 @@ struct SplitArgs {
     // test aid: when non-null, the kernels add one per softmax re-reference
     // event (a row tile moving a reference it already had)
     uint32_t *rescale_count;
+    // partial slots (streamed calls of many rows): item i of the launch
+    // writes partial slot i (else the split kernel's page-list items write
+    // at their logical page); items below accum_slots combine with the
+    // partial the slot already holds (log-sum-exp) instead of replacing it
+    uint32_t slot_partials;
+    uint32_t accum_slots;
 };
 
 struct MergeArgs {

@@ -605,4 +605,19 @@ __device__ __forceinline__ void chunk_pv(RowState (&st)[NT], const uint32_t *vq,
     }
 }
 
+// Log-sum-exp combination of a stored partial (m0, l0, a0) with a new one
+// (m1, l1, a1), in log2 units; a side with l = 0 (no visible key) drops out.
+struct PartCombine {
+    float w0, w1, m, l;
+};
+__device__ __forceinline__ PartCombine part_combine(float m0, float l0, float m1, float l1) {
+    PartCombine c;
+    const bool e0 = !(l0 > 0.f), e1 = !(l1 > 0.f);
+    c.m = e0 ? m1 : (e1 ? m0 : fmaxf(m0, m1));
+    c.w0 = e0 ? 0.f : fast_exp2(m0 - c.m);
+    c.w1 = e1 ? 0.f : fast_exp2(m1 - c.m);
+    c.l = c.w0 * l0 + c.w1 * l1;
+    return c;
+}
+
 }  // namespace kvattn_dev

@@ -144,6 +144,13 @@ int check_params(const kvattn_params &p, std::string &why) {
     return KVATTN_OK;
 }
 
+// Partial slots of streamed calls of more than 32 rows per KV head: pages
+// per launch, at least the streamed chunk size.
+uint32_t stream_slots(const kvattn_params &p) {
+    const uint32_t chunk = p.chunk_slots ? p.chunk_slots : 16;
+    return std::max<uint32_t>(16, std::min(chunk, std::max<uint32_t>(p.n_ring_slots, 1)));
+}
+
 // Partial-buffer capacity in (split, row, query head) units.
 size_t partial_units(const kvattn_params &p) {
     const uint32_t G = p.n_q_heads / p.n_kv_heads;
@@ -156,7 +163,8 @@ size_t partial_units(const kvattn_params &p) {
     const uint64_t wide = std::min<uint64_t>((uint64_t)p.max_pages_per_layer * p.max_rows * p.n_q_heads,
                                              std::max<uint64_t>(kWideMaxWorkgroups * block,
                                                                 (uint64_t)p.max_rows * p.n_q_heads));
-    return (size_t)std::max(narrow, wide);
+    const uint64_t slotted = p.n_ring_slots ? (uint64_t)stream_slots(p) * p.max_rows * p.n_q_heads : 0;
+    return (size_t)std::max(std::max(narrow, wide), slotted);
 }
 
 struct WsLayout {
@@ -475,6 +483,23 @@ struct HipExec {
     float *out;
     SplitArgs a;
     int nrt;
+    // Calls of more than 32 rows per KV head: every launch covers at most
+    // `slots` pages, one per split, and item i of a launch accumulates into
+    // partial slot i, so the partials stay slots x rows however long the
+    // history; each staged ring chunk is read by all row blocks of the call
+    // before its consumed fence.  Up to 96 rows per KV head run the split
+    // kernel on row_blocks 32-row blocks, more the wide kernel.
+    bool slotted = false, wide = false;
+    uint32_t slots = 0, n_init = 0, row_blocks = 1;
+    int wide_waves = 8;
+
+    int launch_items(uint32_t n_items) {
+        a.accum_slots = n_init;
+        const int rc = wide ? launch_wide(h, a, n_items, row_blocks, wide_waves)
+                            : launch_split(h, a, n_items, row_blocks, nrt);
+        n_init = std::max(n_init, n_items);
+        return rc;
+    }
 
     int drain() {
         HIP_TRY(h, hipStreamSynchronize(h->copy));
@@ -549,7 +574,13 @@ struct HipExec {
         if (!L.n_resident) return KVATTN_OK;
         a.page_list = h->d_rlist(layer);
         a.list_offset = 0;
-        return launch_split(h, a, L.n_resident, 1, nrt);
+        if (!slotted) return launch_split(h, a, L.n_resident, 1, nrt);
+        for (uint32_t g = 0; g < L.n_resident; g += slots) {
+            a.list_offset = g;
+            const int rc = launch_items(std::min(slots, L.n_resident - g));
+            if (rc) return rc;
+        }
+        return KVATTN_OK;
     }
     int compute(const ChunkRef &c) {
         const long ob = obs_slot(c, false);
@@ -559,20 +590,31 @@ struct HipExec {
         a.page_list = h->d_slist(c.layer);
         a.list_offset = c.first;
         a.ring_base = (uint32_t)(c.ordinal_base % h->ring_slots);
-        if ((rc = launch_split(h, a, c.count, 1, nrt))) return rc;
+        if ((rc = slotted ? launch_items(c.count) : launch_split(h, a, c.count, 1, nrt))) return rc;
         if (ob >= 0 && (rc = obs_record(ob, 3, h->compute))) return rc;
         HIP_TRY(h, hipEventRecord(h->sched.consumed_event(c.event), h->compute));
         return KVATTN_OK;
     }
-    int merge(uint32_t layer) { return run_merge(h, W, h->layers[layer].n_pages, out, workspace_partials(h)); }
+    int merge(uint32_t layer) {
+        return run_merge(h, W, slotted ? n_init : h->layers[layer].n_pages, out, workspace_partials(h));
+    }
 };
 
 int attend_streamed(kvattn_t h, uint32_t layer, const float *q, uint32_t W, float *out) {
-    const uint32_t G = h->p.n_q_heads / h->p.n_kv_heads;
-    if (W * G > kNarrowRows)
-        return fail(h, KVATTN_E_UNSUPPORTED, "streamed layers support at most %u rows per KV head (W*G = %u)", kNarrowRows, W * G);
-    HipExec x{h, W, q, out, base_args(h, layer, W, q), W * G <= 16 ? 1 : 2};
+    const uint32_t rows = W * (h->p.n_q_heads / h->p.n_kv_heads);
+    HipExec x{h, W, q, out, base_args(h, layer, W, q), rows <= 16 ? 1 : 2};
     x.a.page_list = h->d_rlist(layer);
+    if (rows > kNarrowRows) {
+        // the same kernels and row blocks as a resident call of this width
+        const Plan pl = plan_resident(h->p, h->layers[layer].n_tokens, h->layers[layer].n_pages, W, h->n_cus);
+        x.slotted = true;
+        x.slots = stream_slots(h->p);
+        x.wide = pl.wide;
+        x.wide_waves = pl.wide_waves;
+        x.row_blocks = pl.n_row_blocks;
+        x.nrt = pl.nrt;
+        x.a.slot_partials = 1;
+    }
     return drive_streamed_layer(h->sched, layer, x);
 }
 
@@ -633,14 +675,11 @@ int validate_table(kvattn_t h, const kvattn_params &p, const uint32_t *page_tabl
     return KVATTN_OK;
 }
 
-int attend(kvattn_t h, uint32_t layer, const float *q, uint32_t W, float *out, bool prefill) {
+int attend(kvattn_t h, uint32_t layer, const float *q, uint32_t W, float *out) {
     int rc = validate_call(h, layer, q, W, out);
     if (rc) return rc;
     const LayerState &L = h->layers[layer];
-    if (L.n_streamed) {
-        if (prefill) return fail(h, KVATTN_E_UNSUPPORTED, "prefill chunks need an all-resident layer (layer %u streams %u pages)", layer, L.n_streamed);
-        return attend_streamed(h, layer, q, W, out);
-    }
+    if (L.n_streamed) return attend_streamed(h, layer, q, W, out);
     const Plan pl = plan_resident(h->p, L.n_tokens, L.n_pages, W, h->n_cus);
     return attend_resident(h, layer, q, W, out, pl, workspace_partials(h));
 }
@@ -940,14 +979,14 @@ int kvattn_append(kvattn_t h, uint32_t layer, const float *d_k, const float *d_v
     return KVATTN_OK;
 }
 
-int kvattn_decode(kvattn_t h, uint32_t layer, const float *d_q, float *d_out) { return attend(h, layer, d_q, 1, d_out, false); }
+int kvattn_decode(kvattn_t h, uint32_t layer, const float *d_q, float *d_out) { return attend(h, layer, d_q, 1, d_out); }
 
 int kvattn_verify(kvattn_t h, uint32_t layer, const float *d_q, uint32_t W, float *d_out) {
-    return attend(h, layer, d_q, W, d_out, false);
+    return attend(h, layer, d_q, W, d_out);
 }
 
 int kvattn_prefill_chunk(kvattn_t h, uint32_t layer, const float *d_q, uint32_t R, float *d_out) {
-    return attend(h, layer, d_q, R, d_out, true);
+    return attend(h, layer, d_q, R, d_out);
 }
 
 int kvattn_verify_noalloc(kvattn_t h, uint32_t layer, const float *d_q, uint32_t W, float *d_out) {

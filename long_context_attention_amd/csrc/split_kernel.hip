@@ -32,7 +32,7 @@ struct SplitCfg {
     static constexpr int ring_bytes = stages * C::bytes;
     // the combine after the loop reuses the rings: per wave and row of one
     // 16-row tile, m, l and a padded 132-float accumulator row
-    static constexpr int combine_bytes = waves * 16 * (2 + 132) * 4;
+    static constexpr int combine_bytes = waves * 16 * (2 + 132) * 4 + 32 * 4;
     static constexpr int lds_bytes = waves * ring_bytes > combine_bytes ? waves * ring_bytes : combine_bytes;
     static_assert(lds_bytes <= 163840, "LDS budget");
 };
@@ -261,7 +261,11 @@ __global__ __launch_bounds__((64 * SplitCfg<NT, KT, VT>::waves), 1) void split_k
     float *sm_m = reinterpret_cast<float *>(smem);
     float *sm_l = sm_m + kSplitWaves * 16;
     float *sm_o = sm_l + kSplitWaves * 16;
+    float *sm_old = sm_o + kSplitWaves * 16 * OS;  // stored (m, l) of the tile's rows (accumulating slots)
     const uint32_t units = a.W * a.Hq;
+    // partial written by this workgroup: its slot, or its page / range split
+    const uint32_t pidx = a.slot_partials ? item : split;
+    const bool accum = item < a.accum_slots;
 #pragma unroll
     for (int t = 0; t < NT; t++) {
         __syncthreads();  // rings (first tile) or the previous tile's reads are done
@@ -278,9 +282,18 @@ __global__ __launch_bounds__((64 * SplitCfg<NT, KT, VT>::waves), 1) void split_k
             for (int n = 0; n < 8; n++)
                 *reinterpret_cast<floatx4 *>(&sm_o[(wave * 16 + c16) * OS + 16 * n + 4 * grp]) = st[t].acc[n];
         }
-        __syncthreads();
         const uint32_t row0 = block_row0 + 16 * t;
         const uint32_t rows_here = row0 < rows_kv ? min(16u, rows_kv - row0) : 0u;
+        // an accumulating slot's stored (m, l) are read before any thread
+        // overwrites them
+        if (accum && threadIdx.x < rows_here) {
+            const uint32_t rk = row0 + threadIdx.x;
+            const uint32_t wq = rk / a.G, hh = rk - wq * a.G;
+            const size_t pu = (size_t)pidx * units + wq * a.Hq + kvh * a.G + hh;
+            sm_old[2 * threadIdx.x] = a.part_ml[pu * 2];
+            sm_old[2 * threadIdx.x + 1] = a.part_ml[pu * 2 + 1];
+        }
+        __syncthreads();
         for (uint32_t idx = threadIdx.x; idx < rows_here * 128; idx += blockDim.x) {
             const uint32_t r = idx >> 7, d = idx & 127;  // a wave's 64 threads share row r
             // all reads first, no branch between them: a wave with no visible
@@ -308,7 +321,13 @@ __global__ __launch_bounds__((64 * SplitCfg<NT, KT, VT>::waves), 1) void split_k
             const uint32_t rk = row0 + r;
             const uint32_t wq = rk / a.G, hh = rk - wq * a.G;
             const uint32_t unit = wq * a.Hq + kvh * a.G + hh;
-            const size_t pu = (size_t)split * units + unit;
+            const size_t pu = (size_t)pidx * units + unit;
+            if (accum) {
+                const PartCombine c = part_combine(sm_old[2 * r], sm_old[2 * r + 1], M, L);
+                A = (c.w0 > 0.f ? c.w0 * a.part_o[pu * 128 + d] : 0.f) + c.w1 * A;
+                M = c.m;
+                L = c.l;
+            }
             a.part_o[pu * 128 + d] = A;
             if (d == 0) {
                 a.part_ml[pu * 2] = M;

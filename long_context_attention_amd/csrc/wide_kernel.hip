@@ -181,9 +181,16 @@ __global__ __launch_bounds__((64 * WAVES), 1) void wide_kernel(const SplitArgs a
     const uint32_t rows_kv = a.W * a.G;
     const uint32_t n_chunks_all = (a.n_tokens + 31) >> 5;
     const uint32_t cpp = a.T >> 5;
+    // a split is a range of split_chunks chunks, or (page list) one page
     const uint32_t split = blockIdx.x;
-    const uint32_t c_begin = split * a.split_chunks;
-    const uint32_t c_end = min(c_begin + a.split_chunks, n_chunks_all);
+    uint32_t c_begin, c_end;
+    if (a.page_list) {
+        c_begin = table_at(a.page_list, a.list_offset + split) * cpp;
+        c_end = min(c_begin + cpp, n_chunks_all);
+    } else {
+        c_begin = split * a.split_chunks;
+        c_end = min(c_begin + a.split_chunks, n_chunks_all);
+    }
     const uint32_t n = c_end - c_begin;  // chunks of this split (>= 1)
     const uint32_t clean_end = (a.n_tokens - a.W + 1) >> 5;
     const bool active = wave_row0 < rows_kv;  // wave has rows to compute
@@ -282,8 +289,11 @@ __global__ __launch_bounds__((64 * WAVES), 1) void wide_kernel(const SplitArgs a
         }
     }
 
-    // ---- partials of this wave's rows
+    // ---- partials of this wave's rows (slot `split`; an accumulating slot
+    // combines with what it holds: the wave owns the row, so its reads of
+    // the stored values precede its writes)
     const uint32_t units = a.W * a.Hq;
+    const bool accum = split < a.accum_slots;
 #pragma unroll
     for (int t = 0; t < NT; t++) {
         float l = st[t].l_run;
@@ -294,11 +304,22 @@ __global__ __launch_bounds__((64 * WAVES), 1) void wide_kernel(const SplitArgs a
             const uint32_t w = r / a.G, hh = r - w * a.G;
             const uint32_t unit = w * a.Hq + kvh * a.G + hh;
             const size_t pu = (size_t)split * units + unit;
+            float m = st[t].m_ref;
+            if (accum) {
+                const PartCombine c = part_combine(a.part_ml[pu * 2], a.part_ml[pu * 2 + 1], m, l);
+#pragma unroll
+                for (int k = 0; k < 8; k++) {
+                    const floatx4 old = *reinterpret_cast<const floatx4 *>(a.part_o + pu * 128 + 16 * k + 4 * grp);
+                    st[t].acc[k] = (c.w0 > 0.f ? c.w0 * old : floatx4{0.f, 0.f, 0.f, 0.f}) + c.w1 * st[t].acc[k];
+                }
+                m = c.m;
+                l = c.l;
+            }
 #pragma unroll
             for (int k = 0; k < 8; k++)
                 *reinterpret_cast<floatx4 *>(a.part_o + pu * 128 + 16 * k + 4 * grp) = st[t].acc[k];
             if (grp == 0) {
-                a.part_ml[pu * 2] = st[t].m_ref;
+                a.part_ml[pu * 2] = m;
                 a.part_ml[pu * 2 + 1] = l;
             }
         }
