@@ -51,7 +51,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="decode-40k")
+    ap.add_argument("--workload", default="all",
+                    help="all (default): decode-40k as the headline, then verify-160k W=1-6, prefill-120k and "
+                         "stream-256k W=1 and 4 in the same run; or one workload")
     ap.add_argument("--width", type=int, default=0, help="query rows for verify / streamed workloads")
     ap.add_argument("--mode", choices=["graph", "eager"], default=None,
                     help="graph: replay a captured HIP graph of the 64-layer pass (resident workloads); "
@@ -389,7 +391,7 @@ def cpu_model():
 
 
 # --------------------------------------------------------------------------- cpu baseline
-def cpu_baseline(w, rows, kind, inputs, budget_s=10.0, types=KV_TYPES["q8_0-q4_0"]):
+def cpu_baseline(w, rows, kind, inputs, budget_s=10.0, types=KV_TYPES["q8_0-q4_0"], one_core=True):
     """The oracle (fp64 C, OpenMP over (row, head)) on a bounded sample of the
     same workload: whole layers (a seeded sample of rows for prefill) until
     about budget_s seconds of CPU work, scaled to tokens/s of the full
@@ -417,6 +419,12 @@ def cpu_baseline(w, rows, kind, inputs, budget_s=10.0, types=KV_TYPES["q8_0-q4_0
         layers += 1
     # full pass = n_layers layers x rows rows; sample = `layers` layers x len(sample_rows) rows
     pass_s = spent * (w.n_layers / layers) * rows / len(sample_rows)
+    out = {"value": rows / pass_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "cpu": {"model": cpu_model(), "logical_cpus": os.cpu_count()},
+           "sample": f"{layers} of {w.n_layers} layers of {w.name} ({w.n_tokens} keys, {w.n_q_heads} query heads, "
+                     f"{len(sample_rows)} of {rows} rows), {spent:.1f} s measured, scaled to the full pass"}
+    if not one_core:
+        return out
     # one core: the first sampled row of one layer (the oracle is linear in rows and layers)
     kvl = inputs.draw_layer(w.n_tokens, w.n_kv_heads, 0, w.wid, device="cuda", k_type=types[0], v_type=types[1])
     pages = kvl.pages.cpu().numpy()
@@ -428,51 +436,18 @@ def cpu_baseline(w, rows, kind, inputs, budget_s=10.0, types=KV_TYPES["q8_0-q4_0
                         v_type=types[1])
     one = time.perf_counter() - t0
     one_pass_s = one * w.n_layers * rows
-    return {"value": rows / pass_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "cpu": {"model": cpu_model(), "logical_cpus": os.cpu_count()},
-            "sample": f"{layers} of {w.n_layers} layers of {w.name} ({w.n_tokens} keys, {w.n_q_heads} query heads, "
-                      f"{len(sample_rows)} of {rows} rows), {spent:.1f} s measured, scaled to the full pass",
-            "one_core": {"value": rows / one_pass_s, "unit": "tokens/s",
-                         "sample": f"1 row of 1 layer, {one:.2f} s measured, scaled to the full pass"}}
+    out["one_core"] = {"value": rows / one_pass_s, "unit": "tokens/s",
+                       "sample": f"1 row of 1 layer, {one:.2f} s measured, scaled to the full pass"}
+    return out
 
 
-# --------------------------------------------------------------------------- main
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU: this path has no multi-GPU mode (asked for --gpus {args.gpus}). "
-              "Run with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
-    import torch
-
-    import inputs
-    import long_context_attention_amd as kv
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    if args.h2d_ceiling:
-        print(json.dumps({"h2d_ceiling": h2d_ceiling(torch)}), flush=True)
-        return
-    w = inputs.WORKLOADS[args.workload]
-    if args.hbm_ceiling:
-        layer_bytes = w.n_tokens * w.n_kv_heads * KV_TYPES[args.kv_types][3]
-        print(json.dumps({"workload": w.name, "hbm_read_ceiling": hbm_read_ceiling(layer_bytes)}), flush=True)
-        return
-    n_layers = args.layers or w.n_layers
-    streamed = w.resident_fraction < 1.0
-    mode = args.mode or ("eager" if streamed else "graph")
-    if streamed and mode == "graph":
-        print("streamed workloads run eagerly (the copy stream is driven by the host)", file=sys.stderr)
-        sys.exit(2)
-    log(f"bench: workload {w.name}, {n_layers} layers, mode {mode}: building inputs")
-    t0 = time.perf_counter()
-    types = KV_TYPES[args.kv_types]
-    default_types = args.kv_types == "q8_0-q4_0"
-    h, qs, outs, kind, rows, hist = build(w, args.width, n_layers, torch, kv, inputs, types, args.split_pages,
-                                          args.deterministic, args.chunk_slots)
-    log(f"bench: inputs ready in {time.perf_counter() - t0:.1f} s; {kind} rows={rows}")
+# --------------------------------------------------------------------------- timing
+def time_workload(h, qs, outs, kind, rows, w, n_layers, mode, steps, warmup, torch, streamed):
+    """Warm up, then time `steps` passes (HIP events on the compute stream
+    around them), then the same steps again with an event between steps for
+    the spread.  Returns (ms per pass, wall s, per-layer kernel ms, kernel
+    timing description, per-launch split / merge figures, step spread)."""
     stream = h.compute_stream
-
     graph = None
     if mode == "graph":
         with torch.cuda.stream(stream):
@@ -490,135 +465,203 @@ def main():
             one_pass(h, qs, outs, kind, rows)
 
     with torch.cuda.stream(stream):
-        for _ in range(args.warmup):
+        for _ in range(warmup):
             step()
     torch.cuda.synchronize()
-    log(f"bench: warmup {args.warmup} done; timing {args.steps} steps")
-
-    chunks = -(-(w.n_pages - w.n_resident) // (args.chunk_slots or 16)) if streamed else 0
-    launches_per_pass = n_layers * (chunks + 3)
+    chunks = -(-(w.n_pages - w.n_resident) // 16) if streamed else 0
     if graph is None:
-        h.profile(max(1, args.steps) * launches_per_pass)
+        h.profile(max(1, steps) * n_layers * (2 * chunks + 40))
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
         e0.record(stream)
         t_start = time.perf_counter()
-        for i in range(args.steps):
+        for _ in range(steps):
             step()
         e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     elapsed_ms = e0.elapsed_time(e1)
-    ms_per_step = elapsed_ms / args.steps
+    per_launch = None
     if graph is None:
-        kernel_timing = "per-launch HIP events on the compute stream during the timed steps"
+        timing = "per-launch HIP events on the compute stream during the timed steps"
         split_ms, n_split, merge_ms, n_merge = h.profile_read(reset=True)
         h.profile(0)
         layer_ms = split_ms + merge_ms
+        if n_split:
+            per_launch = {"split_mean": round(split_ms / n_split, 5), "split_launches": n_split,
+                          "merge_mean": round(merge_ms / max(n_merge, 1), 5), "merge_launches": n_merge}
     else:
-        # a resident layer is the split kernel then its merge kernel, back to
-        # back in the graph; HIP events around the timed replays give their
+        # a resident layer is the attention kernel then its merge kernel, back
+        # to back in the graph; HIP events around the timed replays give their
         # mean per layer (gaps included)
-        kernel_timing = ("HIP events on the compute stream around the timed graph replays, per layer "
-                         "(split kernel + merge kernel)")
-        split_ms, n_split, merge_ms, n_merge = 0.0, 0, 0.0, 0
+        timing = ("HIP events on the compute stream around the timed graph replays, per layer "
+                  "(attention kernel + merge kernel)")
         layer_ms = elapsed_ms
-    n_layer_calls = args.steps * n_layers
-
-    # spread: the same K steps again, one event between steps (outside the
-    # timed region above, whose figures stand alone)
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     with torch.cuda.stream(stream):
         marks[0].record(stream)
-        for i in range(args.steps):
+        for i in range(steps):
             step()
             marks[i + 1].record(stream)
     torch.cuda.synchronize()
-    step_ms = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
+    step_ms = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(steps)])
+    spread = {"median": round(float(np.median(step_ms)), 4), "p10": round(float(np.percentile(step_ms, 10)), 4),
+              "p90": round(float(np.percentile(step_ms, 90)), 4),
+              "how": "a second run of the same steps with an event between steps"}
+    return elapsed_ms / steps, wall, layer_ms / (steps * n_layers), timing, per_launch, spread
 
-    adaptive = None
-    if args.adaptive and streamed:
-        adaptive = adaptive_run(h, w, hist, qs, outs, kind, rows, n_layers, max(2, min(args.steps, 5)), torch, kv)
 
-    writer = None
-    if args.writer and kind != "prefill" and not streamed:
-        writer = time_writer(h, w, rows, n_layers, args.steps, torch, inputs, stream, types[3])
-
-    # ---- figures
-    tokens_per_step = rows
-    value = tokens_per_step / (ms_per_step / 1e3)
-    keys_per_layer = w.n_tokens  # every key of the history is read once per layer (all rows share it)
-    kv_bytes_layer = keys_per_layer * w.n_kv_heads * types[3]
-    kv_gbps = kv_bytes_layer * n_layers / (ms_per_step / 1e3) / 1e9
+def figures(w, rows, kind, n_layers, ms_per_step, layer_ms, types, streamed, ceiling=None):
+    """Throughput and the roofline of the dominant kernel for one measured
+    workload and width."""
+    value = rows / (ms_per_step / 1e3)
+    kv_bytes_layer = w.n_tokens * w.n_kv_heads * types[3]   # every key of the history, read once per layer
     flops_layer = 4.0 * w.n_q_heads * 128 * sum(w.n_tokens - rows + r + 1 for r in range(rows))
-    result = {
-        "metric": METRIC,
-        "value": round(value, 3),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f16",
-        "data": "synthetic",
-        "config": {"workload": w.name, "layers": n_layers, "context": w.n_tokens, "page_tokens": 256,
-                   "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": 128, "rows": rows,
-                   "kv_types": types[2], "mode": mode, "split_pages": args.split_pages or "auto",
-                   "chunk_order": "static" if args.deterministic else "claimed in splits of >= 96 chunks, else static",
-                   "resident_fraction": w.resident_fraction, "ring_slots": w.ring_slots,
-                   "chunk_slots": (args.chunk_slots or 16) if streamed else None},
-        "gpu": gpu_info(torch),
-        "layers_per_s": round(n_layers / (ms_per_step / 1e3), 1),
-        "kv_gbps": round(kv_gbps, 1),
-        "kv_frac_hbm_peak": round(kv_gbps / HBM_PEAK_GBPS, 4),
-        "wall_s": round(wall, 3),
-        "step_ms_spread": {"median": round(float(np.median(step_ms)), 4),
-                           "p10": round(float(np.percentile(step_ms, 10)), 4),
-                           "p90": round(float(np.percentile(step_ms, 90)), 4),
-                           "how": "a second run of the same steps with an event between steps"},
-    }
+    kv_gbps = kv_bytes_layer * n_layers / (ms_per_step / 1e3) / 1e9
+    out = {"value": round(value, 3), "unit": "tokens/s", "ms_per_step": round(ms_per_step, 4),
+           "layers_per_s": round(n_layers / (ms_per_step / 1e3), 1), "kv_gbps": round(kv_gbps, 1),
+           "kv_frac_hbm_peak": round(kv_gbps / HBM_PEAK_GBPS, 4),
+           "algorithmic": {"kv_bytes_per_layer": kv_bytes_layer, "flops_per_layer": flops_layer}}
+    default_types = types[0] == 8 and types[1] == 2
     if streamed:
         n_str = w.n_pages - w.n_resident
         h2d = n_str * 256 * w.n_kv_heads * types[3] * n_layers / (ms_per_step / 1e3) / 1e9
-        result["h2d_gbps"] = round(h2d, 2)
-    if streamed:
-        # the pass is bound by the host link: report it against the measured ceiling
-        ceiling = h2d_ceiling(torch)
-        result["h2d_ceiling"] = ceiling
+        out["h2d_gbps"] = round(h2d, 2)
         c = ceiling["contiguous_gbps"]
-        result["roofline"] = {"bound": "host-link", "achieved": result["h2d_gbps"], "peak": c, "unit": "GB/s",
-                              "frac": round(result["h2d_gbps"] / c, 4), "traffic": None}
-    if not streamed:
-        # the split kernel and its merge read the layer's quantised K/V once
-        achieved = kv_bytes_layer * n_layer_calls / (layer_ms / 1e3) / 1e9
-        if kind == "prefill":
-            tflops = flops_layer * n_layer_calls / (layer_ms / 1e3) / 1e12
-            result["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
-                                  "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
-                                  "traffic": None}
-            result["kv_gbps_kernels"] = round(achieved, 1)
-        else:
-            result["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                                  "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                                  "traffic": measured_traffic(w.name, rows) if default_types else None}
-            # the contraction runs on the matrix cores at every width: its rate
-            tflops = flops_layer * n_layer_calls / (layer_ms / 1e3) / 1e12
-            result["mfma_tflops"] = round(tflops, 2)
-            result["mfma_frac"] = round(tflops / MFMA_F16_PEAK_TFLOPS, 4)
-        result["kernel_ms"] = {"layer_mean": round(layer_ms / n_layer_calls, 5), "timing": kernel_timing}
-        if n_split:
-            result["kernel_ms"].update({"split_mean": round(split_ms / n_split, 5), "split_launches": n_split,
-                                        "merge_mean": round(merge_ms / max(n_merge, 1), 5),
-                                        "merge_launches": n_merge})
-    if writer is not None:
-        result["writer"] = writer
-    if adaptive is not None:
-        result["adaptive"] = adaptive
+        # the pass is bound by the host link: streamed bytes against the measured ceiling
+        out["roofline"] = {"bound": "host-link", "achieved": out["h2d_gbps"], "peak": c, "unit": "GB/s",
+                           "frac": round(out["h2d_gbps"] / c, 4), "traffic": None}
+        return out
+    achieved = kv_bytes_layer / (layer_ms / 1e3) / 1e9
+    tflops = flops_layer / (layer_ms / 1e3) / 1e12
+    traffic = measured_traffic(w.name, rows) if default_types else None
+    if kind == "prefill":
+        out["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": traffic}
+        out["kv_gbps_kernels"] = round(achieved, 1)
+    else:
+        out["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                           "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic}
+        # the contraction runs on the matrix cores at every width: its rate
+        out["mfma_tflops"] = round(tflops, 2)
+        out["mfma_frac"] = round(tflops / MFMA_F16_PEAK_TFLOPS, 4)
+    return out
+
+
+def measure(w, widths, args, torch, kv, inputs, types, steps, warmup, cpu_budget, ceiling=None, extras=False):
+    """Build one workload, then time it at each width (sharing the pages);
+    returns {width: result}."""
+    n_layers = args.layers or w.n_layers
+    streamed = w.resident_fraction < 1.0
+    mode = args.mode or ("eager" if streamed else "graph")
+    if streamed and mode == "graph":
+        raise SystemExit("streamed workloads run eagerly (the copy stream is driven by the host)")
+    log(f"bench: workload {w.name}, {n_layers} layers, mode {mode}, widths {widths}: building inputs")
+    t0 = time.perf_counter()
+    h, qs, outs, kind, rows, hist = build(w, max(widths), n_layers, torch, kv, inputs, types, args.split_pages,
+                                          args.deterministic, args.chunk_slots)
+    log(f"bench: inputs ready in {time.perf_counter() - t0:.1f} s")
+    results = {}
+    for W in widths:
+        if W != rows:
+            qs = [inputs.draw_queries(W, w.n_q_heads, l, w.wid, device="cuda") for l in range(n_layers)]
+            outs = [torch.empty_like(q) for q in qs]
+            rows = W
+        k = "prefill" if kind == "prefill" else ("decode" if W == 1 else "verify")
+        log(f"bench: {w.name} {k} rows={W}: warmup {warmup}, timing {steps} steps")
+        ms, wall, layer_ms, timing, per_launch, spread = time_workload(h, qs, outs, k, W, w, n_layers, mode, steps,
+                                                                       warmup, torch, streamed)
+        r = figures(w, W, k, n_layers, ms, layer_ms, types, streamed, ceiling)
+        r["config"] = {"workload": w.name, "layers": n_layers, "context": w.n_tokens, "page_tokens": 256,
+                       "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": 128, "rows": W,
+                       "kv_types": types[2], "mode": mode, "split_pages": args.split_pages or "auto",
+                       "chunk_order": "static" if args.deterministic else
+                       "claimed in splits of >= 96 chunks, else static",
+                       "resident_fraction": w.resident_fraction, "ring_slots": w.ring_slots,
+                       "chunk_slots": (args.chunk_slots or 16) if streamed else None}
+        r["steps"], r["warmup"], r["wall_s"], r["step_ms_spread"] = steps, warmup, round(wall, 3), spread
+        if not streamed:
+            r["kernel_ms"] = {"layer_mean": round(layer_ms, 5), "timing": timing}
+            if per_launch:
+                r["kernel_ms"].update(per_launch)
+        if extras and args.adaptive and streamed:
+            r["adaptive"] = adaptive_run(h, w, hist, qs, outs, k, W, n_layers, max(2, min(steps, 5)), torch, kv)
+        if extras and args.writer and k != "prefill" and not streamed:
+            r["writer"] = time_writer(h, w, W, n_layers, steps, torch, inputs, h.compute_stream, types[3])
+        if cpu_budget > 0:
+            log(f"bench: timing the oracle on a CPU sample ({w.name}, rows={W})")
+            r["cpu_baseline"] = cpu_baseline(w, W, k, inputs, budget_s=cpu_budget, types=types, one_core=extras)
+        results[W] = r
+    h.destroy()
+    del h, qs, outs, hist
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return results
+
+
+# --------------------------------------------------------------------------- main
+CONTRACT_KEYS = ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better", "scaling",
+                 "vs_baseline", "dtype", "data", "config")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this path has no multi-GPU mode (asked for --gpus {args.gpus}). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import inputs
+    import long_context_attention_amd as kv
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.h2d_ceiling:
+        print(json.dumps({"h2d_ceiling": h2d_ceiling(torch)}), flush=True)
+        return
+    types = KV_TYPES[args.kv_types]
+    every = args.workload == "all"
+    w = inputs.WORKLOADS["decode-40k" if every else args.workload]
+    if args.hbm_ceiling:
+        layer_bytes = w.n_tokens * w.n_kv_heads * types[3]
+        print(json.dumps({"workload": w.name, "hbm_read_ceiling": hbm_read_ceiling(layer_bytes)}), flush=True)
+        return
+    budget = 0.0 if args.no_cpu_baseline else 10.0
+    streamed = w.resident_fraction < 1.0
+    ceiling = h2d_ceiling(torch) if streamed else None
+    width = args.width or (w.widths[-1] if w.prefill_rows else (w.widths[0] if not streamed else 1))
+    head = measure(w, [width], args, torch, kv, inputs, types, args.steps, args.warmup, budget, ceiling,
+                   extras=True)[width]
+    result = {"metric": METRIC, "value": head["value"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+              "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+              "vs_baseline": None, "dtype": "f16", "data": "synthetic", "config": head["config"],
+              "gpu": gpu_info(torch)}
+    result.update({k: v for k, v in head.items() if k not in CONTRACT_KEYS})
+    if ceiling is not None:
+        result["h2d_ceiling"] = ceiling
+    if every:
+        # the other workloads of the same metric, each at its widths, in the
+        # same run: their own throughput, roofline and oracle baseline
+        # (smaller CPU samples)
+        configs = {}
+        cb = 0.0 if args.no_cpu_baseline else 3.0
+        for W, r in measure(inputs.WORKLOADS["verify-160k"], [1, 2, 3, 4, 5, 6], args, torch, kv, inputs, types,
+                            args.steps, args.warmup, cb).items():
+            configs[f"verify-160k W={W}"] = r
+        pf = inputs.WORKLOADS["prefill-120k"]
+        for W, r in measure(pf, [pf.prefill_rows], args, torch, kv, inputs, types, args.steps, args.warmup,
+                            cb).items():
+            configs[f"prefill-120k R={W}"] = r
+        sw = inputs.WORKLOADS["stream-256k"]
+        ceil = h2d_ceiling(torch)
+        result["h2d_ceiling"] = ceil
+        s_steps = max(1, min(args.steps, 3))
+        for W, r in measure(sw, [1, 4], args, torch, kv, inputs, types, s_steps, 1, cb, ceil).items():
+            configs[f"stream-256k W={W}"] = r
+        result["configs"] = configs
     if args.with_copy_kernel:
         a = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device="cuda")
         b = torch.empty_like(a)
@@ -626,10 +669,6 @@ def main():
             torch.neg(a, out=b)
         torch.cuda.synchronize()
         result["copy_kernel_bytes"] = {"read": a.numel() * 4, "write": b.numel() * 4}
-    if not args.no_cpu_baseline:
-        log("bench: timing the oracle on a CPU sample")
-        result["cpu_baseline"] = cpu_baseline(w, rows, kind, inputs, types=types)
-    h.destroy()
     print(json.dumps(result), flush=True)
 
 

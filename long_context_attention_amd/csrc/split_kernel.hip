@@ -39,8 +39,10 @@ struct SplitCfg {
 
 // STREAM: chunk loads carry the non-temporal hint (each chunk is read by one
 // workgroup); calls of several row blocks, whose blocks read the same chunks,
-// load without it.
-template <int NT, int KT, int VT, bool STREAM>
+// load without it.  COUNT: the test instantiation that counts softmax
+// re-reference events (SplitArgs::rescale_count); the others carry no trace
+// of the counter.
+template <int NT, int KT, int VT, bool STREAM, bool COUNT>
 __global__ __launch_bounds__((64 * SplitCfg<NT, KT, VT>::waves), 1) void split_kernel(const SplitArgs a) {
     using C = Chunk<KT, VT>;
     constexpr int kSplitWaves = SplitCfg<NT, KT, VT>::waves;
@@ -240,7 +242,7 @@ __global__ __launch_bounds__((64 * SplitCfg<NT, KT, VT>::waves), 1) void split_k
                 read_vscales<KT, VT>(stg, grp, vd);
             }
 #pragma unroll
-            for (int t = 0; t < NT; t++) chunk_probs<VT>(st[t], s[t], vd, pv_pf[t], a.rescale_count);
+            for (int t = 0; t < NT; t++) chunk_probs<VT>(st[t], s[t], vd, pv_pf[t], COUNT ? a.rescale_count : nullptr);
             read_vcodes<KT, VT>(stg, lane, pv_vq);
             if constexpr (!C::vblk)
                 if (tail) clear_padding_vcodes<KT, VT>(pv_vq, grp, a.n_tokens - 32 * c);
@@ -476,20 +478,28 @@ namespace {
 
 // Calls f(kernel, waves, lds bytes) with the split kernel of row tiles rt and
 // the element-type pair (without the non-temporal hint when `blocks`: several
-// row blocks, which have two row tiles); false for an unsupported pair.
+// row blocks, which have two row tiles; the counting instantiation when
+// `count`); false for an unsupported pair.
 template <class F>
-bool with_split_kernel(int rt, uint32_t kt, uint32_t vt, bool blocks, F f) {
+bool with_split_kernel(int rt, uint32_t kt, uint32_t vt, bool blocks, bool count, F f) {
     using namespace kvattn_dev;
     auto pick = [&](auto nt, auto ktc, auto vtc) {
         constexpr int NT = decltype(nt)::value, KT = decltype(ktc)::value, VT = decltype(vtc)::value;
         using Cfg = SplitCfg<NT, KT, VT>;
+        const uint32_t lds = (uint32_t)Cfg::lds_bytes;
         if constexpr (NT == 2) {
             if (blocks) {
-                f(&split_kernel<NT, KT, VT, false>, Cfg::waves, (uint32_t)Cfg::lds_bytes);
+                if (count)
+                    f(&split_kernel<NT, KT, VT, false, true>, Cfg::waves, lds);
+                else
+                    f(&split_kernel<NT, KT, VT, false, false>, Cfg::waves, lds);
                 return true;
             }
         }
-        f(&split_kernel<NT, KT, VT, true>, Cfg::waves, (uint32_t)Cfg::lds_bytes);
+        if (count)
+            f(&split_kernel<NT, KT, VT, true, true>, Cfg::waves, lds);
+        else
+            f(&split_kernel<NT, KT, VT, true, false>, Cfg::waves, lds);
         return true;
     };
     using I1 = std::integral_constant<int, 1>;
@@ -508,7 +518,7 @@ bool with_split_kernel(int rt, uint32_t kt, uint32_t vt, bool blocks, F f) {
 
 size_t kvattn_split_smem_bytes(int rt, uint32_t k_type, uint32_t v_type) {
     size_t bytes = 0;
-    with_split_kernel(rt, k_type, v_type, false, [&](auto, int, uint32_t lds) { bytes = lds; });
+    with_split_kernel(rt, k_type, v_type, false, false, [&](auto, int, uint32_t lds) { bytes = lds; });
     return bytes;
 }
 
@@ -523,11 +533,12 @@ hipError_t kvattn_split_setup() {
     for (const auto &pr : pairs)
         for (int rt = 1; rt <= 2; rt++)
             for (int blocks = 0; blocks <= 1; blocks++)
-                with_split_kernel(rt, pr[0], pr[1], blocks != 0, [&](auto kern, int, uint32_t lds) {
-                    if (err == hipSuccess)
-                        err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-                });
+                for (int count = 0; count <= 1; count++)
+                    with_split_kernel(rt, pr[0], pr[1], blocks != 0, count != 0, [&](auto kern, int, uint32_t lds) {
+                        if (err == hipSuccess)
+                            err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                    });
     return err;
 }
 
@@ -538,7 +549,8 @@ hipError_t kvattn_launch_split(const SplitArgs &a, uint32_t n_items, uint32_t n_
                                hipEvent_t ev_start, hipEvent_t ev_stop) {
     (void)hipGetLastError();  // clear a stale error so the check below reports this launch
     const dim3 grid(a.Hkv, n_items, n_row_blocks);  // n_items <= 4096 pages
-    const bool ok = with_split_kernel(rt, a.k_type, a.v_type, n_row_blocks > 1, [&](auto kern, int waves, uint32_t lds) {
+    const bool ok = with_split_kernel(rt, a.k_type, a.v_type, n_row_blocks > 1, a.rescale_count != nullptr,
+                                      [&](auto kern, int waves, uint32_t lds) {
         if (ev_start)
             hipExtLaunchKernelGGL(kern, grid, dim3(64 * waves), lds, s, ev_start, ev_stop, 0, a);
         else

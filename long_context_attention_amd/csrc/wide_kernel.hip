@@ -1,5 +1,7 @@
 // wide_kernel.hip -- the kernel for calls with more than 96 rows per KV head
 // (prefill chunks, wide verify).
+#include <type_traits>
+
 #include "kernels_common.h"
 
 namespace kvattn_dev {
@@ -160,7 +162,8 @@ __device__ __forceinline__ void dequant_view(const uint8_t *raw, uint8_t *view, 
     }
 }
 
-template <int KT, int VT, int WAVES>
+// COUNT: the test instantiation that counts softmax re-reference events.
+template <int KT, int VT, int WAVES, bool COUNT>
 __global__ __launch_bounds__((64 * WAVES), 1) void wide_kernel(const SplitArgs a) {
     using C = Chunk<KT, VT>;
     constexpr int NT = 2;
@@ -269,7 +272,7 @@ __global__ __launch_bounds__((64 * WAVES), 1) void wide_kernel(const SplitArgs a
         view_scores<NT>(st, view, lane, s);
         if (c >= clean_end) mask_scores<NT>(st, 32 * c, grp, s);
 #pragma unroll
-        for (int t = 0; t < NT; t++) view_probs(st[t], s[t], pf[t], a.rescale_count);
+        for (int t = 0; t < NT; t++) view_probs(st[t], s[t], pf[t], COUNT ? a.rescale_count : nullptr);
         view_pv<NT>(st, view, lane, pf);
     };
     // step of two chunks: p and p + 1 are computed from their views while
@@ -343,20 +346,25 @@ hipError_t kvattn_launch_wide(const SplitArgs &a, uint32_t n_splits, uint32_t n_
         else
             hipLaunchKernelGGL(kern, grid, block, 0, s, a);
     };
-    auto pick = [&](auto kern8, auto kern12) {
+    const bool count = a.rescale_count != nullptr;
+    auto pick = [&](auto ktc, auto vtc) {
+        constexpr int KT = decltype(ktc)::value, VT = decltype(vtc)::value;
         if (waves == 8)
-            go(kern8);
+            count ? go(wide_kernel<KT, VT, 8, true>) : go(wide_kernel<KT, VT, 8, false>);
         else
-            go(kern12);
+            count ? go(wide_kernel<KT, VT, 12, true>) : go(wide_kernel<KT, VT, 12, false>);
     };
+    using F16 = std::integral_constant<int, kTypeF16>;
+    using Q4 = std::integral_constant<int, kTypeQ4_0>;
+    using Q8 = std::integral_constant<int, kTypeQ8_0>;
     if (a.k_type == kTypeQ8_0 && a.v_type == kTypeQ4_0)
-        pick(wide_kernel<kTypeQ8_0, kTypeQ4_0, 8>, wide_kernel<kTypeQ8_0, kTypeQ4_0, 12>);
+        pick(Q8{}, Q4{});
     else if (a.k_type == kTypeQ8_0 && a.v_type == kTypeQ8_0)
-        pick(wide_kernel<kTypeQ8_0, kTypeQ8_0, 8>, wide_kernel<kTypeQ8_0, kTypeQ8_0, 12>);
+        pick(Q8{}, Q8{});
     else if (a.k_type == kTypeQ4_0 && a.v_type == kTypeQ4_0)
-        pick(wide_kernel<kTypeQ4_0, kTypeQ4_0, 8>, wide_kernel<kTypeQ4_0, kTypeQ4_0, 12>);
+        pick(Q4{}, Q4{});
     else if (a.k_type == kTypeF16 && a.v_type == kTypeF16)
-        pick(wide_kernel<kTypeF16, kTypeF16, 8>, wide_kernel<kTypeF16, kTypeF16, 12>);
+        pick(F16{}, F16{});
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

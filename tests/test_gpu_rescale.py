@@ -22,9 +22,11 @@ wide kernel (c * d) is exact as well.  What remains is binary16 rounding on
 the value side (P * d_V or V' and P), relative 2^-12 of |V|, and fp32
 accumulation.
 
-Each case also reads the kernels' re-reference counter (a test aid of the
-C ABI) and requires the branch to have run.  Every output element is
-compared with the fp64 oracle reading the same page bytes.
+Each case runs twice: through the kernels' counting instantiation, whose
+re-reference counter (a test aid of the C ABI) must show the branch ran, and
+through the production instantiation (the same arithmetic without the
+counter).  Every output element of both is compared with the fp64 oracle
+reading the same page bytes.
 """
 import math
 
@@ -152,9 +154,12 @@ def dominant_case(N, Hq, Hkv, W, k_type, v_type, seed):
     return layer, on_f16_grid(h)
 
 
-def run_counted(h, q, W, kind, layer=0):
+def run_call(h, q, W, kind, counted, layer=0):
+    """One call; counted: through the kernels' counting instantiation (the
+    counter is read back), else the production one."""
     counter = torch.zeros(1, dtype=torch.int32, device="cuda")
-    h.count_rescales(counter)
+    if counted:
+        h.count_rescales(counter)
     qd = q.to("cuda").contiguous()
     out = torch.full_like(qd, float("nan"))
     if kind == "prefill":
@@ -167,13 +172,19 @@ def run_counted(h, q, W, kind, layer=0):
 
 
 def check(h, layer, q, W, kind, Hq, Hkv, what, page_tokens=256):
-    got, events = run_counted(h, q, W, kind)
+    """The counting instantiation shows the branch ran; both it and the
+    production instantiation (same arithmetic) must match the oracle."""
+    got, events = run_call(h, q, W, kind, True)
+    plain, none = run_call(h, q, W, kind, False)
     ref = oracle_out(layer, q, Hq, Hkv, page_tokens=page_tokens)
     err = float(np.max(np.abs(got - ref)))
-    say(f"  {what}: max-abs err {err:.3e}, re-reference events {events}")
-    assert np.isfinite(got).all()
+    err_plain = float(np.max(np.abs(plain - ref)))
+    say(f"  {what}: max-abs err {err:.3e} (production kernels {err_plain:.3e}, bitwise equal "
+        f"{np.array_equal(got, plain)}), re-reference events {events}")
+    assert np.isfinite(got).all() and np.isfinite(plain).all()
     assert events > 0, "the inputs did not reach the re-reference branch"
-    assert err <= TOL
+    assert none == 0
+    assert err <= TOL and err_plain <= TOL
     return events
 
 
