@@ -761,6 +761,8 @@ int kvattn_create(const kvattn_params *params, void *d_pool, size_t pool_bytes, 
     if (e == hipSuccess) e = kvattn_split_setup();
     if (e != hipSuccess) {
         int code = fail(nullptr, KVATTN_E_HIP, "device / event setup failed: %s", hipGetErrorString(e));
+        if (h->upload_done) (void)hipEventDestroy(h->upload_done);
+        if (h->compute_mark) (void)hipEventDestroy(h->compute_mark);
         delete h;
         return code;
     }
