@@ -82,6 +82,10 @@ def parse():
                          "per layer (64 buffers, libkvattn_probe) and print it as JSON")
     ap.add_argument("--h2d-ceiling", action="store_true",
                     help="only measure the host-to-device ceiling (pinned copies) and print it as JSON")
+    ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: turn the counter collections of a --with-copy-kernel run of --workload / "
+                         "--width (rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE) into "
+                         "profiles/traffic_<workload>_w<rows>.txt, the per-layer HBM traffic the roofline reports")
     return ap.parse_args()
 
 
@@ -166,6 +170,60 @@ def measured_traffic(workload, rows):
     if rec.get("kernel_source_sha256") != sha:
         return None
     return rec.get("traffic_bytes_per_layer")
+
+
+TRAFFIC_SOURCES = ["kernels_common.h", "split_kernel.hip", "wide_kernel.hip"]
+
+
+def traffic_record(fetch_csv, write_csv, workload, rows, cmd_fetch, cmd_write):
+    """Per-dispatch means of FETCH_SIZE / WRITE_SIZE (KiB) for the attention
+    kernel (split or wide) and the merge of each layer call, each scaled by
+    the same counter's reading for the reference copy (torch.neg over 256 MiB:
+    reads 256 MiB, writes 256 MiB) in the same run; the record names the kernel
+    sources and their hash, and the roofline uses it only while they match."""
+    import csv
+    import hashlib
+
+    def means(path, counter):
+        acc = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                k = r["Kernel_Name"]
+                kind = ("attention" if ("split_kernel" in k or "wide_kernel" in k) else
+                        "merge" if "merge" in k else "copy_ref" if "neg_kernel" in k else None)
+                if kind:
+                    acc.setdefault(kind, []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
+
+    f, nf = means(fetch_csv, "FETCH_SIZE")
+    w, _ = means(write_csv, "WRITE_SIZE")
+    ref_kib = 256 * 1024
+    fs, ws = ref_kib / f["copy_ref"], ref_kib / w["copy_ref"]
+    att = (f["attention"] * fs + w["attention"] * ws) * 1024
+    mer = (f.get("merge", 0.0) * fs + w.get("merge", 0.0) * ws) * 1024
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "long_context_attention_amd", "csrc")
+    for name in TRAFFIC_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as fh:
+            h.update(fh.read())
+    import inputs
+    wl = inputs.WORKLOADS[workload]
+    return {"workload": workload, "rows": rows, "kernels": ["attention (split or wide kernel)", "merge"],
+            "kernel_sources": TRAFFIC_SOURCES, "kernel_source_sha256": h.hexdigest(),
+            "dispatches": nf,
+            "fetch_size_kib": {k: round(v, 1) for k, v in f.items()},
+            "write_size_kib": {k: round(v, 1) for k, v in w.items()},
+            "scale": {"fetch": round(fs, 4), "write": round(ws, 4)},
+            "traffic_bytes_per_layer": round(att + mer), "attention_bytes": round(att), "merge_bytes": round(mer),
+            "algorithmic_bytes_per_layer": wl.n_tokens * wl.n_kv_heads * BYTES_PER_TOKEN_HEAD,
+            "commands": {"fetch": cmd_fetch, "write": cmd_write},
+            "method": "FETCH_SIZE and WRITE_SIZE in KiB per dispatch, averaged over the attention and merge "
+                      "dispatches of the eager passes; each scaled by the reading of the same counter for "
+                      "torch.neg over a 256 MiB float32 tensor (reads 256 MiB, writes 256 MiB) run three times in "
+                      "the same process: fetch scale = 262144 / fetch_kib(copy), write scale = 262144 / "
+                      "write_kib(copy).  The record holds for kernel sources whose concatenated sha256 matches."}
 
 
 # --------------------------------------------------------------------------- KV writer
@@ -608,6 +666,23 @@ CONTRACT_KEYS = ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per
 
 def main():
     args = parse()
+    if args.traffic_record:
+        wl = "decode-40k" if args.workload == "all" else args.workload
+        import inputs
+        w = inputs.WORKLOADS[wl]
+        rows = args.width or (w.prefill_rows or w.widths[0])
+        base = (f"python -u <repo>/bench.py --workload {wl} --width {rows} --mode eager --steps 2 --warmup 1 "
+                "--no-cpu-baseline --with-copy-kernel" + (f" --layers {args.layers}" if args.layers else ""))
+        cmd = "cd /tmp && timeout -s KILL 300 rocprofv3 --pmc {c} -f csv -d <out>/{d} -o {d} -- " + base
+        rec = traffic_record(args.traffic_record[0], args.traffic_record[1], wl, rows,
+                             cmd.format(c="FETCH_SIZE", d="fetch"), cmd.format(c="WRITE_SIZE", d="write"))
+        path = os.path.join(ROOT, "profiles", f"traffic_{wl}_w{rows}.txt")
+        with open(path, "w") as fh:
+            json.dump(rec, fh, indent=1)
+            fh.write("\n")
+        print(json.dumps({"traffic_record": path, "traffic_bytes_per_layer": rec["traffic_bytes_per_layer"],
+                          "algorithmic_bytes_per_layer": rec["algorithmic_bytes_per_layer"]}))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this path has no multi-GPU mode (asked for --gpus {args.gpus}). "
               "Run with --gpus 1.", file=sys.stderr)
