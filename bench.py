@@ -2,11 +2,16 @@
 """Benchmark of paged Q8_0-K / Q4_0-V attention on one MI355X.
 
 A step is one pass of the hot path over one batch: every layer of the
-workload attends once (64 layers).  Default workload: all-resident TG1 decode,
-40,960-token history (160 pages of 256 tokens) per layer, 40 query heads over
-8 KV heads, head_dim 128, 64 layers with their own seeded N(0,1) data, pages
-scattered over the pool by a seeded permutation.  Inputs are resident in HBM
-before timing starts.
+workload attends once (64 layers).  Headline workload: all-resident TG1
+decode, 40,960-token history (160 pages of 256 tokens) per layer, 40 query
+heads over 8 KV heads, head_dim 128, 64 layers with their own seeded N(0,1)
+data, pages scattered over the pool by a seeded permutation.  Inputs are
+resident in HBM before timing starts.  The default run (`--workload all`)
+then measures, in the same process and JSON line under "configs", the
+163,840-token verify workload at widths 1-6, the 256-row prefill chunk over
+a 122,880-token prefix, and the 262,144-token streamed workload (40 % of the
+pages resident, the rest streamed from pinned host memory) at widths 1 and 4
+against the host-link ceiling measured in the same run.
 
 Prints one JSON line: throughput (tokens/s = query rows per pass x passes/s),
 the roofline of the dominant kernel (the split-KV attention kernel with its
@@ -17,7 +22,7 @@ committed counter summary matches the kernel source), and the fp64 CPU
 oracle timed on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
-                       [--workload decode-40k|verify-160k|stream-256k|prefill-120k]
+                       [--workload all|decode-40k|verify-160k|stream-256k|prefill-120k]
                        [--width W] [--mode graph|eager] [--no-cpu-baseline]
 """
 from __future__ import annotations
