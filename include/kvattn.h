@@ -136,7 +136,8 @@ typedef struct kvattn_params {
  * supported K/V pairs, and a port advertises only real support). */
 int kvattn_supported(uint32_t k_type, uint32_t v_type, uint32_t head_dim);
 
-/* Bytes of one page (0 if the parameters are invalid), computed from the
+/* Bytes of one page (0 if the parameters are invalid; the reason is then in
+ * kvattn_global_error()), computed from the
  * actual K and V types and the geometry ("troed's fork ...", section
  * "Backend-neutral memory and streaming contracts": page offsets follow the
  * quant types; section "KV data movement and attention": 256-position
@@ -144,7 +145,7 @@ int kvattn_supported(uint32_t k_type, uint32_t v_type, uint32_t head_dim);
 size_t kvattn_page_bytes(const kvattn_params *params);
 
 /* Bytes the caller must provide as d_workspace (0 if the parameters are
- * invalid): device page tables, page lists, one staging page and the split
+ * invalid, the reason in kvattn_global_error()): device page tables, page lists, one staging page and the split
  * partials (m, l, acc[128] per split, row and query head, fp32).  The
  * attention operations expose their workspace size beside the span call so
  * the caller can budget it ("troed's fork ...", section "Backend-neutral
@@ -490,7 +491,8 @@ int kvattn_destroy(kvattn_t h);
 const char *kvattn_last_error(kvattn_t h);
 
 /* Message of the last failure of a call that had no handle to report on
- * (kvattn_create).  Thread-local. */
+ * (kvattn_create, the sizing calls, kvattn_validate_page_table,
+ * kvattn_sched_simulate, kvattn_policy_step).  Thread-local. */
 const char *kvattn_global_error(void);
 
 #ifdef __cplusplus

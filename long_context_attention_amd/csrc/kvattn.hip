@@ -695,17 +695,31 @@ int kvattn_supported(uint32_t k_type, uint32_t v_type, uint32_t head_dim) {
     return pair_supported(k_type, v_type) && head_dim == kHeadDim;
 }
 
+// Parameters of the sizing calls, or false with the reason in the thread's
+// global error message.
+static bool sizing_params(const kvattn_params *params, kvattn_params *p) {
+    if (!read_params(params, p)) {
+        fail(nullptr, KVATTN_E_ARG, "null params or struct_size too small");
+        return false;
+    }
+    std::string why;
+    const int rc = check_params(*p, why);
+    if (rc != KVATTN_OK) {
+        fail(nullptr, rc, "%s", why.c_str());
+        return false;
+    }
+    return true;
+}
+
 size_t kvattn_page_bytes(const kvattn_params *params) {
     kvattn_params p;
-    std::string why;
-    if (!read_params(params, &p) || check_params(p, why) != KVATTN_OK) return 0;
+    if (!sizing_params(params, &p)) return 0;
     return page_layout(p).page_bytes;
 }
 
 size_t kvattn_workspace_bytes(const kvattn_params *params) {
     kvattn_params p;
-    std::string why;
-    if (!read_params(params, &p) || check_params(p, why) != KVATTN_OK) return 0;
+    if (!sizing_params(params, &p)) return 0;
     return workspace_layout(p).total;
 }
 
@@ -1242,19 +1256,22 @@ int kvattn_validate_page_table(const kvattn_params *params, const uint32_t *page
  * layer, first, count, ordinal base, event, wait event. */
 int kvattn_sched_simulate(uint32_t n_layers, uint32_t n_slots, uint32_t chunk_slots, const uint32_t *streamed_counts,
                           const uint32_t *call_layers, uint32_t n_calls, int64_t *ops, uint32_t max_ops, uint32_t *n_ops) {
-    if (!streamed_counts || !call_layers || !ops || !n_ops || n_layers == 0 || n_slots == 0) return KVATTN_E_ARG;
+    if (!streamed_counts || !call_layers || !ops || !n_ops || n_layers == 0 || n_slots == 0)
+        return fail(nullptr, KVATTN_E_ARG, "null argument, or no layers or no ring slots");
     StreamPlanner pl;
     pl.init(n_layers, n_slots, chunk_slots ? chunk_slots : 16);
     pl.set_layer_counts(std::vector<uint32_t>(streamed_counts, streamed_counts + n_layers));
     SimExec x{ops, max_ops};
     for (uint32_t i = 0; i < n_calls; i++) {
-        if (call_layers[i] >= n_layers) return KVATTN_E_RANGE;
+        if (call_layers[i] >= n_layers)
+            return fail(nullptr, KVATTN_E_RANGE, "call %u names layer %u of %u", i, call_layers[i], n_layers);
         if (streamed_counts[call_layers[i]] == 0) continue;
         int rc = drive_streamed_layer(pl, call_layers[i], x);
-        if (rc) return rc;
+        if (rc) return fail(nullptr, rc, "the planner failed on call %u (layer %u)", i, call_layers[i]);
     }
     *n_ops = x.n;
-    return x.overflow ? KVATTN_E_NOSPACE : KVATTN_OK;
+    if (x.overflow) return fail(nullptr, KVATTN_E_NOSPACE, "more than max_ops (%u) operations", max_ops);
+    return KVATTN_OK;
 }
 
 }  // extern "C"
