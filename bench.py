@@ -154,11 +154,12 @@ def one_pass(h, qs, outs, kind, rows):
 
 
 # --------------------------------------------------------------------------- traffic
-def measured_traffic(workload, rows):
+def measured_traffic(workload, rows, field="traffic_bytes_per_layer"):
     """HBM bytes per layer call (split + merge kernels) from the committed
     FETCH_SIZE / WRITE_SIZE counter summary of this workload, if it was taken
     on the current kernel sources (the record names them and their hash;
-    else None)."""
+    else None).  Streamed workloads: `field` picks the host-link bytes the
+    ring copies read per layer call."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}_w{rows}.txt")
     csrc = os.path.join(ROOT, "long_context_attention_amd", "csrc")
@@ -174,10 +175,11 @@ def measured_traffic(workload, rows):
         return None
     if rec.get("kernel_source_sha256") != sha:
         return None
-    return rec.get("traffic_bytes_per_layer")
+    return rec.get(field)
 
 
 TRAFFIC_SOURCES = ["kernels_common.h", "split_kernel.hip", "wide_kernel.hip"]
+STREAM_TRAFFIC_SOURCES = TRAFFIC_SOURCES + ["copy_kernels.hip"]
 
 
 def traffic_record(fetch_csv, write_csv, workload, rows, cmd_fetch, cmd_write):
@@ -197,26 +199,48 @@ def traffic_record(fetch_csv, write_csv, workload, rows, cmd_fetch, cmd_write):
                     continue
                 k = r["Kernel_Name"]
                 kind = ("attention" if ("split_kernel" in k or "wide_kernel" in k) else
-                        "merge" if "merge" in k else "copy_ref" if "neg_kernel" in k else None)
+                        "merge" if "merge" in k else "copy_ref" if "neg_kernel" in k else
+                        "ring_copy" if "ring_copy" in k else None)
                 if kind:
                     acc.setdefault(kind, []).append(float(r["Counter_Value"]))
-        return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
+        return ({k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()},
+                {k: sum(v) for k, v in acc.items()})
 
-    f, nf = means(fetch_csv, "FETCH_SIZE")
-    w, _ = means(write_csv, "WRITE_SIZE")
+    f, nf, fsum = means(fetch_csv, "FETCH_SIZE")
+    w, _, wsum = means(write_csv, "WRITE_SIZE")
     ref_kib = 256 * 1024
     fs, ws = ref_kib / f["copy_ref"], ref_kib / w["copy_ref"]
-    att = (f["attention"] * fs + w["attention"] * ws) * 1024
-    mer = (f.get("merge", 0.0) * fs + w.get("merge", 0.0) * ws) * 1024
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "long_context_attention_amd", "csrc")
-    for name in TRAFFIC_SOURCES:
-        with open(os.path.join(csrc, name), "rb") as fh:
-            h.update(fh.read())
     import inputs
     wl = inputs.WORKLOADS[workload]
-    return {"workload": workload, "rows": rows, "kernels": ["attention (split or wide kernel)", "merge"],
-            "kernel_sources": TRAFFIC_SOURCES, "kernel_source_sha256": h.hexdigest(),
+    streamed = wl.resident_fraction < 1.0
+    sources = STREAM_TRAFFIC_SOURCES if streamed else TRAFFIC_SOURCES
+    extra = {}
+    if streamed:
+        # several attention launches per layer call (resident pages, then one
+        # per streamed chunk) and ring copies ahead of them: totals over the
+        # run divided by the layer calls (one merge each)
+        calls = nf["merge"]
+        att = (fsum["attention"] * fs + wsum["attention"] * ws) * 1024 / calls
+        mer = (fsum["merge"] * fs + wsum["merge"] * ws) * 1024 / calls
+        rc_f = fsum.get("ring_copy", 0.0) * fs * 1024 / calls
+        rc_w = wsum.get("ring_copy", 0.0) * ws * 1024 / calls
+        h2d = (wl.n_pages - wl.n_resident) * 256 * wl.n_kv_heads * BYTES_PER_TOKEN_HEAD
+        extra = {"layer_calls": calls, "ring_copy_fetch_bytes_per_layer": round(rc_f),
+                 "ring_copy_write_bytes_per_layer": round(rc_w), "h2d_algorithmic_bytes_per_layer": h2d,
+                 "note": "ring copies are counted per layer call of the run (the copies of one layer run "
+                         "ahead of it); fetch = bytes read over the host link, write = bytes written into "
+                         "the ring"}
+    else:
+        att = (f["attention"] * fs + w["attention"] * ws) * 1024
+        mer = (f.get("merge", 0.0) * fs + w.get("merge", 0.0) * ws) * 1024
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "long_context_attention_amd", "csrc")
+    for name in sources:
+        with open(os.path.join(csrc, name), "rb") as fh:
+            h.update(fh.read())
+    rec = {"workload": workload, "rows": rows, "kernels": ["attention (split or wide kernel)", "merge"] +
+           (["ring_copy"] if streamed else []),
+            "kernel_sources": sources, "kernel_source_sha256": h.hexdigest(),
             "dispatches": nf,
             "fetch_size_kib": {k: round(v, 1) for k, v in f.items()},
             "write_size_kib": {k: round(v, 1) for k, v in w.items()},
@@ -229,6 +253,8 @@ def traffic_record(fetch_csv, write_csv, workload, rows, cmd_fetch, cmd_write):
                       "torch.neg over a 256 MiB float32 tensor (reads 256 MiB, writes 256 MiB) run three times in "
                       "the same process: fetch scale = 262144 / fetch_kib(copy), write scale = 262144 / "
                       "write_kib(copy).  The record holds for kernel sources whose concatenated sha256 matches."}
+    rec.update(extra)
+    return rec
 
 
 # --------------------------------------------------------------------------- KV writer
@@ -594,8 +620,15 @@ def figures(w, rows, kind, n_layers, ms_per_step, layer_ms, types, streamed, cei
         out["h2d_gbps"] = round(h2d, 2)
         c = ceiling["contiguous_gbps"]
         # the pass is bound by the host link: streamed bytes against the measured ceiling
+        # traffic: the bytes the ring copies read over the host link per pass,
+        # from the committed counter record when it matches the sources
+        rc = measured_traffic(w.name, rows, "ring_copy_fetch_bytes_per_layer") if default_types else None
         out["roofline"] = {"bound": "host-link", "achieved": out["h2d_gbps"], "peak": c, "unit": "GB/s",
-                           "frac": round(out["h2d_gbps"] / c, 4), "traffic": None}
+                           "frac": round(out["h2d_gbps"] / c, 4),
+                           "traffic": round(rc * n_layers) if rc is not None else None}
+        att = measured_traffic(w.name, rows) if default_types else None
+        if att is not None:
+            out["hbm_traffic_bytes_per_layer"] = att
         return out
     achieved = kv_bytes_layer / (layer_ms / 1e3) / 1e9
     tflops = flops_layer / (layer_ms / 1e3) / 1e12
