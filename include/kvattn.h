@@ -329,6 +329,24 @@ int kvattn_debug_read_page(kvattn_t h, uint32_t layer, uint32_t logical_page, vo
 int kvattn_debug_count_rescales(kvattn_t h, uint32_t *d_counter);
 
 /*
+ * Test aid: a device-side check of the streaming schedule's two fences (a
+ * ready fence before a chunk is read, a consumed fence before its slots are
+ * refilled: "troed's fork ...", section "KV data movement and attention").
+ * While d_counters (two caller-owned device uint32, zeroed by the caller) is
+ * non-NULL, each ring slot a streamed chunk fills is tagged with the page's
+ * global ordinal (plus skew, 0 normally) on the copy stream once its copy
+ * has finished, and the tags of the chunk's slots are compared with the
+ * ordinals the compute expects on the compute stream just before and just
+ * after the launch that reads them: d_counters[0] counts mismatches (a slot
+ * read before its copy finished, or refilled before its reader finished),
+ * d_counters[1] the slot checks made.  A nonzero skew makes every check fail,
+ * which shows the check runs.  The call drains both streams and restarts the
+ * schedule, so every chunk computed afterwards was copied, and tagged, after
+ * it.  NULL stops checking.  KVATTN_E_ARG if misaligned.
+ */
+int kvattn_debug_check_ring(kvattn_t h, uint32_t *d_counters, uint32_t skew);
+
+/*
  * Host only (no GPU work): the page-table checks kvattn_set_layer applies
  * that need no handle state -- range of pool ids and ring slots, no physical
  * page named twice, streamed pages need a host history (has_history != 0)

@@ -10,7 +10,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvattn.so")
-SOURCES = ["kvattn.hip", "split_kernel.hip", "wide_kernel.hip", "writer_kernel.hip", "copy_kernels.hip"]
+SOURCES = ["kvattn.hip", "split_kernel.hip", "wide_kernel.hip", "writer_kernel.hip", "copy_kernels.hip", "debug_kernels.hip"]
 HEADERS = ["attn_kernels.h", "kernels_common.h", "sched.h"]
 PROBE_LIB = os.path.join(HERE, "libkvattn_probe.so")
 PROBE_SOURCES = ["read_probe.hip"]

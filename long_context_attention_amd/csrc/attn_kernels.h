@@ -68,6 +68,17 @@ struct RingCopyArgs {
     size_t page_bytes;
 };
 
+// Ring-slot tags (test aid): slot (ring_base + o) mod n_slots of a chunk's
+// streamed page o (first <= o < first + count) is tagged with the page's
+// global ordinal ord_lo + o (low 32 bits) plus skew when its copy has
+// finished, and checked against ord_lo + o around the compute that reads it:
+// counter[0] += mismatches, counter[1] += pages checked.
+struct RingTagArgs {
+    uint32_t *tags;
+    uint32_t *counter;
+    uint32_t ring_base, ord_lo, first, count, n_slots, skew;
+};
+
 // KV writer: quantise R new token rows (positions n_old .. n_old + R - 1) of
 // one layer into their pages.  k, v: fp32 [R][Hkv][128].
 struct WriterArgs {
@@ -97,6 +108,8 @@ size_t kvattn_split_smem_bytes(int rt, uint32_t k_type, uint32_t v_type);
 hipError_t kvattn_launch_table_write(const TableWriteArgs &a, hipStream_t s);
 hipError_t kvattn_launch_writer(const WriterArgs &a, hipStream_t s);
 hipError_t kvattn_launch_ring_copy(const RingCopyArgs &a, hipStream_t s);
+// check = false: write the chunk's tags; true: check them
+hipError_t kvattn_launch_ring_tag(const RingTagArgs &a, bool check, hipStream_t s);
 hipError_t kvattn_split_setup();
 uint32_t kvattn_merge_max_splits();
 // rt: row tiles of 16 rows per workgroup (1 or 2); n_row_blocks blocks of 16 * rt rows

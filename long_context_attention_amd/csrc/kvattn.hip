@@ -168,7 +168,7 @@ size_t partial_units(const kvattn_params &p) {
 }
 
 struct WsLayout {
-    size_t tables, rlists, slists, staging, part_ml, part_o, total;
+    size_t tables, rlists, slists, staging, part_ml, part_o, ring_tags, total;
 };
 
 WsLayout workspace_layout(const kvattn_params &p) {
@@ -181,7 +181,8 @@ WsLayout workspace_layout(const kvattn_params &p) {
     w.staging = w.slists + align_up(ents);
     w.part_ml = w.staging + align_up(page_layout(p).page_bytes);
     w.part_o = w.part_ml + align_up(units * 2 * sizeof(float));
-    w.total = w.part_o + align_up(units * kHeadDim * sizeof(float));
+    w.ring_tags = w.part_o + align_up(units * kHeadDim * sizeof(float));
+    w.total = w.ring_tags + align_up((size_t)p.n_ring_slots * sizeof(uint32_t));
     return w;
 }
 
@@ -240,6 +241,8 @@ struct kvattn {
     hipEvent_t upload_done = nullptr;
     hipEvent_t compute_mark = nullptr;  // compute-stream position uploads wait for
     uint32_t *dbg_rescales = nullptr;   // test aid: re-reference event counter (device)
+    uint32_t *dbg_ring = nullptr;       // test aid: ring-slot tag check counters (device, 2 words)
+    uint32_t dbg_ring_skew = 0;         // test aid: added to the tags written (0: none)
     void *scratch = nullptr;            // this device's static scratch (kvattn_verify_noalloc)
     hipError_t scratch_err = hipSuccess;
     std::vector<LayerState> layers;
@@ -270,6 +273,7 @@ struct kvattn {
     uint32_t *d_slist(uint32_t layer) { return reinterpret_cast<uint32_t *>(wsp + ws.slists) + (size_t)layer * p.max_pages_per_layer; }
     float *part_ml() { return reinterpret_cast<float *>(wsp + ws.part_ml); }
     float *part_o() { return reinterpret_cast<float *>(wsp + ws.part_o); }
+    uint32_t *ring_tags() { return reinterpret_cast<uint32_t *>(wsp + ws.ring_tags); }
 };
 
 namespace {
@@ -539,8 +543,24 @@ struct HipExec {
         int rc;
         if (ob >= 0 && (rc = obs_record(ob, 0, h->copy))) return rc;
         if ((rc = copy_pages(c, L))) return rc;
+        if (h->dbg_ring && (rc = ring_tags(c, false, h->copy))) return rc;
         if (ob >= 0 && (rc = obs_record(ob, 1, h->copy))) return rc;
         HIP_TRY(h, hipEventRecord(h->sched.ready_event(c.event), h->copy));
+        return KVATTN_OK;
+    }
+    // test aid: write (after its copy) or check (around its compute) the
+    // generation tags of the chunk's ring slots
+    int ring_tags(const ChunkRef &c, bool check, hipStream_t s) {
+        RingTagArgs t;
+        t.tags = h->ring_tags();
+        t.counter = h->dbg_ring;
+        t.ring_base = (uint32_t)(c.ordinal_base % h->ring_slots);
+        t.ord_lo = (uint32_t)c.ordinal_base;
+        t.first = c.first;
+        t.count = c.count;
+        t.n_slots = h->ring_slots;
+        t.skew = h->dbg_ring_skew;
+        HIP_TRY(h, kvattn_launch_ring_tag(t, check, s));
         return KVATTN_OK;
     }
     int copy_pages(const ChunkRef &c, const LayerState &L) {
@@ -590,7 +610,9 @@ struct HipExec {
         a.page_list = h->d_slist(c.layer);
         a.list_offset = c.first;
         a.ring_base = (uint32_t)(c.ordinal_base % h->ring_slots);
+        if (h->dbg_ring && (rc = ring_tags(c, true, h->compute))) return rc;
         if ((rc = slotted ? launch_items(c.count) : launch_split(h, a, c.count, 1, nrt))) return rc;
+        if (h->dbg_ring && (rc = ring_tags(c, true, h->compute))) return rc;
         if (ob >= 0 && (rc = obs_record(ob, 3, h->compute))) return rc;
         HIP_TRY(h, hipEventRecord(h->sched.consumed_event(c.event), h->compute));
         return KVATTN_OK;
@@ -1185,6 +1207,22 @@ int kvattn_observe_read(kvattn_t h, int reset, kvattn_policy_observation *out) {
     if (reset) {
         h->obs_used = 0;
         h->obs_of.clear();
+    }
+    return KVATTN_OK;
+}
+
+int kvattn_debug_check_ring(kvattn_t h, uint32_t *d_counters, uint32_t skew) {
+    if (!h) return fail(nullptr, KVATTN_E_ARG, "null handle");
+    if (reinterpret_cast<uintptr_t>(d_counters) % 4) return fail(h, KVATTN_E_ARG, "misaligned counters");
+    HIP_TRY(h, hipStreamSynchronize(h->copy));
+    HIP_TRY(h, hipStreamSynchronize(h->compute));
+    h->dbg_ring = d_counters;
+    h->dbg_ring_skew = d_counters ? skew : 0u;
+    // chunks copied from here on carry tags (nothing prefetched survives)
+    if (h->p.n_ring_slots) {
+        std::vector<uint32_t> counts;
+        streamed_counts(h, counts);
+        h->sched.set_layer_counts(counts);
     }
     return KVATTN_OK;
 }

@@ -92,7 +92,7 @@ EXPORTS = ["kvattn_supported", "kvattn_page_bytes", "kvattn_workspace_bytes", "k
            "kvattn_upload_pages", "kvattn_set_layer", "kvattn_decode", "kvattn_verify", "kvattn_verify_noalloc",
            "kvattn_prefill_chunk",
            "kvattn_append",
-           "kvattn_synchronize", "kvattn_debug_read_page", "kvattn_debug_count_rescales", "kvattn_validate_page_table", "kvattn_sched_simulate",
+           "kvattn_synchronize", "kvattn_debug_read_page", "kvattn_debug_count_rescales", "kvattn_debug_check_ring", "kvattn_validate_page_table", "kvattn_sched_simulate",
            "kvattn_profile", "kvattn_profile_read", "kvattn_policy_step", "kvattn_observe", "kvattn_observe_read",
            "kvattn_set_ring_slots", "kvattn_destroy",
            "kvattn_last_error", "kvattn_global_error"]
@@ -137,6 +137,8 @@ def lib():
     L.kvattn_debug_read_page.restype = I
     L.kvattn_debug_count_rescales.argtypes = [P, P]
     L.kvattn_debug_count_rescales.restype = I
+    L.kvattn_debug_check_ring.argtypes = [P, P, U]
+    L.kvattn_debug_check_ring.restype = I
     L.kvattn_validate_page_table.argtypes = [PP, P, U, I]
     L.kvattn_validate_page_table.restype = I
     L.kvattn_sched_simulate.argtypes = [U, U, U, P, P, U, P, U, ctypes.POINTER(U)]
@@ -296,6 +298,12 @@ class Handle:
         """Test aid: counter is a device uint32 tensor (zeroed by the caller)
         that later calls increment per softmax re-reference event; None stops."""
         _check(lib().kvattn_debug_count_rescales(self.h, None if counter is None else _addr(counter)), self.h)
+
+    def check_ring(self, counters, skew=0):
+        """Test aid: counters is a device tensor of two uint32 (zeroed by the
+        caller): [0] ring-slot tag mismatches, [1] slot checks, counted around
+        every streamed chunk computed from now on; None stops."""
+        _check(lib().kvattn_debug_check_ring(self.h, None if counters is None else _addr(counters), skew), self.h)
 
     def profile(self, max_launches):
         _check(lib().kvattn_profile(self.h, max_launches), self.h)
