@@ -78,6 +78,13 @@ CASES = [
     (5000, 40, 8, 20, "verify", 0),     # 100 rows: the wide kernel
     (100 * 256 - 17, 40, 8, 4, "verify", 1),   # 100 splits: the many-split merge
     (300 * 256, 8, 1, 1, "decode", 1),         # 300 splits
+    # other GQA ratios and head counts: G = 3, 2 with 3 KV heads, 16, 7 (35
+    # rows: two blocks), and a G = 3 prefill on the wide kernel
+    (1000, 12, 4, 3, "verify", 0),
+    (1000, 6, 3, 2, "verify", 0),
+    (2000, 64, 4, 2, "verify", 0),
+    (2000, 28, 4, 5, "verify", 0),
+    (1500, 12, 4, 100, "prefill", 0),
 ]
 
 
