@@ -145,9 +145,10 @@ int kvattn_supported(uint32_t k_type, uint32_t v_type, uint32_t head_dim);
 size_t kvattn_page_bytes(const kvattn_params *params);
 
 /* Bytes the caller must provide as d_workspace (0 if the parameters are
- * invalid, the reason in kvattn_global_error()): device page tables, page lists, one staging page and the split
- * partials (m, l, acc[128] per split, row and query head, fp32).  The
- * attention operations expose their workspace size beside the span call so
+ * invalid, the reason in kvattn_global_error()): device page tables, page
+ * lists, one staging page, the split partials (m, l, acc[128] per split, row
+ * and query head, fp32) and one uint32 per ring slot (the tags of
+ * kvattn_debug_check_ring).  The attention operations expose their workspace size beside the span call so
  * the caller can budget it ("troed's fork ...", section "Backend-neutral
  * memory and streaming contracts"; "Adaptive KV Streaming for llama.cpp",
  * section "Batch and micro-batch sizes": a bounded query workspace). */
