@@ -172,6 +172,29 @@ def test_merge_split_ranges(n_splits):
     h.destroy()
 
 
+def test_merge_capacity_4096_splits():
+    """The largest history a layer may have (4,096 pages, the many-split
+    merge's capacity; ragged last page), one page per split: 4,096 partials
+    per (row, query head) merged, against the oracle on every output."""
+    n_pages = 4096
+    N, Hq, Hkv, W = n_pages * 256 - 100, 4, 1, 2
+    say(f"case merge capacity splits={n_pages} N={N} Hq={Hq} Hkv={Hkv} W={W}")
+    kvl = inputs.draw_layer(N, Hkv, 0, 64, device="cuda")
+    q = inputs.draw_queries(W, Hq, 0, 64)
+    n = kvl.pages.shape[0]
+    assert n == n_pages
+    h = handle(Hq, Hkv, n, n, 8, split_pages=1)
+    place(h, 0, kvl, perm_table(n, 64))
+    got = run(h, 0, q, W, "verify")
+    ref, _ = oracle.attend_paged(np.arange(n, dtype=np.uint32), N, 256, Hq, Hkv, q.numpy(), inputs.scale_for(),
+                                 pool=kvl.pages.cpu().numpy())
+    err = np.max(np.abs(got - ref))
+    say(f"  max-abs err {err:.3e}")
+    assert np.isfinite(got).all()
+    assert err <= TOL
+    h.destroy()
+
+
 @pytest.mark.parametrize("W", [1, 6])
 def test_chunk_order_modes(W):
     """Deterministic mode repeats its bits exactly; the default (waves claim
