@@ -340,8 +340,10 @@ int kvattn_debug_count_rescales(kvattn_t h, uint32_t *d_counter);
  * ordinals the compute expects on the compute stream just before and just
  * after the launch that reads them: d_counters[0] counts mismatches (a slot
  * read before its copy finished, or refilled before its reader finished),
- * d_counters[1] the slot checks made.  A nonzero skew makes every check fail,
- * which shows the check runs.  The call drains both streams and restarts the
+ * d_counters[1] the slot checks made.  After the second check the chunk's
+ * slots are filled with 0xFF bytes (NaN binary16 scales) before its consumed
+ * fence, so any read of a recycled slot before its refill makes the output
+ * NaN.  A nonzero skew makes every check fail, which shows the check runs.  The call drains both streams and restarts the
  * schedule, so every chunk computed afterwards was copied, and tagged, after
  * it.  NULL stops checking.  KVATTN_E_ARG if misaligned.
  */

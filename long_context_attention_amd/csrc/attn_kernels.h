@@ -77,6 +77,8 @@ struct RingTagArgs {
     uint32_t *tags;
     uint32_t *counter;
     uint32_t ring_base, ord_lo, first, count, n_slots, skew;
+    uint8_t *ring;      // poisoning: the ring and its page size
+    size_t page_bytes;
 };
 
 // KV writer: quantise R new token rows (positions n_old .. n_old + R - 1) of
@@ -110,6 +112,8 @@ hipError_t kvattn_launch_writer(const WriterArgs &a, hipStream_t s);
 hipError_t kvattn_launch_ring_copy(const RingCopyArgs &a, hipStream_t s);
 // check = false: write the chunk's tags; true: check them
 hipError_t kvattn_launch_ring_tag(const RingTagArgs &a, bool check, hipStream_t s);
+// fill the chunk's ring slots with 0xFF bytes (binary16 NaN scales)
+hipError_t kvattn_launch_ring_poison(const RingTagArgs &a, hipStream_t s);
 hipError_t kvattn_split_setup();
 uint32_t kvattn_merge_max_splits();
 // rt: row tiles of 16 rows per workgroup (1 or 2); n_row_blocks blocks of 16 * rt rows

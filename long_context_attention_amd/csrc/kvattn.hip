@@ -560,7 +560,21 @@ struct HipExec {
         t.count = c.count;
         t.n_slots = h->ring_slots;
         t.skew = h->dbg_ring_skew;
+        t.ring = h->ring;
+        t.page_bytes = h->lay.page_bytes;
         HIP_TRY(h, kvattn_launch_ring_tag(t, check, s));
+        return KVATTN_OK;
+    }
+    // test aid: once the chunk's readers are done, poison its slots
+    int ring_poison(const ChunkRef &c) {
+        RingTagArgs t{};
+        t.ring_base = (uint32_t)(c.ordinal_base % h->ring_slots);
+        t.first = c.first;
+        t.count = c.count;
+        t.n_slots = h->ring_slots;
+        t.ring = h->ring;
+        t.page_bytes = h->lay.page_bytes;
+        HIP_TRY(h, kvattn_launch_ring_poison(t, h->compute));
         return KVATTN_OK;
     }
     int copy_pages(const ChunkRef &c, const LayerState &L) {
@@ -613,6 +627,7 @@ struct HipExec {
         if (h->dbg_ring && (rc = ring_tags(c, true, h->compute))) return rc;
         if ((rc = slotted ? launch_items(c.count) : launch_split(h, a, c.count, 1, nrt))) return rc;
         if (h->dbg_ring && (rc = ring_tags(c, true, h->compute))) return rc;
+        if (h->dbg_ring && (rc = ring_poison(c))) return rc;
         if (ob >= 0 && (rc = obs_record(ob, 3, h->compute))) return rc;
         HIP_TRY(h, hipEventRecord(h->sched.consumed_event(c.event), h->compute));
         return KVATTN_OK;
