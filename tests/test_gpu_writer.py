@@ -144,3 +144,48 @@ def test_append_rejections():
     assert e.value.code == kv.E_UNSUPPORTED
     h.destroy()
     h2.destroy()
+
+
+@pytest.mark.parametrize("W", [1, 4])
+def test_append_decode_loop_on_streamed_layer(W):
+    """The serving loop on a layer that streams most of its history: each
+    step appends W rows into the resident tail (a new pool page when a page
+    fills), publishes the touched pages into the pinned host history the
+    scheduler streams from, and attends over the grown history through the
+    ring.  The eight steps cross a page boundary; every step's output is
+    compared with the oracle over the published history."""
+    N0, Hq, Hkv, T = 12 * 256 - 5, 40, 8, 256
+    steps = 8
+    n_max = -(-(N0 + steps * W + 256) // T)
+    say(f"case append loop on a streamed layer N0={N0} W={W} steps={steps}")
+    kvl = inputs.draw_layer(N0, Hkv, 0, 96)
+    n0 = kvl.pages.shape[0]
+    rng = np.random.default_rng(96)
+    # the tail page and a third of the others resident; the rest stream
+    res = np.sort(np.append(rng.choice(n0 - 1, (n0 - 1) // 3, replace=False), n0 - 1))
+    table = np.full(n0, kv.PT_HOST, dtype=np.uint32)
+    table[res] = np.arange(len(res))
+    h = handle(Hq, Hkv, len(res) + n_max, n_max, 8, n_ring=5, chunk_slots=2)
+    pb = kv.page_bytes(h.params)
+    hist = torch.zeros((n_max, pb), dtype=torch.uint8).pin_memory()
+    hist[:n0].copy_(kvl.pages)
+    place(h, 0, kvl, table, history=hist)
+    next_pool = len(res)
+    n_tokens = N0
+    k, v = rows(steps * W, Hkv, 97)
+    for s in range(steps):
+        new_pages = -(-(n_tokens + W) // T) - (-(-n_tokens // T))
+        ids = np.arange(next_pool, next_pool + new_pages, dtype=np.uint32)
+        next_pool += new_pages
+        h.append(0, k[s * W:(s + 1) * W].cuda(), v[s * W:(s + 1) * W].cuda(), W, ids, publish=hist)
+        n_tokens += W
+        q = inputs.draw_queries(W, Hq, s, 96)
+        got = run(h, 0, q, W, "verify")
+        n_pages = -(-n_tokens // T)
+        ref, _ = oracle.attend_paged(np.arange(n_pages, dtype=np.uint32), n_tokens, T, Hq, Hkv, q.numpy(),
+                                     inputs.scale_for(), pool=hist[:n_pages].numpy())
+        err = float(np.max(np.abs(got - ref)))
+        say(f"  step {s}: {n_tokens} tokens, {new_pages} new pages, max-abs err {err:.3e}")
+        assert np.isfinite(got).all()
+        assert err <= TOL
+    h.destroy()
