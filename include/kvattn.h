@@ -233,6 +233,12 @@ int kvattn_set_layer(kvattn_t h, uint32_t layer, const uint32_t *page_table, uin
  * host-to-device bytes than W = 1 ("Adaptive KV Streaming for llama.cpp",
  * section "Batch and micro-batch sizes"; the second mirror of "troed's fork
  * ...", footnotes: wide verify as consecutive row tiles over one KV span).
+ * Asynchronous on the compute stream.  On a layer without streamed pages a
+ * call enqueues kernel launches only (no allocation, memset, copy or host
+ * wait), so it may be captured into a HIP graph on the compute stream.  On a
+ * layer with streamed pages it also enqueues copies and events on the copy
+ * stream, driven by the host, and drains both streams when the calls leave
+ * the layer order; such calls run eagerly, not under capture.
  */
 int kvattn_decode(kvattn_t h, uint32_t layer, const float *d_q, float *d_out);
 int kvattn_verify(kvattn_t h, uint32_t layer, const float *d_q, uint32_t W, float *d_out);
