@@ -676,7 +676,7 @@ def measure(w, widths, args, torch, kv, inputs, types, steps, warmup, cpu_budget
                        "chunk_order": "static" if args.deterministic else
                        "claimed in splits of >= 96 chunks, else static",
                        "resident_fraction": w.resident_fraction, "ring_slots": w.ring_slots,
-                       "chunk_slots": (args.chunk_slots or 16) if streamed else None}
+                       "chunk_slots": (args.chunk_slots or max(1, w.ring_slots * 3 // 8)) if streamed else None}
         r["steps"], r["warmup"], r["wall_s"], r["step_ms_spread"] = steps, warmup, round(wall, 3), spread
         if not streamed:
             r["kernel_ms"] = {"layer_mean": round(layer_ms, 5), "timing": timing}

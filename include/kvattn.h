@@ -119,7 +119,8 @@ typedef struct kvattn_params {
     float softmax_scale;          /* 0 => 1/sqrt(head_dim) */
     uint32_t split_pages;         /* pages per split for narrow calls (rows per KV head <= 32);
                                      0 => chosen from the page count and the CU count */
-    uint32_t chunk_slots;         /* ring slots per streamed chunk; 0 => 16 (clamped to the ring) */
+    uint32_t chunk_slots;         /* ring slots per streamed chunk (clamped to the ring); 0 => three
+                                     eighths of the active ring, at least 1 (24 of 64 slots) */
     uint32_t deterministic;       /* 1 => every call gives the same bits for the same history and
                                      queries (fixed chunk-to-wave order inside a split); 0 =>
                                      narrow calls over resident pages with long splits (>= 96

@@ -144,11 +144,20 @@ int check_params(const kvattn_params &p, std::string &why) {
     return KVATTN_OK;
 }
 
+// Ring slots per streamed chunk for a ring of `ring` slots: the caller's
+// chunk_slots, or three eighths of the ring (24 of 64 slots): against 16
+// pages per chunk, measured 1.7 % faster at one row, 0.6 % at four and 9 % at
+// 49 on the 262,144-token streamed workload (fewer, larger copy and compute
+// launches, with still more than two chunks in the ring).
+uint32_t chunk_for(const kvattn_params &p, uint32_t ring) {
+    const uint32_t chunk = p.chunk_slots ? p.chunk_slots : std::max<uint32_t>(1, ring * 3 / 8);
+    return std::max<uint32_t>(1, std::min(chunk, ring));
+}
+
 // Partial slots of streamed calls of more than 32 rows per KV head: pages
 // per launch, at least the streamed chunk size.
 uint32_t stream_slots(const kvattn_params &p) {
-    const uint32_t chunk = p.chunk_slots ? p.chunk_slots : 16;
-    return std::max<uint32_t>(16, std::min(chunk, std::max<uint32_t>(p.n_ring_slots, 1)));
+    return std::max<uint32_t>(16, chunk_for(p, std::max<uint32_t>(p.n_ring_slots, 1)));
 }
 
 // Partial-buffer capacity in (split, row, query head) units.
@@ -817,10 +826,9 @@ int kvattn_create(const kvattn_params *params, void *d_pool, size_t pool_bytes, 
         delete h;
         return code;
     }
-    const uint32_t chunk = p.chunk_slots ? p.chunk_slots : 16;
     h->ring_slots = p.n_ring_slots;
     if (p.n_ring_slots) {
-        if (!h->sched.init(p.n_layers, p.n_ring_slots, std::min(chunk, p.n_ring_slots))) {
+        if (!h->sched.init(p.n_layers, p.n_ring_slots, chunk_for(p, p.n_ring_slots))) {
             (void)hipEventDestroy(h->upload_done);
             (void)hipEventDestroy(h->compute_mark);
             delete h;
@@ -1257,9 +1265,8 @@ int kvattn_set_ring_slots(kvattn_t h, uint32_t n_slots) {
     if (n_slots == h->ring_slots) return KVATTN_OK;
     HIP_TRY(h, hipStreamSynchronize(h->copy));
     HIP_TRY(h, hipStreamSynchronize(h->compute));
-    const uint32_t chunk = h->p.chunk_slots ? h->p.chunk_slots : 16;
     h->sched.destroy();
-    if (!h->sched.init(h->p.n_layers, n_slots, std::min(chunk, n_slots))) return fail(h, KVATTN_E_HIP, "ring event setup failed");
+    if (!h->sched.init(h->p.n_layers, n_slots, chunk_for(h->p, n_slots))) return fail(h, KVATTN_E_HIP, "ring event setup failed");
     std::vector<uint32_t> counts;
     streamed_counts(h, counts);
     h->sched.set_layer_counts(counts);
@@ -1312,7 +1319,7 @@ int kvattn_sched_simulate(uint32_t n_layers, uint32_t n_slots, uint32_t chunk_sl
     if (!streamed_counts || !call_layers || !ops || !n_ops || n_layers == 0 || n_slots == 0)
         return fail(nullptr, KVATTN_E_ARG, "null argument, or no layers or no ring slots");
     StreamPlanner pl;
-    pl.init(n_layers, n_slots, chunk_slots ? chunk_slots : 16);
+    pl.init(n_layers, n_slots, chunk_slots ? std::min(chunk_slots, n_slots) : std::max<uint32_t>(1, n_slots * 3 / 8));
     pl.set_layer_counts(std::vector<uint32_t>(streamed_counts, streamed_counts + n_layers));
     SimExec x{ops, max_ops};
     for (uint32_t i = 0; i < n_calls; i++) {
